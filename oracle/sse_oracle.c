@@ -1,0 +1,357 @@
+/*
+ * sse_oracle.c -- plain sequential fp64 reference for the Sparse State
+ * Expansion (SSE) layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library and must never be used as a
+ * fallback for it.
+ *
+ * Source of the method: the web page "Scaling Linear Attention with Sparse
+ * State Expansion: 中文研读笔记" (study notes on arXiv 2507.16577v2).  Every
+ * citation below names a section or equation of that page.
+ *
+ *   §2.3, eqs. (9)-(14): per token and head,
+ *       e_t  = softmax over the N partitions of the router logits
+ *       T_t  = indices of the k largest entries
+ *       k_t  = softmax over the c key rows of the key logits
+ *       S^i  = Lambda_t S^i + e^i k_t^T v_t   for i in T_t,
+ *       S^i unchanged (no decay, no write)    for i not in T_t,
+ *       o_t  = sum over i in T_t of e^i q_t S^i   (state read after the write)
+ *   §2.1, eq. (6): the transition used by SSE is GLA-style, Lambda_t =
+ *       diag(alpha_t), alpha_t in (0,1]^c scaling the c state rows.
+ *   §2.3 (text under the equations): no renormalisation of e over T_t; the
+ *       same e^i gates the write and the read.
+ *   §2.5: one extra, always-selected shared partition, here with the same
+ *       q, k, alpha and weight 1 on both write and read.
+ *   §2.6 (closing paragraph): unselected partitions keep an identity
+ *       transition; partition outputs are summed back per token.
+ *
+ * Readings taken where the page is silent (each is also listed in the design
+ * notes of the repository):
+ *   - top-k order is descending by logit, equal logits -> lower index first;
+ *     the selection compares the logits themselves (softmax is monotone);
+ *   - log_alpha is given per (token, head, row): alpha = exp(log_alpha);
+ *   - no query scaling, no output normalisation;
+ *   - states start at zero per sequence unless initial states are given.
+ *
+ * Precision: inputs arrive as fp32 or bf16 bit patterns and are converted to
+ * fp64 exactly; everything after that is fp64.
+ *
+ * parity pins: see the tests (brute-force quadratic form, single-state GLA
+ * reduction, identity of unselected states, the page's decay example, the
+ * closed form of Appendix A Prop. 4 as summarised in §2.7, masked linear
+ * attention at alpha = 1).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MAX_N 256
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Exact conversion of one stored input element to fp64. */
+static double load_value(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Softmax over n values (max-subtracted). */
+static void softmax(const double *x, int n, double *out)
+{
+    double m = x[0];
+    for (int i = 1; i < n; i++)
+        if (x[i] > m)
+            m = x[i];
+    double s = 0.0;
+    for (int i = 0; i < n; i++) {
+        out[i] = exp(x[i] - m);
+        s += out[i];
+    }
+    for (int i = 0; i < n; i++)
+        out[i] /= s;
+}
+
+/* TopKIndices of eq. (10): the k largest logits, descending; equal logits ->
+ * lower index first (scan ascending, replace only on strictly greater). */
+static void top_k(const double *z, int n, int k, int *sel)
+{
+    unsigned char taken[ORACLE_MAX_N];
+    memset(taken, 0, sizeof taken);
+    for (int r = 0; r < k; r++) {
+        int best = -1;
+        for (int i = 0; i < n; i++)
+            if (!taken[i] && (best < 0 || z[i] > z[best]))
+                best = i;
+        taken[best] = 1;
+        sel[r] = best;
+    }
+}
+
+/*
+ * One token of the recurrence for one head.
+ *   z[N], q[c], kl[c], la[c], v[d]: this token's inputs (fp64)
+ *   S: (N+1) states of c x d, row-major, partition N is the shared one
+ *   o[d]: output; sel[k], esel[k]: chosen partitions and their router weights
+ *   work: scratch of at least N + 2c doubles
+ */
+static void sse_token(int N, int k, int c, int d, const double *z, const double *q,
+                      const double *kl, const double *la, const double *v, double *S,
+                      double *o, int *sel, double *esel, double *work)
+{
+    double *e = work;           /* [N] router probabilities, eq. (9)       */
+    double *kappa = work + N;   /* [c] softmax key, eq. (11)                */
+    double *alpha = kappa + c;  /* [c] diagonal of Lambda_t, eq. (6)        */
+    const int64_t cd = (int64_t)c * d;
+
+    softmax(z, N, e);
+    top_k(z, N, k, sel);
+    softmax(kl, c, kappa);
+    for (int j = 0; j < c; j++)
+        alpha[j] = exp(la[j]);
+    for (int m = 0; m < d; m++)
+        o[m] = 0.0;
+
+    /* k selected partitions (weight e^i on write and read) followed by the
+     * shared partition (weight 1 on write and read). */
+    for (int r = 0; r <= k; r++) {
+        int part = (r < k) ? sel[r] : N;
+        double w = (r < k) ? e[part] : 1.0;
+        if (r < k)
+            esel[r] = w;
+        double *Sp = S + (int64_t)part * cd;
+        /* eq. (12): S = diag(alpha) S + w k^T v */
+        for (int j = 0; j < c; j++)
+            for (int m = 0; m < d; m++)
+                Sp[(int64_t)j * d + m] = alpha[j] * Sp[(int64_t)j * d + m] + w * kappa[j] * v[m];
+        /* eq. (14): o += w q S (read after the write) */
+        for (int m = 0; m < d; m++) {
+            double acc = 0.0;
+            for (int j = 0; j < c; j++)
+                acc += q[j] * Sp[(int64_t)j * d + m];
+            o[m] += w * acc;
+        }
+    }
+}
+
+/*
+ * Run one (sequence, head) unit over tokens [t0, t1) of token-major inputs
+ *   q, key_logits, log_alpha: [T_tot, H, c];  v: [T_tot, H, d];
+ *   router_logits: [T_tot, H, N]
+ * stored as fp32 or bf16 (dtype).
+ *   S: [(N+1), c, d] fp64, in = initial state, out = final state
+ *   o: [(t1-t0), d]; sel: [(t1-t0), k]; esel: [(t1-t0), k]
+ * Returns 0, or -1 on bad arguments.
+ */
+int sse_oracle_unit(int dtype, const void *q, const void *key_logits, const void *v,
+                    const void *log_alpha, const void *router_logits, int64_t t0, int64_t t1,
+                    int h, int H, int c, int d, int N, int k, double *S, double *o,
+                    int32_t *sel, double *esel)
+{
+    if (N < 1 || N > ORACLE_MAX_N || k < 1 || k > N || c < 1 || d < 1 || h < 0 || h >= H ||
+        t1 < t0)
+        return -1;
+    double *buf = (double *)malloc(sizeof(double) * (size_t)(N + 3 * c + d + N + 2 * c));
+    if (!buf)
+        return -1;
+    double *z = buf, *qq = z + N, *kk = qq + c, *ll = kk + c, *vv = ll + c, *work = vv + d;
+    int selr[ORACLE_MAX_N];
+    for (int64_t t = t0; t < t1; t++) {
+        int64_t rc = (t * H + h) * (int64_t)c, rd = (t * H + h) * (int64_t)d,
+                rn = (t * H + h) * (int64_t)N;
+        for (int i = 0; i < N; i++)
+            z[i] = load_value(router_logits, dtype, rn + i);
+        for (int j = 0; j < c; j++) {
+            qq[j] = load_value(q, dtype, rc + j);
+            kk[j] = load_value(key_logits, dtype, rc + j);
+            ll[j] = load_value(log_alpha, dtype, rc + j);
+        }
+        for (int m = 0; m < d; m++)
+            vv[m] = load_value(v, dtype, rd + m);
+        int64_t lt = t - t0;
+        sse_token(N, k, c, d, z, qq, kk, ll, vv, S, o + lt * d, selr, esel + lt * k, work);
+        for (int r = 0; r < k; r++)
+            sel[lt * k + r] = selr[r];
+    }
+    free(buf);
+    return 0;
+}
+
+/*
+ * Whole varlen forward: sequences s = 0..num_seqs-1 occupy tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]).  Units (s, h) are independent and are
+ * spread over n_threads threads (timing convenience only; each unit is
+ * computed sequentially).
+ *   init: [S, H, N+1, c, d] fp64 or NULL (zeros)
+ *   o: [T_tot, H, d]; final_states: [S, H, N+1, c, d]
+ *   topk_idx, topk_e: [T_tot, H, k]
+ */
+struct fwd_job {
+    int dtype;
+    const void *q, *kl, *v, *la, *z;
+    const int32_t *cu;
+    int num_seqs, H, c, d, N, k;
+    const double *init;
+    double *o, *fs, *e;
+    int32_t *idx;
+    int next_unit; /* shared counter, protected by mu */
+    pthread_mutex_t mu;
+    int status;
+};
+
+static void *fwd_worker(void *arg)
+{
+    struct fwd_job *J = (struct fwd_job *)arg;
+    const int64_t cd = (int64_t)J->c * J->d, st = (int64_t)(J->N + 1) * cd;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int u = J->next_unit++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->num_seqs * J->H)
+            break;
+        int s = u / J->H, h = u % J->H;
+        int64_t t0 = J->cu[s], t1 = J->cu[s + 1], L = t1 - t0;
+        double *S = J->fs + (int64_t)u * st;
+        if (J->init)
+            memcpy(S, J->init + (int64_t)u * st, sizeof(double) * (size_t)st);
+        else
+            memset(S, 0, sizeof(double) * (size_t)st);
+        double *o = (double *)malloc(sizeof(double) * (size_t)(L * J->d + 1));
+        double *e = (double *)malloc(sizeof(double) * (size_t)(L * J->k + 1));
+        int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(L * J->k + 1));
+        int rc = (o && e && idx) ? sse_oracle_unit(J->dtype, J->q, J->kl, J->v, J->la, J->z, t0,
+                                                   t1, h, J->H, J->c, J->d, J->N, J->k, S, o,
+                                                   idx, e)
+                                 : -1;
+        if (rc == 0) {
+            for (int64_t t = 0; t < L; t++) {
+                int64_t g = (t0 + t) * J->H + h;
+                memcpy(J->o + g * J->d, o + t * J->d, sizeof(double) * (size_t)J->d);
+                memcpy(J->e + g * J->k, e + t * J->k, sizeof(double) * (size_t)J->k);
+                memcpy(J->idx + g * J->k, idx + t * J->k, sizeof(int32_t) * (size_t)J->k);
+            }
+        } else {
+            J->status = -1;
+        }
+        free(o);
+        free(e);
+        free(idx);
+    }
+    return NULL;
+}
+
+int sse_oracle_forward(int dtype, const void *q, const void *key_logits, const void *v,
+                       const void *log_alpha, const void *router_logits,
+                       const int32_t *cu_seqlens, int num_seqs, int H, int c, int d, int N,
+                       int k, const double *init_states, double *o, double *final_states,
+                       int32_t *topk_idx, double *topk_e, int n_threads)
+{
+    if (num_seqs < 0 || H < 1 || n_threads < 1)
+        return -1;
+    for (int s = 0; s < num_seqs; s++)
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+    struct fwd_job J;
+    memset(&J, 0, sizeof J);
+    J.dtype = dtype;
+    J.q = q;
+    J.kl = key_logits;
+    J.v = v;
+    J.la = log_alpha;
+    J.z = router_logits;
+    J.cu = cu_seqlens;
+    J.num_seqs = num_seqs;
+    J.H = H;
+    J.c = c;
+    J.d = d;
+    J.N = N;
+    J.k = k;
+    J.init = init_states;
+    J.o = o;
+    J.fs = final_states;
+    J.e = topk_e;
+    J.idx = topk_idx;
+    pthread_mutex_init(&J.mu, NULL);
+    if (n_threads == 1) {
+        fwd_worker(&J);
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+        int started = 0;
+        for (int i = 0; i < n_threads; i++)
+            if (pthread_create(&th[i], NULL, fwd_worker, &J) == 0)
+                started++;
+            else
+                break;
+        if (started == 0)
+            fwd_worker(&J);
+        for (int i = 0; i < started; i++)
+            pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&J.mu);
+    return J.status;
+}
+
+/*
+ * One decode step (§2.6: decode recurs only on the selected states) for B
+ * independent sequences x H heads, one token each.
+ *   inputs: q, key_logits, log_alpha [B, H, c]; v [B, H, d]; router [B, H, N]
+ *   states: [B, H, N+1, c, d] fp64, updated in place
+ *   o: [B, H, d]; topk_idx, topk_e: [B, H, k]
+ * It is the forward of a length-1 sequence per (b, h).
+ */
+int sse_oracle_decode_step(int dtype, const void *q, const void *key_logits, const void *v,
+                           const void *log_alpha, const void *router_logits, int B, int H, int c,
+                           int d, int N, int k, double *states, double *o, int32_t *topk_idx,
+                           double *topk_e)
+{
+    const int64_t st = (int64_t)(N + 1) * c * d;
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            int64_t u = (int64_t)b * H + h;
+            /* token b of a [B, H, .] array is row b of a token-major array */
+            int rc = sse_oracle_unit(dtype, q, key_logits, v, log_alpha, router_logits, b, b + 1,
+                                     h, H, c, d, N, k, states + u * st, o + u * d,
+                                     topk_idx + u * k, topk_e + u * k);
+            if (rc)
+                return rc;
+        }
+    return 0;
+}
+
+/*
+ * Varlen grouping (§2.6, varlen paragraph): records (token, slot) are
+ * gathered per (sequence, head, partition) segment in time order.  Segment
+ * id g = (s*H + h)*N + i.
+ *   topk_idx: [T_tot, H, k]
+ *   seg_offsets: [num_seqs*H*N + 1]; seg_tok, seg_slot: [T_tot*H*k]
+ * Plain definition: for every segment in id order, scan its sequence in time
+ * order and append every (t, j) whose j-th choice is the segment's partition.
+ */
+int sse_oracle_group(const int32_t *topk_idx, const int32_t *cu_seqlens, int num_seqs, int H,
+                     int N, int k, int32_t *seg_offsets, int32_t *seg_tok, int32_t *seg_slot)
+{
+    int64_t pos = 0;
+    for (int s = 0; s < num_seqs; s++)
+        for (int h = 0; h < H; h++)
+            for (int i = 0; i < N; i++) {
+                seg_offsets[((int64_t)s * H + h) * N + i] = (int32_t)pos;
+                for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; t++)
+                    for (int j = 0; j < k; j++)
+                        if (topk_idx[(t * H + h) * k + j] == i) {
+                            seg_tok[pos] = (int32_t)t;
+                            seg_slot[pos] = j;
+                            pos++;
+                        }
+            }
+    seg_offsets[(int64_t)num_seqs * H * N] = (int32_t)pos;
+    return 0;
+}
