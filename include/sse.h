@@ -1,0 +1,173 @@
+/*
+ * sse.h -- C ABI of the MI355X (gfx950) Sparse State Expansion library.
+ *
+ * The operation is the SSE linear-attention layer of the web page "Scaling
+ * Linear Attention with Sparse State Expansion: 中文研读笔记" (study notes on
+ * arXiv 2507.16577v2).  Per token t and head h:
+ *
+ *   e_t     = softmax over N partitions of router_logits[t,h,:]   (§2.3, eq. 9)
+ *   T_t     = the topk partitions with the largest logits           (§2.3, eq. 10)
+ *             (descending; equal logits -> lower index first)
+ *   kappa_t = softmax over the c rows of key_logits[t,h,:]          (§2.3, eq. 11)
+ *   alpha_t = exp(log_alpha[t,h,:]), one decay per state row        (§2.1, eq. 6)
+ *   S^i     = diag(alpha_t) S^i + e^i kappa_t^T v_t   for i in T_t   (§2.3, eq. 12)
+ *   S^i     unchanged (no decay, no write)            for i not in T_t
+ *   S^sh    = diag(alpha_t) S^sh + kappa_t^T v_t   (always-active shared
+ *             partition, weight 1, same q/k/alpha; §2.5)
+ *   o_t     = sum_{i in T_t} e^i q_t S^i + q_t S^sh    (read after the write;
+ *             §2.3 eqs. 13-14, §2.6 gated sum back to the token)
+ *
+ * e is not renormalised over T_t (§2.3).  No query scale is applied.
+ *
+ * Conventions for every entry point
+ *   - Device pointers unless stated otherwise; buffers are dense, row-major,
+ *     in the layouts given.  The caller owns every buffer; the library never
+ *     allocates or frees memory and never synchronises the stream.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All
+ *     work is enqueued on it asynchronously.
+ *   - `dtype` selects the storage type of the five token inputs:
+ *     SSE_F32 (float) or SSE_BF16 (bfloat16, 2-byte bit patterns).  States,
+ *     outputs and all accumulation are fp32.
+ *   - Supported sizes: c, d in {32, 64, 128}; 1 <= topk <= N <= 64,
+ *     topk <= 8; H >= 1.
+ *   - Argument checks run on the host before any launch.  They return
+ *     SSE_ERR_INVALID_ARG (null pointer, negative or inconsistent size),
+ *     SSE_ERR_UNSUPPORTED (size outside the supported set) or
+ *     SSE_ERR_WORKSPACE (workspace too small); nothing is launched then.
+ *     A failed launch returns SSE_ERR_HIP.  No C++ exception crosses this
+ *     interface.
+ *   - Preconditions the library does not check (documented, not detected):
+ *     cu_seqlens is non-decreasing with cu_seqlens[0] == 0 and
+ *     cu_seqlens[num_seqs] == total_tokens; every length <= max_seqlen;
+ *     inputs are finite; log_alpha <= 0 and the sum of log_alpha over any 64
+ *     consecutive records of one partition stays above -80 (the chunked
+ *     factorisation multiplies by exp of minus that sum in fp32).
+ */
+#ifndef SSE_H
+#define SSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSE_OK = 0,
+    SSE_ERR_INVALID_ARG = 1,
+    SSE_ERR_UNSUPPORTED = 2,
+    SSE_ERR_WORKSPACE = 3,
+    SSE_ERR_HIP = 4
+} sse_status;
+
+typedef enum { SSE_F32 = 0, SSE_BF16 = 1 } sse_dtype;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *sse_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sse_version(void);
+
+/*
+ * Bytes of device workspace sse_forward needs for these sizes (0 if the
+ * sizes are invalid).  The workspace holds the router choice, the grouping
+ * arrays and the segment bookkeeping; it may be reused across calls on the
+ * same stream.
+ */
+size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                   int c, int d, int N, int topk);
+
+/*
+ * Varlen forward (prefill) over packed sequences.
+ * Defined by §2.3 eqs. (9)-(14) with the shared partition of §2.5, computed
+ * with the varlen grouping of §2.6: the records of each (sequence, head,
+ * partition) are gathered in time order and run through a chunked gated
+ * linear attention whose per-partition clock only advances on the
+ * partition's own records (identity transition elsewhere, §2.6).
+ *
+ *   q, key_logits, log_alpha  [total_tokens, H, c]   (dtype)
+ *   v                         [total_tokens, H, d]   (dtype)
+ *   router_logits             [total_tokens, H, N]   (dtype)
+ *   cu_seqlens                [num_seqs + 1] int32, device; sequence s is
+ *                             tokens [cu_seqlens[s], cu_seqlens[s+1]); states
+ *                             restart at every sequence start
+ *   max_seqlen                upper bound of every sequence length (host int)
+ *   initial_states            [num_seqs, H, N+1, c, d] fp32 or NULL (zeros);
+ *                             partition index N is the shared partition
+ *   o                         [total_tokens, H, d] fp32 (written)
+ *   final_states              [num_seqs, H, N+1, c, d] fp32 (written; a
+ *                             partition that no token selects keeps its
+ *                             initial state bit for bit)
+ *   topk_idx, topk_w          [total_tokens, H, topk] int32 / fp32, or NULL:
+ *                             the chosen partitions (descending logits) and
+ *                             their router probabilities
+ *   workspace                 device buffer of workspace_bytes >=
+ *                             sse_forward_workspace_bytes(...)
+ * o may not alias any input.  Accumulation of the k+1 partition reads into o
+ * uses fp32 atomics, so o may differ between runs in the last bits.
+ */
+int sse_forward(const void *q, const void *key_logits, const void *v, const void *log_alpha,
+                const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
+                int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                const float *initial_states, float *o, float *final_states, int32_t *topk_idx,
+                float *topk_w, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step (§2.6: decoding recurs only on the selected states).
+ * B independent sequences, one new token each, for every head.
+ *   q, key_logits, log_alpha  [B, H, c]   (dtype)
+ *   v                         [B, H, d]   (dtype)
+ *   router_logits             [B, H, N]   (dtype)
+ *   states                    [B, H, N+1, c, d] fp32, updated in place; the
+ *                             N - topk unselected routed states of every
+ *                             (b, h) are neither read nor written
+ *   o                         [B, H, d] fp32 (written)
+ *   topk_idx                  [B, H, topk] int32 or NULL
+ * Needs no workspace.  Deterministic: the same inputs give the same bits.
+ */
+int sse_decode_step(const void *q, const void *key_logits, const void *v, const void *log_alpha,
+                    const void *router_logits, int dtype, int B, int H, int c, int d, int N,
+                    int topk, float *states, float *o, int32_t *topk_idx, void *stream);
+
+/*
+ * Stage entry point: the router alone (§2.3 eqs. 9-10) for `rows` rows of
+ * N logits (rows = tokens x heads).
+ *   router_logits [rows, N] (dtype) -> topk_idx [rows, topk] int32,
+ *   topk_w [rows, topk] fp32 (router probability of each chosen partition).
+ * Deterministic.  The forward pass runs the same device code.
+ */
+int sse_router_topk(const void *router_logits, int dtype, int64_t rows, int N, int topk,
+                    int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Bytes of workspace sse_group_by_partition needs (0 if sizes are invalid). */
+size_t sse_group_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H, int N,
+                                 int topk);
+
+/*
+ * Stage entry point: the varlen grouping of §2.6.  Records (token, slot) of
+ * every (sequence s, head h, partition i) segment, segment id
+ * g = (s*H + h)*N + i, are laid out in id order, time order inside a
+ * segment (a stable counting sort).
+ *   topk_idx    [total_tokens, H, topk] int32 (partition of each choice)
+ *   topk_w      [total_tokens, H, topk] fp32 or NULL
+ *   seg_offsets [num_seqs*H*N + 1] int32: segment g is
+ *               records [seg_offsets[g], seg_offsets[g+1])
+ *   seg_tok     [total_tokens*H*topk] int32: global token index of a record
+ *   seg_slot    [total_tokens*H*topk] int32 or NULL: the record's rank j in
+ *               its token's top-k list
+ *   seg_w       [total_tokens*H*topk] fp32 or NULL (requires topk_w): the
+ *               record's router probability
+ * Deterministic.  The forward pass runs the same device code.
+ */
+int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
+                           const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+                           int64_t total_tokens, int H, int N, int topk, int32_t *seg_offsets,
+                           int32_t *seg_tok, int32_t *seg_slot, float *seg_w, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSE_H */

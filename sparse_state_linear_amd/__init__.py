@@ -1,0 +1,208 @@
+"""Python binding of the gfx950 Sparse State Expansion (SSE) library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libsse_amd.so`` (built in-tree by ``sparse_state_linear_amd.build``),
+reached through the C ABI of ``include/sse.h``.  PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing, every entry point raises.
+
+Names mirror the C entry points: ``sse_forward``, ``sse_decode_step``,
+``sse_router_topk``, ``sse_group_by_partition`` and the workspace queries.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsse_amd.so")
+
+SSE_OK, SSE_ERR_INVALID_ARG, SSE_ERR_UNSUPPORTED, SSE_ERR_WORKSPACE, SSE_ERR_HIP = range(5)
+SSE_F32, SSE_BF16 = 0, 1
+
+EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
+            "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
+            "sse_group_by_partition")
+
+_lib = None
+
+
+class SSEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libsse_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m sparse_state_linear_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.sse_status_string.argtypes = [I]
+    L.sse_status_string.restype = ctypes.c_char_p
+    L.sse_version.argtypes = []
+    L.sse_version.restype = I
+    L.sse_forward_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I]
+    L.sse_forward_workspace_bytes.restype = SZ
+    L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
+                              SZ, P]
+    L.sse_forward.restype = I
+    L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
+    L.sse_decode_step.restype = I
+    L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
+    L.sse_router_topk.restype = I
+    L.sse_group_workspace_bytes.argtypes = [I64, I, I, I, I, I]
+    L.sse_group_workspace_bytes.restype = SZ
+    L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
+    L.sse_group_by_partition.restype = I
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().sse_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SSE_OK:
+        raise SSEError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSE_BF16
+    if t.dtype == torch.float32:
+        return SSE_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, shape, dtype, name, device):
+    if t.shape != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def sse_forward_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk) -> int:
+    return int(lib().sse_forward_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N,
+                                                 topk))
+
+
+def sse_forward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens, max_seqlen=None,
+                initial_states=None, *, o=None, final_states=None, topk_idx=None, topk_w=None,
+                workspace=None):
+    """Varlen SSE forward.  q/key_logits/log_alpha [T,H,c], v [T,H,d],
+    router_logits [T,H,N] (bf16 or fp32, one dtype), cu_seqlens int32
+    [S+1] on the device.  Returns (o [T,H,d] fp32, final_states
+    [S,H,N+1,c,d] fp32).  Optional preallocated outputs/workspace avoid
+    allocation; ``max_seqlen`` (host int) avoids a device->host read."""
+    dev = q.device
+    T, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (T, H, c), "q"), (key_logits, (T, H, c), "key_logits"),
+                       (log_alpha, (T, H, c), "log_alpha"), (v, (T, H, d), "v"),
+                       (router_logits, (T, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S > 0 else 0
+    if initial_states is not None:
+        _need(initial_states, (S, H, N + 1, c, d), torch.float32, "initial_states", dev)
+    if o is None:
+        o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, N + 1, c, d), dtype=torch.float32, device=dev)
+    ws_bytes = sse_forward_workspace_bytes(T, S, max_seqlen, H, c, d, N, topk)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sse_forward(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                           _ptr(router_logits), _dtype_code(q), _ptr(cu_seqlens), S,
+                           int(max_seqlen), T, H, c, d, N, topk, _ptr(initial_states), _ptr(o),
+                           _ptr(final_states), _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
+                           workspace.numel(), _stream(dev))
+    _check(st, "sse_forward")
+    return o, final_states
+
+
+def sse_decode_step(q, key_logits, v, log_alpha, router_logits, N, topk, states, *, o=None,
+                    topk_idx=None):
+    """One decode token per (b, h).  Inputs [B,H,.]; ``states``
+    [B,H,N+1,c,d] fp32 is updated in place.  Returns o [B,H,d] fp32."""
+    dev = q.device
+    B, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (B, H, c), "q"), (key_logits, (B, H, c), "key_logits"),
+                       (log_alpha, (B, H, c), "log_alpha"), (v, (B, H, d), "v"),
+                       (router_logits, (B, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    _need(states, (B, H, N + 1, c, d), torch.float32, "states", dev)
+    if o is None:
+        o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    st = lib().sse_decode_step(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                               _ptr(router_logits), _dtype_code(q), B, H, c, d, N, topk,
+                               _ptr(states), _ptr(o), _ptr(topk_idx), _stream(dev))
+    _check(st, "sse_decode_step")
+    return o
+
+
+def sse_router_topk(router_logits, topk):
+    """Router alone: [rows, N] logits -> (topk_idx int32, topk_w fp32) [rows, topk]."""
+    dev = router_logits.device
+    N = router_logits.shape[-1]
+    z = router_logits.reshape(-1, N)
+    if not z.is_contiguous():
+        raise ValueError("router_logits must be contiguous")
+    rows = z.shape[0]
+    idx = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((rows, topk), dtype=torch.float32, device=dev)
+    st = lib().sse_router_topk(_ptr(z), _dtype_code(z), rows, N, topk, _ptr(idx), _ptr(w),
+                               _stream(dev))
+    _check(st, "sse_router_topk")
+    return idx, w
+
+
+def sse_group_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, N, topk) -> int:
+    return int(lib().sse_group_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, N, topk))
+
+
+def sse_group_by_partition(topk_idx, topk_w, cu_seqlens, N, max_seqlen=None):
+    """Stable grouping of [T,H,k] top-k choices into (sequence, head,
+    partition) segments.  Returns (seg_offsets, seg_tok, seg_slot, seg_w)."""
+    dev = topk_idx.device
+    T, H, K = topk_idx.shape
+    _need(topk_idx, (T, H, K), torch.int32, "topk_idx", dev)
+    if topk_w is not None:
+        _need(topk_w, (T, H, K), torch.float32, "topk_w", dev)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S > 0 else 0
+    off = torch.empty(S * H * N + 1, dtype=torch.int32, device=dev)
+    tok = torch.empty(T * H * K, dtype=torch.int32, device=dev)
+    slot = torch.empty(T * H * K, dtype=torch.int32, device=dev)
+    sw = torch.empty(T * H * K, dtype=torch.float32, device=dev) if topk_w is not None else None
+    nbytes = sse_group_workspace_bytes(T, S, max_seqlen, H, N, K)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sse_group_by_partition(_ptr(topk_idx), _ptr(topk_w), _ptr(cu_seqlens), S,
+                                      int(max_seqlen), T, H, N, K, _ptr(off), _ptr(tok),
+                                      _ptr(slot), _ptr(sw), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "sse_group_by_partition")
+    return off, tok, slot, sw
