@@ -1,0 +1,275 @@
+"""Benchmark of the SSE hot path on one MI355X.
+
+One step = one sse_forward over the main workload (bf16, B=4, H=16, T=8192,
+c=d=128, N=16, k=2, router std 1.5): routing + counts, grouping, chunked
+GLA over all partition segments with the combine into o.  ``value`` is that
+forward's throughput in tokens/s (B*T tokens per step, all heads), with the
+inputs already resident in HBM.  The decode step (256 sequences x H=16,
+c=d=128, N=16, k=2, 64 consecutive steps) is timed in the same run and
+reported under "decode".
+
+roofline: the dominant kernel is the chunked GLA kernel; its duration comes
+from HIP events recorded around it on the library's stream during the timed
+steps (sse_trace_*).  Its algorithmic bytes per launch are the token inputs
+read once, o written once and the final states written once.
+
+cpu_baseline: the fp64 oracle (untuned) on a bounded sample of the same
+workload: a number of (sequence, head) units, over the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSE fwd tokens/s (T=8K,c=d=128,N=16,k=2) + decode tok/s; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+NAMES = ("q", "key_logits", "v", "log_alpha", "router_logits")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def forward_bytes(T, S, H, c, d, N, in_bytes=2):
+    """Algorithmic HBM bytes of one forward: token inputs read once (q, key
+    logits, log_alpha, v, router logits), o written once (fp32), final
+    states written once (fp32)."""
+    inputs = T * H * in_bytes * (3 * c + d + N)
+    return inputs + T * H * 4 * d + S * H * (N + 1) * c * d * 4
+
+
+def pass_bytes(T, S, H, c, d, parts, in_bytes=2):
+    """Algorithmic bytes of one chunked-GLA pass over `parts` partitions of
+    every (sequence, head): each token's q, key logits, log_alpha and v read
+    once, its o row written once, the pass's final states written once."""
+    return T * H * in_bytes * (3 * c + d) + T * H * 4 * d + S * H * parts * c * d * 4
+
+
+def chunk_flops(records, c, d, C=64):
+    """Algorithmic flops of the chunked form: 2 (C c/2 + C d/2 + 2 c d) per record."""
+    return records * 2 * (C * c / 2 + C * d / 2 + 2 * c * d)
+
+
+def run_forward(args, w, si, sse, torch):
+    inp = si.forward_inputs(w)
+    T = int(inp["cu_seqlens"][-1])
+    S = w.B
+    d_in = {n: to_dev(inp[n]) for n in NAMES + ("cu_seqlens",)}
+    del inp
+    o = torch.empty((T, w.H, w.d), dtype=torch.float32, device="cuda")
+    fs = torch.empty((S, w.H, w.N + 1, w.c, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sse.sse_forward_workspace_bytes(T, S, w.T, w.H, w.c, w.d, w.N, w.topk),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], w.T,
+                        o=o, final_states=fs, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sse.sse_trace_enable(True)
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stages, calls = sse.sse_trace_read()
+    sse.sse_trace_enable(False)
+    return T, S, total_ms, {k: v / max(calls, 1) for k, v in stages.items()}, calls
+
+
+def run_decode(args, si, sse, torch):
+    w = si.WORKLOADS["decode_bf16"]
+    states0 = torch.empty((w.B, w.H, w.N + 1, w.c, w.d), dtype=torch.float32, device="cuda")
+    for b in range(w.B):
+        states0[b].copy_(torch.from_numpy(si.decode_states(w, b)))
+    toks = si.decode_inputs(w)
+    d_in = {n: to_dev(toks[n]) for n in NAMES}
+    del toks
+    st = states0.clone()
+    o = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device="cuda")
+    steps = w.decode_steps
+
+    def run():
+        for t in range(steps):
+            sse.sse_decode_step(*(d_in[n][t] for n in NAMES), w.N, w.topk, st, o=o)
+
+    run()  # warm-up pass
+    best = None
+    stream = torch.cuda.current_stream()
+    for _ in range(args.decode_reps):
+        st.copy_(states0)  # restore pristine states outside the timed region
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    per_step_ms = best / steps
+    # per step: k+1 states of c*d fp32 read and written per (b, h); inputs; o
+    state_bytes = w.B * w.H * (w.topk + 1) * w.c * w.d * 4 * 2
+    in_bytes = w.B * w.H * 2 * (3 * w.c + w.d + w.N) + w.B * w.H * 4 * w.d
+    gbs = (state_bytes + in_bytes) / (per_step_ms * 1e-3) / 1e9
+    return {
+        "workload": "decode_bf16: 256 seqs x H=16, c=d=128, N=16, k=2, 64 steps, states N(0,0.1)",
+        "tokens_per_s": w.B * steps / (best * 1e-3),
+        "ms_per_step": per_step_ms,
+        "bytes_per_step": state_bytes + in_bytes,
+        "achieved_GBs": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "reps": args.decode_reps,
+    }
+
+
+def cpu_baseline(args, w, si):
+    import oracle
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    n_units = args.cpu_units or 4 * threads
+    inp = si.forward_inputs(w)
+    units = [(u % w.B, (u * 5) % w.H) for u in range(n_units)]
+    cu = inp["cu_seqlens"]
+    # gather the sampled (sequence, head) units as independent 1-head sequences
+    sel = {n: np.stack([inp[n][cu[s]:cu[s + 1], h] for (s, h) in units])[:, :, None]
+           for n in NAMES}
+    sub = {n: np.ascontiguousarray(sel[n].reshape(-1, 1, sel[n].shape[-1])) for n in NAMES}
+    lens = [int(cu[s + 1] - cu[s]) for (s, h) in units]
+    cus = np.zeros(len(units) + 1, np.int32)
+    cus[1:] = np.cumsum(lens)
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    oracle.forward(*(sub[n] for n in NAMES), cus, w.N, w.topk, threads=threads, lib=lib)
+    el = time.perf_counter() - t0
+    head_tokens = int(sum(lens))
+    return {
+        "value": head_tokens / w.H / el,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(units)} (sequence, head) units of the main workload "
+                  f"({head_tokens} head-tokens = {head_tokens / w.H:.0f} full tokens), "
+                  f"{el:.1f} s wall on {threads} threads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--cpu-units", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_state_linear_amd as sse
+    import sse_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = si.WORKLOADS["main_bf16"]
+    log("forward", w.notes)
+    T, S, total_ms, stages, calls = run_forward(args, w, si, sse, torch)
+    ms = total_ms / args.steps
+    tokens_per_s = T / (ms * 1e-3)
+    # dominant kernel: the routed pass (k of the k+1 partition reads)
+    kern = {"routed": ("chunk_kernel<64,128,128,2,1,bf16,routed>", w.N, T * w.H * w.topk),
+            "shared": ("chunk_kernel<64,128,128,2,1,bf16,shared>", 1, T * w.H)}
+    dom = max(kern, key=lambda k: stages[k])
+    kname, parts, records = kern[dom]
+    kb = pass_bytes(T, S, w.H, w.c, w.d, parts)
+    kf = chunk_flops(records, w.c, w.d)
+    k_ms = stages[dom]
+    achieved = kb / (k_ms * 1e-3) / 1e9
+    fb = forward_bytes(T, S, w.H, w.c, w.d, w.N)
+    ff = chunk_flops(T * w.H * (w.topk + 1), w.c, w.d)
+    roof_ms = max(fb / (HBM_PEAK_GBS * 1e9), ff / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    log(f"forward {ms:.3f} ms/step; stages {stages}")
+
+    decode = None
+    if not args.no_decode:
+        log("decode", si.WORKLOADS["decode_bf16"].notes)
+        decode = run_decode(args, si, sse, torch)
+        log(f"decode {decode['ms_per_step'] * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(args, w, si)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "main_bf16: SSE forward, B=4 H=16 T=8192 c=d=128 N=16 k=2 + shared "
+                        "partition, bf16 inputs, fp32 state, router logits N(0,1.5)",
+            "tokens_per_step": T,
+            "head_tokens_per_step": T * w.H,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kname,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel_ms": k_ms,
+            "algorithmic_bytes_per_launch": kb,
+            "algorithmic_flops_per_launch": kf,
+            "mfma_frac": kf / (k_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        },
+        "forward_roofline": {
+            "algorithmic_bytes": fb,
+            "algorithmic_flops": ff,
+            "roofline_ms": roof_ms,
+            "frac": roof_ms / ms,
+            "stage_ms": stages,
+            "traced_calls": calls,
+        },
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,8 +104,9 @@ size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_s
  *                             their router probabilities
  *   workspace                 device buffer of workspace_bytes >=
  *                             sse_forward_workspace_bytes(...)
- * o may not alias any input.  Accumulation of the k+1 partition reads into o
- * uses fp32 atomics, so o may differ between runs in the last bits.
+ * o may not alias any input.  The shared partition's read is stored into o
+ * first; the k routed reads are then added with fp32 atomics, so o may differ
+ * between runs in the last bits.
  */
 int sse_forward(const void *q, const void *key_logits, const void *v, const void *log_alpha,
                 const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
@@ -165,6 +166,24 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
                            int64_t total_tokens, int H, int N, int topk, int32_t *seg_offsets,
                            int32_t *seg_tok, int32_t *seg_slot, float *seg_w, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Stage tracing (profiling aid, not part of the method).  While enabled,
+ * every sse_forward records HIP events on its stream around its five
+ * stages: 0 = routing + per-block counts + key-softmax normalisers,
+ * 1 = grouping scan and scatter, 2 = local states of the pieces of long
+ * shared chains, 3 = shared partition (stores o), 4 = routed partitions
+ * (add into o).  Events of the last 256 calls are kept.  Tracing assumes
+ * one device per process.
+ *   sse_trace_enable(1) creates the events (first time) and starts a fresh
+ *   record; sse_trace_enable(0) stops recording.
+ *   sse_trace_read waits for the recorded calls to finish, writes the summed
+ *   milliseconds of stages 0..n_stages-1 into ms_per_stage, the number of
+ *   calls summed into *calls, and starts a fresh record.
+ */
+#define SSE_TRACE_STAGES 5
+int sse_trace_enable(int enable);
+int sse_trace_read(float *ms_per_stage, int n_stages, int64_t *calls);
 
 #ifdef __cplusplus
 }

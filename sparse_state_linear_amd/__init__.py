@@ -24,7 +24,7 @@ SSE_F32, SSE_BF16 = 0, 1
 
 EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
             "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
-            "sse_group_by_partition")
+            "sse_group_by_partition", "sse_trace_enable", "sse_trace_read")
 
 _lib = None
 
@@ -63,6 +63,10 @@ def lib():
     L.sse_group_workspace_bytes.restype = SZ
     L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
     L.sse_group_by_partition.restype = I
+    L.sse_trace_enable.argtypes = [I]
+    L.sse_trace_enable.restype = I
+    L.sse_trace_read.argtypes = [P, I, P]
+    L.sse_trace_read.restype = I
     _lib = L
     return L
 
@@ -206,3 +210,20 @@ def sse_group_by_partition(topk_idx, topk_w, cu_seqlens, N, max_seqlen=None):
                                       _ptr(slot), _ptr(sw), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "sse_group_by_partition")
     return off, tok, slot, sw
+
+
+TRACE_STAGES = ("route_count", "group", "shared_local", "shared", "routed")
+
+
+def sse_trace_enable(enable: bool = True):
+    """Start (or stop) recording HIP events around the forward's stages."""
+    _check(lib().sse_trace_enable(int(bool(enable))), "sse_trace_enable")
+
+
+def sse_trace_read():
+    """Summed milliseconds per forward stage since the last read, and the
+    number of calls they cover (waits for those calls to finish)."""
+    ms = (ctypes.c_float * len(TRACE_STAGES))()
+    calls = ctypes.c_int64(0)
+    _check(lib().sse_trace_read(ms, len(TRACE_STAGES), ctypes.byref(calls)), "sse_trace_read")
+    return {n: float(ms[i]) for i, n in enumerate(TRACE_STAGES)}, int(calls.value)

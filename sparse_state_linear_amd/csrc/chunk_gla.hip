@@ -1,5 +1,5 @@
 // chunk_gla.hip -- chunked gated linear attention over partition segments
-// (routed and shared) for gfx950, MFMA bf16 with fp32 state.
+// (routed and shared) for gfx950: MFMA bf16 with fp32 state.
 //
 // Method: "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记".
 // A routed partition's state only moves on the records that select it (§2.6:
@@ -8,32 +8,44 @@
 // linear attention (§2.1 eq. 6, diagonal decay) over its own subsequence, with
 // the router probability w gating both the write and the read (§2.3, eqs.
 // 12-14).  The shared partition (§2.5) is the segment of all tokens with w = 1.
-// Every token's k+1 partition reads are added into o (§2.6, gated sum back to
-// the token).
+// Every token's k+1 partition reads are summed into o (§2.6, gated sum back to
+// the token): the shared pass stores o, the routed pass adds into it.
 //
-// Chunked form used here, for a chunk of C records r = 0..C-1 with
-// b_r = sum_{u<=r} log_alpha_u (per state row j, within the chunk) and
-// b_C = b at the chunk's last record:
+// Chunked form, for a chunk of C records r = 0..C-1 with b_r = sum_{u<=r}
+// log_alpha_u (per state row j, within the chunk), b_C = b at the last record:
 //   Qt[r,j]  = q[r,j] exp(b[r,j])
 //   Kh[s,j]  = w_s kappa[s,j] exp(-b[s,j])
-//   A[r,s]   = (Qt Kh^T)[r,s] for s <= r, else 0      (own write is read)
+//   A[r,s]   = (Qt Kh^T)[r,s] for s <= r, else 0      (the own write is read)
 //   O        = w_r (A V + Qt S_in)
 //   S_out    = diag(exp(b_C)) (S_in + Kh^T V)
-// which is the token recurrence unrolled over the chunk.
+// which is the token recurrence unrolled over the chunk.  kappa comes from the
+// per-token normaliser stored by the router pass (w kappa exp(-b) is one exp2
+// of kl log2e - cr - b with cr = lnz2 - log2 w), so no row reduction is needed.
 //
 // Precision: MFMA takes bf16 operands; each operand that is not exactly a bf16
-// value is carried as LV bf16 terms (x = t0 + t1 + ...), and the products of
+// value is carried as LV bf16 terms (x = t0 + t1 + ...) and the products of
 // term pairs with level sum < LV are accumulated in fp32.  LV = 2 for bf16
 // inputs (q and v exact, ~16-bit products), LV = 3 for fp32 inputs (~24-bit).
 //
-// Block = 4 waves, one segment, all of d, chunks of kC records (64 for bf16
-// inputs, 32 for fp32 inputs).  Wave w owns state columns
-// [32w, 32w+32) (c x 32 fp32 in MFMA accumulator layout) and the matching
-// output columns.  Per chunk: (1) all waves gather the chunk's records and
-// build Qt, Kh (record-major), Kh^T (row-major) and V^T in LDS; (2) the 10
-// causal 16x16 tiles of A are spread over the waves and written back to LDS;
-// (3) each column wave accumulates O = A V + Qt S (32x32x16 MFMA), adds w_r O
-// into o with fp32 atomics, then updates its state slice.
+// Long chains: a shared segment is cut into pieces of piece_len records.  A
+// pre-pass (mode Local) computes each piece's local state (from zero) and its
+// decay product; a piece then starts from
+//   S_in(p) = D_{p-1} (... (D_0 S_init + S_loc(0)) ...) + S_loc(p-1)
+// so all pieces run in parallel.
+//
+// Block = 4 waves, one piece (shared) or segment (routed), all of d, chunks of
+// C records (64 for bf16 inputs, 32 for fp32 inputs).  Wave w owns state and
+// output columns [32w, 32w+32) (c x 32 fp32 in MFMA accumulator layout) and
+// prepares key/query columns [w c/4, (w+1) c/4) for all records of a chunk:
+// lane = (group of 4 columns, group of consecutive records), so the decay
+// cumsum is in-lane plus a short cross-lane scan and every LDS store is a
+// vector store.  Software pipeline per chunk n:
+//   start loads of chunk n+1, metadata of chunk n+2
+//   MFMA phase of chunk n  |  element-wise preparation of chunk n+1
+//   outputs of chunk n; barrier; store chunk n+1 operands; barrier;
+//   causal A tiles of chunk n+1 (16x16x32 MFMA); barrier
+// The barriers wait only for LDS traffic, so global loads and output atomics
+// stay in flight across them.
 #include "sse_launch.h"
 
 namespace sse {
@@ -42,50 +54,106 @@ namespace {
 
 constexpr int kNW = 4;        // waves per block
 constexpr int kThreads = kNW * kWave;
+constexpr int kPC = 4;        // columns per lane in the preparation layout
 
-template <int kC, int CK, int DV, int LV, int LVV>
-struct Lds {
-    static constexpr int QS = CK + 8;  // record-major row stride (elements)
-    static constexpr int TS = kC + 8;  // row stride of the record-minor arrays
-    uint16_t q[LV][kC][QS];            // Qt terms, record-major
-    union {
-        uint16_t kr[LV][kC][QS];       // Kh terms, record-major (A tiles read it)
-        uint16_t a[LV][kC][TS];        // A terms [r][s] (after the tiles are built)
-    } u;
-    uint16_t kt[LV][CK][TS];           // Kh terms transposed [j][s]
-    uint16_t vt[LVV][DV][TS];          // V terms transposed [col][s]
-    int tok[kC];
-    float w[kC];
-    float ebc[CK];                     // exp(b_C) per state row
-    float coltot[kNW][CK];             // per-wave sums of log_alpha*log2(e)
+enum { kModeLocal = 0, kModeShared = 1, kModeRouted = 2 };
+
+template <int C, int CK, int DV, int LV, int LVV>
+struct Smem {
+    static constexpr int QS = CK + 8;   // record-major row stride (elements)
+    static constexpr int TS = C + 8;    // record-minor row stride (elements)
+    uint16_t q[LV][C][QS];              // Qt terms [r][j]
+    uint16_t kr[LV][C][QS];             // Kh terms [s][j]
+    uint16_t kt[LV][CK][TS];            // Kh terms [j][s]
+    uint16_t vt[LVV][DV][TS];           // V terms [col][s]
+    uint16_t a[LV][C][TS];              // A terms [r][s]
+    float ebc[CK];                      // exp(b_C) per state row
+    int mtok[3][C];                     // record token; ~token marks a padded record
+    float mcr[3][C];                    // exponent offset lnz2 - log2 w (+inf if padded)
+    float mw[3][C];                     // read gate (0 if padded)
 };
 
-template <typename TIn, int CPL>
-struct Row;  // loads CPL consecutive elements of one input row
+// Four consecutive input values of one row.
+template <typename TIn>
+struct Vec4;
 template <>
-struct Row<bf16_t, 1> {
-    static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[1]) { x[0] = to_f32(p[0]); }
-};
-template <>
-struct Row<bf16_t, 2> {
-    static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[2]) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-        x[0] = __uint_as_float(u << 16);
-        x[1] = __uint_as_float(u & 0xffff0000u);
+struct Vec4<bf16_t> {
+    uint2 u;
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = (e < 2) ? u.x : u.y;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ __forceinline__ uint16_t bits(int e) const {
+        const uint32_t w = (e < 2) ? u.x : u.y;
+        return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
     }
 };
 template <>
-struct Row<float, 1> {
-    static __device__ __forceinline__ void load(const float* p, float (&x)[1]) { x[0] = p[0]; }
-};
-template <>
-struct Row<float, 2> {
-    static __device__ __forceinline__ void load(const float* p, float (&x)[2]) {
-        const float2 u = *reinterpret_cast<const float2*>(p);
-        x[0] = u.x;
-        x[1] = u.y;
+struct Vec4<float> {
+    float4 f;
+    __device__ __forceinline__ void load(const float* p) { f = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
     }
+    __device__ __forceinline__ uint16_t bits(int) const { return 0; }
 };
+
+// Preparation layout: CW columns per wave, NCG groups of 4 columns, NG
+// groups of RPG consecutive records.
+template <int C, int CKD>
+struct Geo {
+    static constexpr int CW = CKD / kNW;
+    static constexpr int NCG = CW / kPC;
+    static constexpr int NG = kWave / NCG;
+    static constexpr int RPG = C / NG;
+    static_assert(CW % kPC == 0 && RPG >= 1 && C % NG == 0, "unsupported shape");
+};
+
+template <int L>
+__device__ __forceinline__ void split4(const float (&x)[kPC], uint2 (&out)[L]) {
+    float r[kPC];
+#pragma unroll
+    for (int e = 0; e < kPC; e++) r[e] = x[e];
+#pragma unroll
+    for (int l = 0; l < L; l++) {
+        uint16_t h[kPC];
+#pragma unroll
+        for (int e = 0; e < kPC; e++) {
+            h[e] = f32_to_bf16_bits(r[e]);
+            if (l + 1 < L) r[e] -= bf16_bits_to_f32(h[e]);
+        }
+        out[l].x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        out[l].y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    }
+}
+
+__device__ __forceinline__ uint16_t elem(const uint2& v, int e) {
+    const uint32_t w = (e < 2) ? v.x : v.y;
+    return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// Store R consecutive 16-bit values (R in {1, 2, 4, 8}).
+template <int R>
+__device__ __forceinline__ void store_run(uint16_t* p, const uint16_t (&v)[R]) {
+    if constexpr (R == 1) {
+        p[0] = v[0];
+    } else if constexpr (R == 2) {
+        *reinterpret_cast<uint32_t*>(p) = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+    } else if constexpr (R == 4) {
+        uint2 x;
+        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+        *reinterpret_cast<uint2*>(p) = x;
+    } else {
+        uint4 x;
+        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+        x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+        x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+        *reinterpret_cast<uint4*>(p) = x;
+    }
+}
 
 __device__ __forceinline__ u16x8 lds8(const uint16_t* p) {
     return *reinterpret_cast<const u16x8*>(p);
@@ -96,7 +164,7 @@ __device__ __forceinline__ u16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) 
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Accumulate sum over term pairs (x, y) with x + y < max(LA, LB) of A_x B_y.
+// sum over term pairs (x, y) with x + y < max(LA, LB) of A_x B_y
 template <int LA, int LB>
 __device__ __forceinline__ void mma32_terms(const u16x8 (&a)[LA], const u16x8 (&b)[LB], f32x16& c) {
     constexpr int L = LA > LB ? LA : LB;
@@ -116,14 +184,17 @@ __device__ __forceinline__ void mma16_terms(const u16x8 (&a)[LA], const u16x8 (&
             if (x + y < L) c = mfma16(a[x], b[y], c);
 }
 
-}  // namespace
+// Barrier for LDS hazards only: global loads and atomics may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-// Causal 16x16 tile ti of A^T (s-tile st, r-tile rt).  The first
-// nt(nt+1)/2 tiles have st <= rt; the remaining nt/2 are the tiles just
-// above the diagonal inside each 32-record block, which are stored as zeros.
-template <int kC>
+// Causal 16x16 tile ti of A^T (s-tile st, r-tile rt).  The first nt(nt+1)/2
+// tiles have st <= rt; the remaining nt/2 are the tiles just above the
+// diagonal inside each 32-record block, stored as zeros.
+template <int C>
 __device__ __forceinline__ void a_tile(int ti, int& st, int& rt) {
-    constexpr int nt = kC / 16, ncausal = nt * (nt + 1) / 2;
+    constexpr int nt = C / 16, ncausal = nt * (nt + 1) / 2;
     if (ti < ncausal) {
         rt = 0;
         while ((rt + 1) * (rt + 2) / 2 <= ti) rt++;
@@ -134,302 +205,301 @@ __device__ __forceinline__ void a_tile(int ti, int& st, int& rt) {
     }
 }
 
-template <int kC, int CK, int DV, int LV, int LVV, typename TIn>
-__global__ __launch_bounds__(kThreads, 1) void chunk_gla_kernel(const ChunkArgs a) {
-    using L = Lds<kC, CK, DV, LV, LVV>;
-    constexpr int kRecPerWave = kC / kNW;            // records per wave in the prep phase
-    constexpr int kOT = kC / 32;                     // 32-record output tiles
-    constexpr int NS = DV / 32;                      // column waves
-    constexpr int CPL = CK >= 64 ? CK / 64 : 1;      // prep columns per lane
-    constexpr int PACT = CK >= 64 ? 64 : CK;         // active prep lanes
-    constexpr int VPL = DV >= 64 ? DV / 64 : 1;
-    constexpr int VACT = DV >= 64 ? 64 : DV;
-    constexpr int RT_N = CK / 32;                    // 32-row tiles of the state
-    constexpr int QS = L::QS, TS = L::TS;
-    __shared__ __attribute__((aligned(16))) L sm;
+}  // namespace
+
+template <int C, int CK, int DV, int LV, int LVV, typename TIn, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
+    using SM = Smem<C, CK, DV, LV, LVV>;
+    using GK = Geo<C, CK>;
+    using GV = Geo<C, DV>;
+    constexpr bool kLocal = MODE == kModeLocal;
+    constexpr int kOT = C / 32;          // 32-record output tiles
+    constexpr int NS = DV / 32;          // column waves
+    constexpr int RT_N = CK / 32;        // 32-row tiles of the state
+    __shared__ __attribute__((aligned(16))) SM sm;
 
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int hh = lane / 32, l32 = lane % 32;
     const int H = a.H, N = a.N;
-    const int SH = a.num_seqs * H;
+    const bool col_wave = NS == kNW || wv < NS;  // this wave owns state columns
 
-    // ---- which segment this block runs
-    const int unit = blockIdx.x;
-    int s, h, part;
-    int64_t rec0, nrec;
-    bool shared;
-    if (unit < SH) {
-        shared = true;
-        s = unit / H;
-        h = unit % H;
-        part = N;
-        rec0 = a.cu[s];
-        nrec = a.cu[s + 1] - rec0;
-    } else {
-        shared = false;
-        const int g = unit - SH;
+    // ---------------- which records this block runs ----------------
+    int s, h, part, piece = 0, npieces = 1;
+    int64_t lo, n;
+    if constexpr (MODE == kModeRouted) {
+        const int g = blockIdx.x;
         part = g % N;
         s = g / N / H;
         h = g / N % H;
-        rec0 = a.seg_offsets[g];
-        nrec = a.seg_offsets[g + 1] - rec0;
+        lo = a.seg_offsets[g];
+        n = a.seg_offsets[g + 1] - lo;
+    } else {
+        const int sh = blockIdx.x;
+        s = sh / H;
+        h = sh % H;
+        part = N;
+        piece = blockIdx.y;
+        const int64_t t0 = a.cu[s], len = a.cu[s + 1] - t0;
+        npieces = len > 0 ? (int)((len + a.piece_len - 1) / a.piece_len) : 1;
+        if (piece >= npieces - (kLocal ? 1 : 0)) return;  // uniform
+        lo = t0 + (int64_t)piece * a.piece_len;
+        n = min<int64_t>(a.piece_len, len - (int64_t)piece * a.piece_len);
+        if (n < 0) n = 0;
     }
+    const int64_t nchunks = (n + C - 1) / C;
+    const bool last_piece = piece == npieces - 1;
+    const int64_t sbase = (((int64_t)s * H + h) * (N + 1) + part) * CK * DV;
+    const int64_t abase = ((int64_t)s * H + h) * a.max_pieces;
 
     const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
     const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
     const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
     const TIn* __restrict__ gl = static_cast<const TIn*>(a.la);
 
-    // ---- state slice of this wave: rows 32*RT + 8*(i/4) + 4*(lane/32) + i%4,
-    //      column 32*wv + lane%32
-    const int64_t sbase = (((int64_t)s * H + h) * (N + 1) + part) * CK * DV;
-    const int hh = lane / 32, l32 = lane % 32;
+    // ---------------- initial state of this wave's column slice ----------------
+    // rows 32 rt + 8 (i/4) + 4 hh + i%4, column 32 wv + l32
     f32x16 S[RT_N];
 #pragma unroll
     for (int rt = 0; rt < RT_N; rt++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            float x = 0.f;
-            if (wv < NS && a.init) {
+        for (int i = 0; i < 16; i++) S[rt][i] = 0.f;
+    if (col_wave && !kLocal) {
+        const int col = 32 * wv + l32;
+#pragma unroll
+        for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
                 const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
-                x = a.init[sbase + (int64_t)row * DV + 32 * wv + l32];
+                float x = a.init ? a.init[sbase + (int64_t)row * DV + col] : 0.f;
+                for (int p = 0; p < piece; p++) {
+                    const int64_t ab = abase + p;
+                    x = a.agg_D[ab * CK + row] * x + a.agg_S[(ab * CK + row) * DV + col];
+                }
+                S[rt][i] = x;
             }
-            S[rt][i] = x;
-        }
+    }
 
-    for (int64_t base = 0; base < nrec; base += kC) {
-        __syncthreads();  // previous chunk fully consumed
-        if (tid < kC) {
-            const int64_t r = base + tid;
-            int tok = -1;
-            float w = 0.f;
-            if (r < nrec) {
-                tok = shared ? (int)(rec0 + r) : a.seg_tok[rec0 + r];
-                w = shared ? 1.f : a.seg_w[rec0 + r];
-            }
-            sm.tok[tid] = tok;
-            sm.w[tid] = w;
+    // ---------------- metadata of one chunk ----------------
+    // Every thread loads (record index tid % C, clamped into the piece) so the
+    // loads carry no branch; threads < C store it after the next barrier.
+    // Padded records keep a real token (so every address stays valid), marked
+    // by storing its bitwise complement.
+    auto meta_load = [&](int64_t chunk, int& tok, float& cr, float& w) {
+        const int64_t idx = chunk * C + (tid % C);
+        const int64_t ci = idx < n ? idx : (n > 0 ? n - 1 : 0);
+        if constexpr (MODE == kModeRouted) {
+            tok = a.seg_tok[lo + ci];
+            cr = a.seg_cr[lo + ci];
+            w = a.seg_w[lo + ci];
+        } else {
+            tok = (int)(lo + ci);
+            cr = a.lnz2[((int64_t)tok) * H + h];
+            w = 1.f;
         }
-        __syncthreads();
+    };
+    auto meta_store = [&](int64_t chunk, int buf, int tok, float cr, float w) {
+        const bool valid = chunk * C + tid < n;
+        sm.mtok[buf][tid] = valid ? tok : ~tok;
+        sm.mcr[buf][tid] = valid ? cr : INFINITY;
+        sm.mw[buf][tid] = valid ? w : 0.f;
+    };
+    auto tok_of = [](int m) { return m >= 0 ? m : ~m; };
 
-        // ================= phase 1: gather + elementwise prep =================
-        {
-            const int r0 = wv * kRecPerWave;
-            const bool act = lane < PACT;
-            const int j0 = lane * CPL;
-            float qv[kRecPerWave][CPL], kv[kRecPerWave][CPL], lv[kRecPerWave][CPL];
+    // ---------------- raw loads of one chunk into registers ----------------
+    constexpr int RPG = GK::RPG, RPGV = GV::RPG;
+    const int cg = lane % GK::NCG, gk_ = lane / GK::NCG;
+    const int j0 = wv * GK::CW + cg * kPC, r0 = gk_ * RPG;
+    const int cgv = lane % GV::NCG, gv_ = lane / GV::NCG;
+    const int c0v = wv * GV::CW + cgv * kPC, r0v = gv_ * RPGV;
+    Vec4<TIn> rq[RPG], rk[RPG], rl[RPG], rv[RPGV];
+    auto raw_load = [&](int buf) {
 #pragma unroll
-            for (int r = 0; r < kRecPerWave; r++) {
-                const int tok = sm.tok[r0 + r];
-                if (tok >= 0 && act) {
-                    const int64_t off = ((int64_t)tok * H + h) * CK + j0;
-                    Row<TIn, CPL>::load(gq + off, qv[r]);
-                    Row<TIn, CPL>::load(gk + off, kv[r]);
-                    Row<TIn, CPL>::load(gl + off, lv[r]);
-                } else {
+        for (int i = 0; i < RPG; i++) {
+            const int64_t off = ((int64_t)tok_of(sm.mtok[buf][r0 + i]) * H + h) * CK + j0;
+            if constexpr (!kLocal) rq[i].load(gq + off);
+            rk[i].load(gk + off);
+            rl[i].load(gl + off);
+        }
 #pragma unroll
-                    for (int e = 0; e < CPL; e++) qv[r][e] = kv[r][e] = lv[r][e] = 0.f;
-                }
-            }
-            // value rows -> V^T terms
-            {
-                const int c0 = lane * VPL;
+        for (int i = 0; i < RPGV; i++)
+            rv[i].load(gv + ((int64_t)tok_of(sm.mtok[buf][r0v + i]) * H + h) * DV + c0v);
+    };
+
+    // ---------------- element-wise preparation into registers ----------------
+    uint2 pq[RPG][LV], pk[RPG][LV];
+    float ebc_own[kPC];
+    float btot[kPC] = {0.f, 0.f, 0.f, 0.f};
+    auto prep = [&](int buf) {
+        float run[kPC] = {0.f, 0.f, 0.f, 0.f};
+        float bb[RPG][kPC];
 #pragma unroll
-                for (int r = 0; r < kRecPerWave; r += 2) {
-                    const int tA = sm.tok[r0 + r], tB = sm.tok[r0 + r + 1];
-                    if (lane < VACT) {
-                        float xa[VPL], xb[VPL];
-                        if (tA >= 0) Row<TIn, VPL>::load(gv + ((int64_t)tA * H + h) * DV + c0, xa);
-                        else for (int e = 0; e < VPL; e++) xa[e] = 0.f;
-                        if (tB >= 0) Row<TIn, VPL>::load(gv + ((int64_t)tB * H + h) * DV + c0, xb);
-                        else for (int e = 0; e < VPL; e++) xb[e] = 0.f;
+        for (int i = 0; i < RPG; i++) {
+            const bool valid = sm.mtok[buf][r0 + i] >= 0;
 #pragma unroll
-                        for (int e = 0; e < VPL; e++) {
-                            uint16_t ta[LVV], tb[LVV];
-                            split_levels<LVV>(xa[e], ta);
-                            split_levels<LVV>(xb[e], tb);
-#pragma unroll
-                            for (int l = 0; l < LVV; l++)
-                                *reinterpret_cast<uint32_t*>(&sm.vt[l][c0 + e][r0 + r]) =
-                                    (uint32_t)ta[l] | ((uint32_t)tb[l] << 16);
-                        }
-                    }
-                }
-            }
-            // row max of the key logits (softmax stabiliser), per record
-            float mrow[kRecPerWave];
-#pragma unroll
-            for (int r = 0; r < kRecPerWave; r++) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < CPL; e++) mx = act ? fmaxf(mx, kv[r][e]) : mx;
-                mrow[r] = wave_max(mx);
-            }
-            // in-chunk cumulative log-decay (log2 units), per column
-            float b2[kRecPerWave][CPL], run[CPL];
-#pragma unroll
-            for (int e = 0; e < CPL; e++) run[e] = 0.f;
-#pragma unroll
-            for (int r = 0; r < kRecPerWave; r++)
-#pragma unroll
-                for (int e = 0; e < CPL; e++) {
-                    run[e] = fmaf(lv[r][e], kLog2e, run[e]);
-                    b2[r][e] = run[e];
-                }
-            if (act)
-#pragma unroll
-                for (int e = 0; e < CPL; e++) sm.coltot[wv][j0 + e] = run[e];
-            __syncthreads();
-            float offs[CPL], tot[CPL];
-#pragma unroll
-            for (int e = 0; e < CPL; e++) {
-                offs[e] = 0.f;
-                tot[e] = 0.f;
-                if (act)
-#pragma unroll
-                    for (int w2 = 0; w2 < kNW; w2++) {
-                        const float x = sm.coltot[w2][j0 + e];
-                        if (w2 < wv) offs[e] += x;
-                        tot[e] += x;
-                    }
-            }
-            if (wv == 0 && act)
-#pragma unroll
-                for (int e = 0; e < CPL; e++) sm.ebc[j0 + e] = exp2f(tot[e]);
-            // Qt, unnormalised exp(kl - m - b), softmax denominators
-            float eq[kRecPerWave][CPL], ek[kRecPerWave][CPL];
-#pragma unroll
-            for (int r = 0; r < kRecPerWave; r++) {
-                float part = 0.f;
-#pragma unroll
-                for (int e = 0; e < CPL; e++) {
-                    const float bb = b2[r][e] + offs[e];
-                    const float eb = exp2f(bb);
-                    eq[r][e] = qv[r][e] * eb;
-                    const float x = exp2f((kv[r][e] - mrow[r]) * kLog2e - bb);
-                    ek[r][e] = x;
-                    if (act) part = fmaf(x, eb, part);
-                }
-                const float den = wave_sum(part);
-                const float scale = sm.w[r0 + r] / den;
-#pragma unroll
-                for (int e = 0; e < CPL; e++) ek[r][e] *= scale;
-            }
-            // store the terms
-            if (act) {
-#pragma unroll
-                for (int r = 0; r < kRecPerWave; r++) {
-                    uint16_t tq[CPL][LV], tk[CPL][LV];
-#pragma unroll
-                    for (int e = 0; e < CPL; e++) {
-                        split_levels<LV>(eq[r][e], tq[e]);
-                        split_levels<LV>(ek[r][e], tk[e]);
-                    }
-#pragma unroll
-                    for (int l = 0; l < LV; l++)
-#pragma unroll
-                        for (int e = 0; e < CPL; e++) {
-                            sm.q[l][r0 + r][j0 + e] = tq[e][l];
-                            sm.u.kr[l][r0 + r][j0 + e] = tk[e][l];
-                        }
-                }
-#pragma unroll
-                for (int r = 0; r < kRecPerWave; r += 2) {
-#pragma unroll
-                    for (int e = 0; e < CPL; e++) {
-                        uint16_t ta[LV], tb[LV];
-                        split_levels<LV>(ek[r][e], ta);
-                        split_levels<LV>(ek[r + 1][e], tb);
-#pragma unroll
-                        for (int l = 0; l < LV; l++)
-                            *reinterpret_cast<uint32_t*>(&sm.kt[l][j0 + e][r0 + r]) =
-                                (uint32_t)ta[l] | ((uint32_t)tb[l] << 16);
-                    }
-                }
+            for (int e = 0; e < kPC; e++) {
+                const float x = valid ? rl[i].get(e) : 0.f;
+                run[e] = fmaf(x, kLog2e, run[e]);
+                bb[i][e] = run[e];
             }
         }
-        __syncthreads();
-
-        // ================= phase 2: causal A tiles (16x16x32 MFMA) =============
-        constexpr int kTiles = (kC / 16) * (kC / 16 + 1) / 2 + kC / 32;
-        constexpr int kTilesPerWave = (kTiles + kNW - 1) / kNW;
-        const int g16 = lane / 16, l16 = lane % 16;
-        f32x4 at[kTilesPerWave];
+        float excl[kPC];
 #pragma unroll
-        for (int u = 0; u < kTilesPerWave; u++) {
+        for (int e = 0; e < kPC; e++) {
+            float inc = run[e];
+#pragma unroll
+            for (int off = GK::NCG; off < kWave; off <<= 1) {
+                const float y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            excl[e] = inc - run[e];
+            const float tot = __shfl(inc, kWave - GK::NCG + cg, kWave);
+            ebc_own[e] = __builtin_amdgcn_exp2f(tot);
+            if constexpr (kLocal) btot[e] += tot;
+        }
+#pragma unroll
+        for (int i = 0; i < RPG; i++) {
+            const float cr = sm.mcr[buf][r0 + i];
+            float xq[kPC], xk[kPC];
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                const float b = bb[i][e] + excl[e];
+                if constexpr (!kLocal) xq[e] = rq[i].get(e) * __builtin_amdgcn_exp2f(b);
+                xk[e] = __builtin_amdgcn_exp2f(fmaf(rk[i].get(e), kLog2e, -cr) - b);
+            }
+            if constexpr (!kLocal) split4<LV>(xq, pq[i]);
+            split4<LV>(xk, pk[i]);
+        }
+    };
+    auto prep_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < RPG; i++)
+#pragma unroll
+            for (int l = 0; l < LV; l++) {
+                if constexpr (!kLocal) {
+                    *reinterpret_cast<uint2*>(&sm.q[l][r0 + i][j0]) = pq[i][l];
+                    *reinterpret_cast<uint2*>(&sm.kr[l][r0 + i][j0]) = pk[i][l];
+                }
+            }
+#pragma unroll
+        for (int e = 0; e < kPC; e++)
+#pragma unroll
+            for (int l = 0; l < LV; l++) {
+                uint16_t run[RPG];
+#pragma unroll
+                for (int i = 0; i < RPG; i++) run[i] = elem(pk[i][l], e);
+                store_run<RPG>(&sm.kt[l][j0 + e][r0], run);
+            }
+        // V^T terms
+#pragma unroll
+        for (int e = 0; e < kPC; e++) {
+            if constexpr (LVV == 1) {
+                uint16_t run[RPGV];
+#pragma unroll
+                for (int i = 0; i < RPGV; i++) run[i] = rv[i].bits(e);
+                store_run<RPGV>(&sm.vt[0][c0v + e][r0v], run);
+            } else {
+                uint16_t run[LVV][RPGV];
+#pragma unroll
+                for (int i = 0; i < RPGV; i++) {
+                    float x = rv[i].get(e);
+#pragma unroll
+                    for (int l = 0; l < LVV; l++) {
+                        run[l][i] = f32_to_bf16_bits(x);
+                        if (l + 1 < LVV) x -= bf16_bits_to_f32(run[l][i]);
+                    }
+                }
+#pragma unroll
+                for (int l = 0; l < LVV; l++) store_run<RPGV>(&sm.vt[l][c0v + e][r0v], run[l]);
+            }
+        }
+        if (gk_ == 0)
+#pragma unroll
+            for (int e = 0; e < kPC; e++) sm.ebc[j0 + e] = ebc_own[e];
+    };
+
+    // ---------------- causal A tiles (16x16x32 MFMA) ----------------
+    const int g16 = lane / 16, l16 = lane % 16;
+    auto a_tiles = [&]() {
+        constexpr int kTiles = (C / 16) * (C / 16 + 1) / 2 + C / 32;
+        constexpr int kTPW = (kTiles + kNW - 1) / kNW;
+#pragma unroll
+        for (int u = 0; u < kTPW; u++) {
             const int ti = wv + kNW * u;
-            int st = 1, rt = 0;
-            if (ti < kTiles) a_tile<kC>(ti, st, rt);
+            if (ti >= kTiles) break;  // uniform per wave
+            int st, rt;
+            a_tile<C>(ti, st, rt);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (ti < kTiles && st <= rt) {
+            if (st <= rt) {
 #pragma unroll
                 for (int kk = 0; kk < CK / 32; kk++) {
                     u16x8 ka[LV], qb[LV];
 #pragma unroll
                     for (int l = 0; l < LV; l++) {
-                        ka[l] = lds8(&sm.u.kr[l][16 * st + l16][32 * kk + 8 * g16]);
+                        ka[l] = lds8(&sm.kr[l][16 * st + l16][32 * kk + 8 * g16]);
                         qb[l] = lds8(&sm.q[l][16 * rt + l16][32 * kk + 8 * g16]);
                     }
                     mma16_terms<LV, LV>(ka, qb, acc);
                 }
-                // lane holds r = 16rt + l16 and s = 16st + 4*g16 + i; keep s <= r
-                const int r = 16 * rt + l16;
+                // lane holds r = 16 rt + l16 and s = 16 st + 4 g16 + i; keep s <= r
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    if (16 * st + 4 * g16 + i > r) acc[i] = 0.f;
+                    if (16 * st + 4 * g16 + i > 16 * rt + l16) acc[i] = 0.f;
             }
-            at[u] = acc;
-        }
-        __syncthreads();  // everyone is done reading Kh (record-major)
-#pragma unroll
-        for (int u = 0; u < kTilesPerWave; u++) {
-            const int ti = wv + kNW * u;
-            if (ti >= kTiles) continue;
-            int st, rt;
-            a_tile<kC>(ti, st, rt);
             const int r = 16 * rt + l16, s0 = 16 * st + 4 * g16;
             uint16_t t4[4][LV];
 #pragma unroll
-            for (int i = 0; i < 4; i++) split_levels<LV>(at[u][i], t4[i]);
+            for (int i = 0; i < 4; i++) {
+                float x = acc[i];
+#pragma unroll
+                for (int l = 0; l < LV; l++) {
+                    t4[i][l] = f32_to_bf16_bits(x);
+                    if (l + 1 < LV) x -= bf16_bits_to_f32(t4[i][l]);
+                }
+            }
 #pragma unroll
             for (int l = 0; l < LV; l++) {
-                u16x4 pk = {t4[0][l], t4[1][l], t4[2][l], t4[3][l]};
-                *reinterpret_cast<u16x4*>(&sm.u.a[l][r][s0]) = pk;
+                u16x4 pkd = {t4[0][l], t4[1][l], t4[2][l], t4[3][l]};
+                *reinterpret_cast<u16x4*>(&sm.a[l][r][s0]) = pkd;
             }
         }
-        __syncthreads();
+    };
 
-        // ================= phase 3: outputs and state (column waves) ===========
-        if (wv < NS) {
-            f32x16 O[kOT];
+    // ---------------- MFMA phase of one chunk ----------------
+    f32x16 O[kOT];
+    const int col = 32 * wv + l32;
+    auto mma = [&]() {
+        if constexpr (!kLocal) {
 #pragma unroll
             for (int t = 0; t < kOT; t++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) O[t][i] = 0.f;
-            // O += Qt S_in.  The B operand is this wave's own state registers:
-            // k-step kk uses rows 16kk + {4hh+e, 8+4hh+e} (e < 4), which are
-            // registers 8*(kk%2) + 0..7 of tile kk/2.
+            // O += Qt S_in: the B operand is this wave's state registers; k-step
+            // kk uses rows 16kk + {4hh+e, 8+4hh+e} (e < 4) = registers
+            // 8 (kk%2) + 0..7 of tile kk/2.
 #pragma unroll
             for (int kk = 0; kk < CK / 16; kk++) {
                 u16x8 sb[LV];
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    uint16_t t[LV];
-                    split_levels<LV>(S[kk / 2][8 * (kk % 2) + e], t);
+                    float x = S[kk / 2][8 * (kk % 2) + e];
 #pragma unroll
-                    for (int l = 0; l < LV; l++) sb[l][e] = t[l];
+                    for (int l = 0; l < LV; l++) {
+                        const uint16_t t = f32_to_bf16_bits(x);
+                        sb[l][e] = t;
+                        if (l + 1 < LV) x -= bf16_bits_to_f32(t);
+                    }
                 }
-                const int j0 = 16 * kk + 4 * hh;
+                const int jq = 16 * kk + 4 * hh;
 #pragma unroll
                 for (int t2 = 0; t2 < kOT; t2++) {
                     const int r = 32 * t2 + l32;
                     u16x8 qa[LV];
 #pragma unroll
-                    for (int l = 0; l < LV; l++) qa[l] = lds4x2(&sm.q[l][r][j0], &sm.q[l][r][j0 + 8]);
+                    for (int l = 0; l < LV; l++) qa[l] = lds4x2(&sm.q[l][r][jq], &sm.q[l][r][jq + 8]);
                     mma32_terms<LV, LV>(qa, sb, O[t2]);
                 }
             }
-            // O += A V (causal: row tile t2 needs s < 32 (t2 + 1))
-            const int col = 32 * wv + l32;
+            // O += A V (row tile t2 needs s < 32 (t2 + 1))
 #pragma unroll
             for (int t2 = 0; t2 < kOT; t2++)
 #pragma unroll
@@ -437,63 +507,152 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_gla_kernel(const ChunkArgs 
                     const int r = 32 * t2 + l32, s0 = 16 * ks + 8 * hh;
                     u16x8 aa[LV], vb[LVV];
 #pragma unroll
-                    for (int l = 0; l < LV; l++) aa[l] = lds8(&sm.u.a[l][r][s0]);
+                    for (int l = 0; l < LV; l++) aa[l] = lds8(&sm.a[l][r][s0]);
 #pragma unroll
                     for (int l = 0; l < LVV; l++) vb[l] = lds8(&sm.vt[l][col][s0]);
                     mma32_terms<LV, LVV>(aa, vb, O[t2]);
                 }
-            // o[token] += w_r O[r]
+        }
+        // S_out = diag(exp(b_C)) (S_in + Kh^T V)
+#pragma unroll
+        for (int rt = 0; rt < RT_N; rt++) {
+#pragma unroll
+            for (int ks = 0; ks < C / 16; ks++) {
+                const int j = 32 * rt + l32, s0 = 16 * ks + 8 * hh;
+                u16x8 ka[LV], vb[LVV];
+#pragma unroll
+                for (int l = 0; l < LV; l++) ka[l] = lds8(&sm.kt[l][j][s0]);
+#pragma unroll
+                for (int l = 0; l < LVV; l++) vb[l] = lds8(&sm.vt[l][col][s0]);
+                mma32_terms<LV, LVV>(ka, vb, S[rt]);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const float4 e4 =
+                    *reinterpret_cast<const float4*>(&sm.ebc[32 * rt + 8 * q4 + 4 * hh]);
+                S[rt][4 * q4 + 0] *= e4.x;
+                S[rt][4 * q4 + 1] *= e4.y;
+                S[rt][4 * q4 + 2] *= e4.z;
+                S[rt][4 * q4 + 3] *= e4.w;
+            }
+        }
+    };
+    // o[token] (+)= w_r O[r], branch-free.  Routed: a padded record adds
+    // 0 * O to a real row.  Shared: a padded record's store goes to a dummy row.
+    auto outputs = [&](int buf) {
+        if constexpr (!kLocal) {
 #pragma unroll
             for (int t2 = 0; t2 < kOT; t2++)
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * t2 + 8 * (i / 4) + 4 * hh + (i % 4);
-                    const int tok = sm.tok[r];
-                    if (tok >= 0)
-                        atomic_add_f32(a.o + ((int64_t)tok * H + h) * DV + col, sm.w[r] * O[t2][i]);
+                for (int q4 = 0; q4 < 4; q4++) {
+                    const int rb = 32 * t2 + 8 * q4 + 4 * hh;
+                    const int4 tk = *reinterpret_cast<const int4*>(&sm.mtok[buf][rb]);
+                    const float4 wr = *reinterpret_cast<const float4*>(&sm.mw[buf][rb]);
+                    const int tks[4] = {tk.x, tk.y, tk.z, tk.w};
+                    const float ws[4] = {wr.x, wr.y, wr.z, wr.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float val = ws[e] * O[t2][4 * q4 + e];
+                        const int64_t row = (int64_t)tok_of(tks[e]) * H + h;
+                        if constexpr (MODE == kModeShared) {
+                            const bool valid = tks[e] >= 0;
+                            float* base = valid ? a.o : a.trash;
+                            base[(valid ? row * DV : 0) + col] = val;
+                        } else {
+                            atomic_add_f32(a.o + row * DV + col, val);
+                        }
+                    }
                 }
-            // S_out = diag(exp(b_C)) (S_in + Kh^T V)
-#pragma unroll
-            for (int rt = 0; rt < RT_N; rt++) {
-#pragma unroll
-                for (int ks = 0; ks < kC / 16; ks++) {
-                    const int j = 32 * rt + l32, s0 = 16 * ks + 8 * hh;
-                    u16x8 ka[LV], vb[LVV];
-#pragma unroll
-                    for (int l = 0; l < LV; l++) ka[l] = lds8(&sm.kt[l][j][s0]);
-#pragma unroll
-                    for (int l = 0; l < LVV; l++) vb[l] = lds8(&sm.vt[l][col][s0]);
-                    mma32_terms<LV, LVV>(ka, vb, S[rt]);
-                }
-#pragma unroll
-                for (int i = 0; i < 16; i++) S[rt][i] *= sm.ebc[32 * rt + 8 * (i / 4) + 4 * hh + (i % 4)];
+        }
+    };
+
+    // ---------------- pipeline ----------------
+    if (nchunks > 0) {
+        int mt = 0;
+        float mc = 0.f, mwv = 0.f;
+        meta_load(0, mt, mc, mwv);
+        if (tid < C) meta_store(0, 0, mt, mc, mwv);
+        meta_load(1, mt, mc, mwv);
+        if (tid < C) meta_store(1, 1, mt, mc, mwv);
+        lds_barrier();
+        raw_load(0);
+        prep(0);
+        prep_store();
+        lds_barrier();
+        if constexpr (!kLocal) {
+            a_tiles();
+            lds_barrier();
+        }
+        for (int64_t c = 0; c + 1 < nchunks; c++) {
+            const int cur = (int)(c % 3), nxt = (int)((c + 1) % 3), nn = (int)((c + 2) % 3);
+            raw_load(nxt);
+            meta_load(c + 2, mt, mc, mwv);
+            if (col_wave) mma();
+            prep(nxt);
+            if (col_wave) outputs(cur);
+            lds_barrier();
+            prep_store();
+            if (tid < C) meta_store(c + 2, nn, mt, mc, mwv);
+            lds_barrier();
+            if constexpr (!kLocal) {
+                a_tiles();
+                lds_barrier();
             }
+        }
+        if (col_wave) {
+            mma();
+            outputs((int)((nchunks - 1) % 3));
         }
     }
 
-    if (wv < NS) {
+    // ---------------- results ----------------
+    if constexpr (kLocal) {
+        // local state and decay product of this piece
+        if (col_wave) {
+#pragma unroll
+            for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    a.agg_S[((abase + piece) * CK + row) * DV + col] = S[rt][i];
+                }
+        }
+        if (gk_ == 0)
+#pragma unroll
+            for (int e = 0; e < kPC; e++)
+                a.agg_D[(abase + piece) * CK + j0 + e] = __builtin_amdgcn_exp2f(btot[e]);
+    } else if (col_wave && last_piece) {
 #pragma unroll
         for (int rt = 0; rt < RT_N; rt++)
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
-                a.final_states[sbase + (int64_t)row * DV + 32 * wv + l32] = S[rt][i];
+                a.final_states[sbase + (int64_t)row * DV + col] = S[rt][i];
             }
     }
 }
 
-template <int C, int CK, int DV, int LV, int LVV, typename TIn>
-static void launch_cfg(const ChunkArgs& a, hipStream_t st) {
-    const unsigned units = (unsigned)(a.num_seqs * a.H * (a.N + 1));
-    chunk_gla_kernel<C, CK, DV, LV, LVV, TIn><<<units, kThreads, 0, st>>>(a);
+// ============================ launchers ============================
+namespace {
+
+template <int C, int CK, int DV, int LV, int LVV, typename TIn, int MODE>
+void launch_cfg(const ChunkArgs& a, hipStream_t st) {
+    dim3 grid;
+    if (MODE == kModeRouted)
+        grid = dim3((unsigned)(a.num_seqs * a.H * a.N));
+    else
+        grid = dim3((unsigned)(a.num_seqs * a.H),
+                    (unsigned)(MODE == kModeLocal ? a.max_pieces - 1 : a.max_pieces));
+    if (grid.x == 0 || grid.y == 0) return;
+    chunk_kernel<C, CK, DV, LV, LVV, TIn, MODE><<<grid, kThreads, 0, st>>>(a);
 }
 
-template <int C, int LV, int LVV, typename TIn>
-static bool launch_dtype(const ChunkArgs& a, int c, int d, hipStream_t st) {
-#define SSE_CASE(CC, DD)                                              \
-    if (c == CC && d == DD) {                                         \
-        launch_cfg<C, CC, DD, LV, LVV, TIn>(a, st);                   \
-        return true;                                                  \
+template <int C, int LV, int LVV, typename TIn, int MODE>
+bool launch_shape(const ChunkArgs& a, int c, int d, hipStream_t st) {
+#define SSE_CASE(CC, DD)                                   \
+    if (c == CC && d == DD) {                              \
+        launch_cfg<C, CC, DD, LV, LVV, TIn, MODE>(a, st);  \
+        return true;                                       \
     }
     SSE_CASE(32, 32) SSE_CASE(32, 64) SSE_CASE(32, 128)
     SSE_CASE(64, 32) SSE_CASE(64, 64) SSE_CASE(64, 128)
@@ -502,14 +661,35 @@ static bool launch_dtype(const ChunkArgs& a, int c, int d, hipStream_t st) {
     return false;
 }
 
-hipError_t launch_chunk_gla(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
+template <int MODE>
+hipError_t launch_mode(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
     if ((int64_t)a.num_seqs * a.H == 0) return hipSuccess;
     // bf16 inputs: 64-record chunks, 2 bf16 terms; fp32 inputs: 32-record
-    // chunks (the 3-term operands need 1.5x the LDS), 3 bf16 terms.
-    const bool ok = dtype == kF32 ? launch_dtype<32, 3, 3, float>(a, c, d, st)
-                                  : launch_dtype<64, 2, 1, bf16_t>(a, c, d, st);
+    // chunks (3-term operands need 1.5x the LDS), 3 bf16 terms.
+    const bool ok = dtype == kF32 ? launch_shape<32, 3, 3, float, MODE>(a, c, d, st)
+                                  : launch_shape<64, 2, 1, bf16_t, MODE>(a, c, d, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+}  // namespace
+
+int chunk_piece_len(int dtype) { return dtype == kF32 ? 1024 : 2048; }
+
+int chunk_max_pieces(int max_seqlen, int dtype) {
+    const int p = chunk_piece_len(dtype);
+    return max_seqlen <= 0 ? 1 : (max_seqlen + p - 1) / p;
+}
+
+hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
+    if (a.max_pieces <= 1) return hipSuccess;
+    return launch_mode<kModeLocal>(a, dtype, c, d, st);
+}
+hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
+    return launch_mode<kModeShared>(a, dtype, c, d, st);
+}
+hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
+    return launch_mode<kModeRouted>(a, dtype, c, d, st);
 }
 
 }  // namespace sse

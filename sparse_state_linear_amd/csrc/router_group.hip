@@ -7,7 +7,9 @@
 //
 // Grouping is a stable counting sort done in three launches:
 //   route_count  one block per (sequence*head, 256-token block): routes its
-//                tokens and counts records per partition in LDS;
+//                tokens, counts records per partition in LDS, and stores the
+//                log2 normaliser of each token's key softmax (§2.3, eq. 11)
+//                so that later passes need no row reduction;
 //   block_scan   one block per (sequence, head): exclusive scan over its
 //                N x blocks counts.  The records of (s, h) occupy a known
 //                contiguous range (every token contributes exactly k
@@ -74,19 +76,49 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const TIn* __restrict_
         }
 }
 
+// Loads CK consecutive input values of one row as fp32.
+template <int CK>
+__device__ __forceinline__ void load_row(const bf16_t* p, float (&x)[CK]) {
+#pragma unroll
+    for (int u = 0; u < CK / 8; u++) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[u];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            x[8 * u + 2 * e] = __uint_as_float(w4[e] << 16);
+            x[8 * u + 2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+    }
+}
+template <int CK>
+__device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
+#pragma unroll
+    for (int u = 0; u < CK / 4; u++) {
+        const float4 v = reinterpret_cast<const float4*>(p)[u];
+        x[4 * u] = v.x;
+        x[4 * u + 1] = v.y;
+        x[4 * u + 2] = v.z;
+        x[4 * u + 3] = v.w;
+    }
+}
+
 // Route the tokens of one (sequence, head, token block), count the records
-// per partition, and zero this block's rows of o (the forward accumulates
-// partition reads into o).
-template <int NMAX, typename TIn>
+// per partition, and store lnz2 = log2 of the key-softmax denominator
+// sum_j 2^((kl_j - m) log2 e) plus m log2 e, so that kappa_j =
+// 2^(kl_j log2 e - lnz2).  Blocks of one token block are adjacent in launch
+// order across heads (they read neighbouring rows).
+template <int NMAX, int CK, typename TIn>
 __global__ __launch_bounds__(kTokBlock) void route_count_kernel(
-    const TIn* __restrict__ z, const int32_t* __restrict__ cu, int H, int N, int K, int nblk,
-    int32_t* __restrict__ idx, float* __restrict__ wout, int32_t* __restrict__ counts,
-    float* __restrict__ o_zero, int d) {
+    const TIn* __restrict__ z, const TIn* __restrict__ kl, const int32_t* __restrict__ cu, int H,
+    int N, int K, int nblk, int32_t* __restrict__ idx, float* __restrict__ wout,
+    int32_t* __restrict__ counts, float* __restrict__ lnz2) {
     __shared__ int cnt[kMaxN];
-    const int sh = blockIdx.x, blk = blockIdx.y;
-    const int s = sh / H, h = sh % H;
-    const int64_t t0 = cu[s], t1 = cu[s + 1];
-    const int64_t tb = t0 + (int64_t)blk * kTokBlock;
+    const int h = blockIdx.x % H;
+    const int rest = blockIdx.x / H;
+    const int blk = rest % nblk, s = rest / nblk;
+    const int sh = s * H + h;
+    const int64_t t1 = cu[s + 1];
+    const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
     if (threadIdx.x < kMaxN) cnt[threadIdx.x] = 0;
     __syncthreads();
     const int64_t t = tb + threadIdx.x;
@@ -102,19 +134,22 @@ __global__ __launch_bounds__(kTokBlock) void route_count_kernel(
                 wout[row * K + j] = w[j];
                 atomicAdd(&cnt[sel[j]], 1);
             }
+        if (lnz2) {
+            float x[CK];
+            load_row<CK>(kl + row * CK, x);
+            float m = x[0];
+#pragma unroll
+            for (int j = 1; j < CK; j++) m = fmaxf(m, x[j]);
+            const float m2 = m * kLog2e;
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < CK; j++) sum += exp2f(fmaf(x[j], kLog2e, -m2));
+            lnz2[row] = m2 + log2f(sum);
+        }
     }
     __syncthreads();
     if (counts && threadIdx.x < N)
         counts[((int64_t)sh * N + threadIdx.x) * nblk + blk] = cnt[threadIdx.x];
-    if (o_zero && tb < t1) {
-        const int ntok = (int)min<int64_t>(kTokBlock, t1 - tb);
-        const int q4 = d / 4;
-        for (int e = threadIdx.x; e < ntok * q4; e += blockDim.x) {
-            int64_t tt = tb + e / q4;
-            *reinterpret_cast<float4*>(o_zero + (tt * H + h) * d + 4 * (e % q4)) =
-                make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and
@@ -170,10 +205,13 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
 }
 
 // Stable scatter of the records of one (sequence, head, token block).
+// When lnz2 is given, seg_cr[p] = lnz2[t, h] - log2(w) is stored too: the
+// exponent offset that turns 2^(kl log2 e - seg_cr) into w * kappa.
 __global__ __launch_bounds__(kTokBlock) void scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ win, const int32_t* __restrict__ cu,
     int H, int N, int K, int nblk, const int32_t* __restrict__ pos, int32_t* __restrict__ seg_tok,
-    int32_t* __restrict__ seg_slot, float* __restrict__ seg_w) {
+    int32_t* __restrict__ seg_slot, float* __restrict__ seg_w, const float* __restrict__ lnz2,
+    float* __restrict__ seg_cr) {
     constexpr int NW = kTokBlock / kWave;
     __shared__ int wcnt[NW][kMaxN];
     const int sh = blockIdx.x, blk = blockIdx.y;
@@ -216,7 +254,11 @@ __global__ __launch_bounds__(kTokBlock) void scatter_kernel(
             const int p = pos[((int64_t)sh * N + i) * nblk + blk] + before + rank_in_wave[j];
             seg_tok[p] = (int32_t)t;
             if (seg_slot) seg_slot[p] = j;
-            if (seg_w) seg_w[p] = win[(t * H + h) * K + j];
+            if (seg_w || seg_cr) {
+                const float wj = win[(t * H + h) * K + j];
+                if (seg_w) seg_w[p] = wj;
+                if (seg_cr) seg_cr[p] = lnz2[t * H + h] - log2f(wj);
+            }
         }
     }
 }
@@ -246,32 +288,47 @@ hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int
 
 int group_nblk(int max_seqlen) { return max_seqlen <= 0 ? 1 : (max_seqlen + kTokBlock - 1) / kTokBlock; }
 
+template <int NMAX, typename TIn>
+static void launch_rc_n(dim3 grid, const TIn* z, const TIn* kl, const int32_t* cu, int H, int c,
+                        int N, int K, int nblk, int32_t* idx, float* w, int32_t* counts,
+                        float* lnz2, hipStream_t st) {
+    if (c == 32)
+        route_count_kernel<NMAX, 32, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+    else if (c == 64)
+        route_count_kernel<NMAX, 64, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+    else
+        route_count_kernel<NMAX, 128, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+}
+
 template <typename TIn>
-static hipError_t launch_route_count_t(const void* z, const int32_t* cu, int num_seqs,
-                                       int max_seqlen, int H, int N, int K, int32_t* idx, float* w,
-                                       int32_t* counts, float* o_zero, int d, hipStream_t st) {
+static hipError_t launch_route_count_t(const void* z, const void* kl, const int32_t* cu,
+                                       int num_seqs, int max_seqlen, int H, int c, int N, int K,
+                                       int32_t* idx, float* w, int32_t* counts, float* lnz2,
+                                       hipStream_t st) {
     const int nblk = group_nblk(max_seqlen);
     if ((int64_t)num_seqs * H == 0) return hipSuccess;
-    dim3 grid((unsigned)(num_seqs * H), (unsigned)nblk), block(kTokBlock);
+    dim3 grid((unsigned)((int64_t)num_seqs * nblk * H));
     const TIn* zz = static_cast<const TIn*>(z);
+    const TIn* kk = static_cast<const TIn*>(kl);
     if (N <= 8)
-        route_count_kernel<8, TIn><<<grid, block, 0, st>>>(zz, cu, H, N, K, nblk, idx, w, counts, o_zero, d);
+        launch_rc_n<8, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
     else if (N <= 16)
-        route_count_kernel<16, TIn><<<grid, block, 0, st>>>(zz, cu, H, N, K, nblk, idx, w, counts, o_zero, d);
+        launch_rc_n<16, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
     else if (N <= 32)
-        route_count_kernel<32, TIn><<<grid, block, 0, st>>>(zz, cu, H, N, K, nblk, idx, w, counts, o_zero, d);
+        launch_rc_n<32, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
     else
-        route_count_kernel<64, TIn><<<grid, block, 0, st>>>(zz, cu, H, N, K, nblk, idx, w, counts, o_zero, d);
+        launch_rc_n<64, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
     return hipGetLastError();
 }
 
-hipError_t launch_route_count(const void* z, int dtype, const int32_t* cu, int num_seqs,
-                              int max_seqlen, int H, int N, int K, int32_t* idx, float* w,
-                              int32_t* counts, float* o_zero, int d, hipStream_t st) {
-    return dtype == kF32 ? launch_route_count_t<float>(z, cu, num_seqs, max_seqlen, H, N, K, idx,
-                                                       w, counts, o_zero, d, st)
-                         : launch_route_count_t<bf16_t>(z, cu, num_seqs, max_seqlen, H, N, K,
-                                                        idx, w, counts, o_zero, d, st);
+hipError_t launch_route_count(const void* z, const void* kl, int dtype, const int32_t* cu,
+                              int num_seqs, int max_seqlen, int H, int c, int N, int K,
+                              int32_t* idx, float* w, int32_t* counts, float* lnz2,
+                              hipStream_t st) {
+    return dtype == kF32 ? launch_route_count_t<float>(z, kl, cu, num_seqs, max_seqlen, H, c, N,
+                                                       K, idx, w, counts, lnz2, st)
+                         : launch_route_count_t<bf16_t>(z, kl, cu, num_seqs, max_seqlen, H, c,
+                                                        N, K, idx, w, counts, lnz2, st);
 }
 
 // Count records per (segment, token block) from an existing top-k choice.
@@ -296,7 +353,7 @@ __global__ void zero_int_kernel(int32_t* p) { *p = 0; }
 hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, int num_seqs,
                         int max_seqlen, int H, int N, int K, bool counts_ready, int32_t* counts,
                         int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot, float* seg_w,
-                        hipStream_t st) {
+                        const float* lnz2, float* seg_cr, hipStream_t st) {
     const int nblk = group_nblk(max_seqlen);
     const unsigned SH = (unsigned)(num_seqs * H);
     if (SH == 0) {
@@ -313,7 +370,7 @@ hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     scatter_kernel<<<dim3(SH, nblk), kTokBlock, 0, st>>>(idx, w, cu, H, N, K, nblk, counts,
-                                                         seg_tok, seg_slot, seg_w);
+                                                         seg_tok, seg_slot, seg_w, lnz2, seg_cr);
     return hipGetLastError();
 }
 

@@ -24,11 +24,13 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
 }
 
 struct FwdLayout {
-    size_t idx, w, counts, seg_off, seg_tok, seg_w, total;
+    size_t idx, w, counts, seg_off, seg_tok, seg_w, seg_cr, lnz2, agg_S, agg_D, trash, total;
 };
 
-// Returns false when the sizes overflow the int32 indexing of the kernels.
-bool forward_layout(int64_t T, int S, int max_seqlen, int H, int N, int K, FwdLayout& L) {
+// Workspace carving.  c, d = 0 sizes the grouping part only.  Returns false
+// when the sizes overflow the 32-bit indexing of the kernels.
+bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N, int K,
+                    FwdLayout& L) {
     if (T < 0 || S < 0 || max_seqlen < 0 || H < 1 || N < 1 || K < 1) return false;
     const int64_t recs = T * H * K;
     const int64_t nblk = sse::group_nblk(max_seqlen);
@@ -36,6 +38,10 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int N, int K, FwdLa
     const int64_t units = (int64_t)S * H * (N + 1);
     if (recs >= INT_MAX || cnt >= INT_MAX || units >= INT_MAX || T >= INT_MAX) return false;
     if ((int64_t)S * H >= INT_MAX || (int64_t)S * H * N + 1 >= INT_MAX) return false;
+    if ((int64_t)S * nblk * H >= INT_MAX) return false;
+    // pieces are sized for the shorter (fp32) piece length: an upper bound
+    const int64_t maxp = sse::chunk_max_pieces(max_seqlen, sse::kF32);
+    if (maxp >= 65536) return false;
     size_t off = 0;
     L.idx = off;     off += align_up(sizeof(int32_t) * (size_t)recs);
     L.w = off;       off += align_up(sizeof(float) * (size_t)recs);
@@ -43,11 +49,30 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int N, int K, FwdLa
     L.seg_off = off; off += align_up(sizeof(int32_t) * (size_t)((int64_t)S * H * N + 1));
     L.seg_tok = off; off += align_up(sizeof(int32_t) * (size_t)recs);
     L.seg_w = off;   off += align_up(sizeof(float) * (size_t)recs);
+    L.seg_cr = off;  off += align_up(sizeof(float) * (size_t)recs);
+    L.lnz2 = off;    off += align_up(sizeof(float) * (size_t)(T * H));
+    L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
+    L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
+    L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? d : 1));
     L.total = off;
     return true;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSE_OK : SSE_ERR_HIP; }
+
+// ---- stage tracing: a ring of per-call HIP events (profiling aid) ----------
+constexpr int kTraceCalls = 256;
+constexpr int kTraceMarks = SSE_TRACE_STAGES + 1;
+struct Trace {
+    bool on = false;
+    bool created = false;
+    hipEvent_t ev[kTraceCalls][kTraceMarks];
+    int64_t calls = 0;   // forward calls recorded since the last read
+} g_trace;
+
+inline void trace_mark(int mark, hipStream_t s) {
+    if (g_trace.on) (void)hipEventRecord(g_trace.ev[g_trace.calls % kTraceCalls][mark], s);
+}
 
 }  // namespace
 
@@ -70,7 +95,7 @@ size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_s
                                    int c, int d, int N, int topk) {
     if (check_common(SSE_BF16, H, c, d, N, topk) != SSE_OK) return 0;
     FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, N, topk, L)) return 0;
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L)) return 0;
     return L.total;
 }
 
@@ -88,8 +113,9 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
         return SSE_ERR_INVALID_ARG;
     if (num_seqs > 0 && !final_states) return SSE_ERR_INVALID_ARG;
     FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, N, topk, L))
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L))
         return SSE_ERR_UNSUPPORTED;
+    if (total_tokens * H * (c > d ? c : d) >= INT_MAX) return SSE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -100,13 +126,20 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
     int32_t* seg_tok = reinterpret_cast<int32_t*>(ws + L.seg_tok);
     float* seg_w = reinterpret_cast<float*>(ws + L.seg_w);
+    float* seg_cr = reinterpret_cast<float*>(ws + L.seg_cr);
+    float* lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
 
-    hipError_t e = sse::launch_route_count(router_logits, dtype, cu_seqlens, num_seqs, max_seqlen,
-                                           H, N, topk, idx, w, counts, o, d, s);
+    // 1. router + per-block counts + key-softmax normaliser
+    trace_mark(0, s);
+    hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
+                                           max_seqlen, H, c, N, topk, idx, w, counts, lnz2, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
+    // 2. grouping into (sequence, head, partition) segments
+    trace_mark(1, s);
     e = sse::launch_group(idx, w, cu_seqlens, num_seqs, max_seqlen, H, N, topk, true, counts,
-                          seg_off, seg_tok, nullptr, seg_w, s);
+                          seg_off, seg_tok, nullptr, seg_w, lnz2, seg_cr, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
+    trace_mark(2, s);
     sse::ChunkArgs a;
     a.q = q;
     a.kl = key_logits;
@@ -116,13 +149,65 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.seg_offsets = seg_off;
     a.seg_tok = seg_tok;
     a.seg_w = seg_w;
+    a.seg_cr = seg_cr;
+    a.lnz2 = lnz2;
     a.init = initial_states;
     a.o = o;
     a.final_states = final_states;
+    a.agg_S = reinterpret_cast<float*>(ws + L.agg_S);
+    a.agg_D = reinterpret_cast<float*>(ws + L.agg_D);
+    a.trash = reinterpret_cast<float*>(ws + L.trash);
     a.num_seqs = num_seqs;
     a.H = H;
     a.N = N;
-    return hip_status(sse::launch_chunk_gla(a, dtype, c, d, s));
+    a.piece_len = sse::chunk_piece_len(dtype);
+    a.max_pieces = sse::chunk_max_pieces(max_seqlen, dtype);
+    // 3. local states of the shared pieces (all but the last of a sequence)
+    e = sse::launch_chunk_local(a, dtype, c, d, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    trace_mark(3, s);
+    // 4. shared partition: stores o
+    e = sse::launch_chunk_shared(a, dtype, c, d, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    trace_mark(4, s);
+    // 5. routed partitions: add into o
+    e = sse::launch_chunk_routed(a, dtype, c, d, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    trace_mark(5, s);
+    if (g_trace.on) g_trace.calls++;
+    return SSE_OK;
+}
+
+int sse_trace_enable(int enable) {
+    if (enable && !g_trace.created) {
+        for (int i = 0; i < kTraceCalls; i++)
+            for (int j = 0; j < kTraceMarks; j++)
+                if (hipEventCreate(&g_trace.ev[i][j]) != hipSuccess) return SSE_ERR_HIP;
+        g_trace.created = true;
+    }
+    g_trace.on = enable != 0;
+    g_trace.calls = 0;
+    return SSE_OK;
+}
+
+int sse_trace_read(float* ms_per_stage, int n_stages, int64_t* calls) {
+    if (!ms_per_stage || n_stages < 1 || n_stages > SSE_TRACE_STAGES || !calls)
+        return SSE_ERR_INVALID_ARG;
+    for (int j = 0; j < n_stages; j++) ms_per_stage[j] = 0.f;
+    const int64_t n = g_trace.calls < kTraceCalls ? g_trace.calls : kTraceCalls;
+    *calls = n;
+    if (!g_trace.created || n == 0) return SSE_OK;
+    for (int64_t i = 0; i < n; i++) {
+        hipEvent_t* ev = g_trace.ev[(g_trace.calls - n + i) % kTraceCalls];
+        if (hipEventSynchronize(ev[kTraceMarks - 1]) != hipSuccess) return SSE_ERR_HIP;
+        for (int j = 0; j < n_stages; j++) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, ev[j], ev[j + 1]) != hipSuccess) return SSE_ERR_HIP;
+            ms_per_stage[j] += ms;
+        }
+    }
+    g_trace.calls = 0;
+    return SSE_OK;
 }
 
 int sse_decode_step(const void* q, const void* key_logits, const void* v, const void* log_alpha,
@@ -154,7 +239,7 @@ size_t sse_group_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seq
                                  int topk) {
     if (N < 1 || topk < 1 || topk > N || N > sse::kMaxN || topk > sse::kMaxTopK) return 0;
     FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, N, topk, L)) return 0;
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, 0, 0, N, topk, L)) return 0;
     return L.seg_off - L.counts;
 }
 
@@ -171,13 +256,13 @@ int sse_group_by_partition(const int32_t* topk_idx, const float* topk_w,
     if (total_tokens > 0 && (!topk_idx || !seg_tok)) return SSE_ERR_INVALID_ARG;
     if (seg_w && !topk_w) return SSE_ERR_INVALID_ARG;
     FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, N, topk, L))
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, 0, 0, N, topk, L))
         return SSE_ERR_UNSUPPORTED;
     const size_t need = L.seg_off - L.counts;
     if (workspace_bytes < need || (need > 0 && !workspace)) return SSE_ERR_WORKSPACE;
     return hip_status(sse::launch_group(topk_idx, topk_w, cu_seqlens, num_seqs, max_seqlen, H, N,
                                         topk, false, static_cast<int32_t*>(workspace),
-                                        seg_offsets, seg_tok, seg_slot, seg_w,
+                                        seg_offsets, seg_tok, seg_slot, seg_w, nullptr, nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 

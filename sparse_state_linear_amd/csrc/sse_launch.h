@@ -19,31 +19,46 @@ int group_nblk(int max_seqlen);
 hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int K, int32_t* idx,
                               float* w, hipStream_t st);
 
-hipError_t launch_route_count(const void* z, int dtype, const int32_t* cu, int num_seqs,
-                              int max_seqlen, int H, int N, int K, int32_t* idx, float* w,
-                              int32_t* counts, float* o_zero, int d, hipStream_t st);
+hipError_t launch_route_count(const void* z, const void* kl, int dtype, const int32_t* cu,
+                              int num_seqs, int max_seqlen, int H, int c, int N, int K,
+                              int32_t* idx, float* w, int32_t* counts, float* lnz2,
+                              hipStream_t st);
 
 hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, int num_seqs,
                         int max_seqlen, int H, int N, int K, bool counts_ready, int32_t* counts,
                         int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot, float* seg_w,
-                        hipStream_t st);
+                        const float* lnz2, float* seg_cr, hipStream_t st);
 
+// Arguments of the chunked GLA passes (see chunk_gla.hip).
 struct ChunkArgs {
     const void* q;
     const void* kl;
     const void* v;
     const void* la;
     const int32_t* cu;
-    const int32_t* seg_offsets;
+    const int32_t* seg_offsets;  // routed segments
     const int32_t* seg_tok;
     const float* seg_w;
-    const float* init;
+    const float* seg_cr;
+    const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
+    const float* init;           // [S, H, N+1, c, d] or null
     float* o;
     float* final_states;
+    float* agg_S;                // [S*H, max_pieces, c, d] local piece states
+    float* agg_D;                // [S*H, max_pieces, c] piece decay products
+    float* trash;                // one dummy output row for padded records
     int num_seqs, H, N;
+    int piece_len;               // records per shared piece
+    int max_pieces;
 };
 
-hipError_t launch_chunk_gla(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+// Records per shared piece and the pieces needed for max_seqlen tokens.
+int chunk_piece_len(int dtype);
+int chunk_max_pieces(int max_seqlen, int dtype);
+
+hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 
 hipError_t launch_decode(const void* q, const void* kl, const void* v, const void* la,
                          const void* z, int dtype, int B, int H, int c, int d, int N, int K,
