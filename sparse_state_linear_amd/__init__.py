@@ -17,7 +17,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsse_amd.so")
+# SSE_LIB_PATH selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("SSE_LIB_PATH") or os.path.join(_PKG, "libsse_amd.so")
 
 SSE_OK, SSE_ERR_INVALID_ARG, SSE_ERR_UNSUPPORTED, SSE_ERR_WORKSPACE, SSE_ERR_HIP = range(5)
 SSE_F32, SSE_BF16 = 0, 1

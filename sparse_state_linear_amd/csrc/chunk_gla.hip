@@ -34,18 +34,16 @@
 // so all pieces run in parallel.
 //
 // Block = 4 waves, one piece (shared) or segment (routed), all of d, chunks of
-// C records (64 for bf16 inputs, 32 for fp32 inputs).  Wave w owns state and
+// C = 32 records.  Wave w owns state and
 // output columns [32w, 32w+32) (c x 32 fp32 in MFMA accumulator layout) and
 // prepares key/query columns [w c/4, (w+1) c/4) for all records of a chunk:
 // lane = (group of 4 columns, group of consecutive records), so the decay
 // cumsum is in-lane plus a short cross-lane scan and every LDS store is a
-// vector store.  Software pipeline per chunk n:
-//   start loads of chunk n+1, metadata of chunk n+2
-//   MFMA phase of chunk n  |  element-wise preparation of chunk n+1
-//   outputs of chunk n; barrier; store chunk n+1 operands; barrier;
-//   causal A tiles of chunk n+1 (16x16x32 MFMA); barrier
-// The barriers wait only for LDS traffic, so global loads and output atomics
-// stay in flight across them.
+// vector store.  Two blocks share a CU (LDS ~72 KB, <= 256 registers per
+// lane), so one block's MFMA phase overlaps the other's element-wise work and
+// memory waits.  The loads of chunk n+1 are issued a whole iteration ahead and
+// before chunk n's output stores, and the barriers wait only for LDS traffic,
+// so global loads and output atomics stay in flight across them.
 #include "sse_launch.h"
 
 namespace sse {
@@ -55,6 +53,12 @@ namespace {
 constexpr int kNW = 4;        // waves per block
 constexpr int kThreads = kNW * kWave;
 constexpr int kPC = 4;        // columns per lane in the preparation layout
+#ifndef SSE_BF16_CHUNK
+#define SSE_BF16_CHUNK 32
+#endif
+#ifndef SSE_SHARED_PIECE
+#define SSE_SHARED_PIECE 1024
+#endif
 
 enum { kModeLocal = 0, kModeShared = 1, kModeRouted = 2 };
 
@@ -68,9 +72,9 @@ struct Smem {
     uint16_t vt[LVV][DV][TS];           // V terms [col][s]
     uint16_t a[LV][C][TS];              // A terms [r][s]
     float ebc[CK];                      // exp(b_C) per state row
-    int mtok[3][C];                     // record token; ~token marks a padded record
+    uint32_t mrow[3][C];                // record row t*H + h (a real row even if padded)
     float mcr[3][C];                    // exponent offset lnz2 - log2 w (+inf if padded)
-    float mw[3][C];                     // read gate (0 if padded)
+    float mw[3][C];                     // read gate; -0.0 marks a padded record
 };
 
 // Four consecutive input values of one row.
@@ -79,7 +83,9 @@ struct Vec4;
 template <>
 struct Vec4<bf16_t> {
     uint2 u;
-    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void load(const void* base, uint32_t byte_off) {
+        u = *reinterpret_cast<const uint2*>(static_cast<const char*>(base) + byte_off);
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t w = (e < 2) ? u.x : u.y;
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -92,7 +98,9 @@ struct Vec4<bf16_t> {
 template <>
 struct Vec4<float> {
     float4 f;
-    __device__ __forceinline__ void load(const float* p) { f = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ void load(const void* base, uint32_t byte_off) {
+        f = *reinterpret_cast<const float4*>(static_cast<const char*>(base) + byte_off);
+    }
     __device__ __forceinline__ float get(int e) const {
         return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
     }
@@ -112,20 +120,11 @@ struct Geo {
 
 template <int L>
 __device__ __forceinline__ void split4(const float (&x)[kPC], uint2 (&out)[L]) {
-    float r[kPC];
+    uint32_t lo[L], hi[L];
+    split_pair<L>(x[0], x[1], lo);
+    split_pair<L>(x[2], x[3], hi);
 #pragma unroll
-    for (int e = 0; e < kPC; e++) r[e] = x[e];
-#pragma unroll
-    for (int l = 0; l < L; l++) {
-        uint16_t h[kPC];
-#pragma unroll
-        for (int e = 0; e < kPC; e++) {
-            h[e] = f32_to_bf16_bits(r[e]);
-            if (l + 1 < L) r[e] -= bf16_bits_to_f32(h[e]);
-        }
-        out[l].x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        out[l].y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-    }
+    for (int l = 0; l < L; l++) out[l] = make_uint2(lo[l], hi[l]);
 }
 
 __device__ __forceinline__ uint16_t elem(const uint2& v, int e) {
@@ -207,8 +206,15 @@ __device__ __forceinline__ void a_tile(int ti, int& st, int& rt) {
 
 }  // namespace
 
+// Blocks per CU the register allocation targets: two when the LDS of two
+// blocks fits in the 160 KB of a CU (each SIMD then runs two waves that hide
+// each other's LDS and memory latency), else one.
+template <int C, int CK, int DV, int LV, int LVV>
+constexpr int kMinBlocks = sizeof(Smem<C, CK, DV, LV, LVV>) <= 80 * 1024 ? 2 : 1;
+
 template <int C, int CK, int DV, int LV, int LVV, typename TIn, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
+__global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void chunk_kernel(
+    const ChunkArgs a) {
     using SM = Smem<C, CK, DV, LV, LVV>;
     using GK = Geo<C, CK>;
     using GV = Geo<C, DV>;
@@ -218,7 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
     constexpr int RT_N = CK / 32;        // 32-row tiles of the state
     __shared__ __attribute__((aligned(16))) SM sm;
 
-    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int hh = lane / 32, l32 = lane % 32;
     const int H = a.H, N = a.N;
     const bool col_wave = NS == kNW || wv < NS;  // this wave owns state columns
@@ -265,25 +272,34 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
         for (int i = 0; i < 16; i++) S[rt][i] = 0.f;
     if (col_wave && !kLocal) {
         const int col = 32 * wv + l32;
+        if (a.init) {
 #pragma unroll
-        for (int rt = 0; rt < RT_N; rt++)
+            for (int rt = 0; rt < RT_N; rt++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
-                float x = a.init ? a.init[sbase + (int64_t)row * DV + col] : 0.f;
-                for (int p = 0; p < piece; p++) {
-                    const int64_t ab = abase + p;
-                    x = a.agg_D[ab * CK + row] * x + a.agg_S[(ab * CK + row) * DV + col];
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    S[rt][i] = a.init[sbase + (int64_t)row * DV + col];
                 }
-                S[rt][i] = x;
-            }
+        }
+        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the local-state pass
+        for (int p = 0; p < piece; p++) {
+            const int64_t ab = abase + p;
+#pragma unroll
+            for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    S[rt][i] = a.agg_D[ab * CK + row] * S[rt][i] +
+                               a.agg_S[(ab * CK + row) * DV + col];
+                }
+        }
     }
 
     // ---------------- metadata of one chunk ----------------
     // Every thread loads (record index tid % C, clamped into the piece) so the
     // loads carry no branch; threads < C store it after the next barrier.
-    // Padded records keep a real token (so every address stays valid), marked
-    // by storing its bitwise complement.
+    // Padded records keep a real row (so every address stays valid) and are
+    // marked by a read gate of -0.0.
     auto meta_load = [&](int64_t chunk, int& tok, float& cr, float& w) {
         const int64_t idx = chunk * C + (tid % C);
         const int64_t ci = idx < n ? idx : (n > 0 ? n - 1 : 0);
@@ -299,11 +315,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
     };
     auto meta_store = [&](int64_t chunk, int buf, int tok, float cr, float w) {
         const bool valid = chunk * C + tid < n;
-        sm.mtok[buf][tid] = valid ? tok : ~tok;
+        sm.mrow[buf][tid] = (uint32_t)tok * (uint32_t)H + (uint32_t)h;
         sm.mcr[buf][tid] = valid ? cr : INFINITY;
-        sm.mw[buf][tid] = valid ? w : 0.f;
+        sm.mw[buf][tid] = valid ? w : -0.f;
     };
-    auto tok_of = [](int m) { return m >= 0 ? m : ~m; };
+    auto is_real = [](float w) { return (__float_as_uint(w) >> 31) == 0u; };
 
     // ---------------- raw loads of one chunk into registers ----------------
     constexpr int RPG = GK::RPG, RPGV = GV::RPG;
@@ -312,17 +328,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
     const int cgv = lane % GV::NCG, gv_ = lane / GV::NCG;
     const int c0v = wv * GV::CW + cgv * kPC, r0v = gv_ * RPGV;
     Vec4<TIn> rq[RPG], rk[RPG], rl[RPG], rv[RPGV];
-    auto raw_load = [&](int buf) {
+    auto raw_load_qkl = [&](int buf) {
+        // byte offsets fit in 32 bits (checked on the host): scalar base +
+        // 32-bit vector offset addressing
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const int64_t off = ((int64_t)tok_of(sm.mtok[buf][r0 + i]) * H + h) * CK + j0;
-            if constexpr (!kLocal) rq[i].load(gq + off);
-            rk[i].load(gk + off);
-            rl[i].load(gl + off);
+            const uint32_t off = sm.mrow[buf][r0 + i] * (uint32_t)(CK * sizeof(TIn)) +
+                                 (uint32_t)(j0 * sizeof(TIn));
+            if constexpr (!kLocal) rq[i].load(gq, off);
+            rk[i].load(gk, off);
+            rl[i].load(gl, off);
         }
+    };
+    auto raw_load_v = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < RPGV; i++)
-            rv[i].load(gv + ((int64_t)tok_of(sm.mtok[buf][r0v + i]) * H + h) * DV + c0v);
+            rv[i].load(gv, sm.mrow[buf][r0v + i] * (uint32_t)(DV * sizeof(TIn)) +
+                               (uint32_t)(c0v * sizeof(TIn)));
     };
 
     // ---------------- element-wise preparation into registers ----------------
@@ -334,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
         float bb[RPG][kPC];
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const bool valid = sm.mtok[buf][r0 + i] >= 0;
+            const bool valid = is_real(sm.mw[buf][r0 + i]);
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
                 const float x = valid ? rl[i].get(e) : 0.f;
@@ -446,28 +468,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
                     if (16 * st + 4 * g16 + i > 16 * rt + l16) acc[i] = 0.f;
             }
             const int r = 16 * rt + l16, s0 = 16 * st + 4 * g16;
-            uint16_t t4[4][LV];
+            uint32_t p01[LV], p23[LV];
+            split_pair<LV>(acc[0], acc[1], p01);
+            split_pair<LV>(acc[2], acc[3], p23);
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float x = acc[i];
-#pragma unroll
-                for (int l = 0; l < LV; l++) {
-                    t4[i][l] = f32_to_bf16_bits(x);
-                    if (l + 1 < LV) x -= bf16_bits_to_f32(t4[i][l]);
-                }
-            }
-#pragma unroll
-            for (int l = 0; l < LV; l++) {
-                u16x4 pkd = {t4[0][l], t4[1][l], t4[2][l], t4[3][l]};
-                *reinterpret_cast<u16x4*>(&sm.a[l][r][s0]) = pkd;
-            }
+            for (int l = 0; l < LV; l++)
+                *reinterpret_cast<uint2*>(&sm.a[l][r][s0]) = make_uint2(p01[l], p23[l]);
         }
     };
 
     // ---------------- MFMA phase of one chunk ----------------
     f32x16 O[kOT];
     const int col = 32 * wv + l32;
-    auto mma = [&]() {
+    const uint32_t col4 = 4u * (uint32_t)col;
+    auto mma_out = [&]() {
         if constexpr (!kLocal) {
 #pragma unroll
             for (int t = 0; t < kOT; t++)
@@ -479,15 +493,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
             for (int kk = 0; kk < CK / 16; kk++) {
                 u16x8 sb[LV];
+                {
+                    uint32_t pr[4][LV];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    float x = S[kk / 2][8 * (kk % 2) + e];
+                    for (int e2 = 0; e2 < 4; e2++)
+                        split_pair<LV>(S[kk / 2][8 * (kk % 2) + 2 * e2],
+                                       S[kk / 2][8 * (kk % 2) + 2 * e2 + 1], pr[e2]);
 #pragma unroll
-                    for (int l = 0; l < LV; l++) {
-                        const uint16_t t = f32_to_bf16_bits(x);
-                        sb[l][e] = t;
-                        if (l + 1 < LV) x -= bf16_bits_to_f32(t);
-                    }
+                    for (int l = 0; l < LV; l++)
+                        sb[l] = __builtin_bit_cast(
+                            u16x8, make_uint4(pr[0][l], pr[1][l], pr[2][l], pr[3][l]));
                 }
                 const int jq = 16 * kk + 4 * hh;
 #pragma unroll
@@ -513,7 +528,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
                     mma32_terms<LV, LVV>(aa, vb, O[t2]);
                 }
         }
-        // S_out = diag(exp(b_C)) (S_in + Kh^T V)
+    };
+    // S_out = diag(exp(b_C)) (S_in + Kh^T V)
+    auto mma_state = [&]() {
 #pragma unroll
         for (int rt = 0; rt < RT_N; rt++) {
 #pragma unroll
@@ -546,27 +563,35 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++) {
                     const int rb = 32 * t2 + 8 * q4 + 4 * hh;
-                    const int4 tk = *reinterpret_cast<const int4*>(&sm.mtok[buf][rb]);
+                    const uint4 rw = *reinterpret_cast<const uint4*>(&sm.mrow[buf][rb]);
                     const float4 wr = *reinterpret_cast<const float4*>(&sm.mw[buf][rb]);
-                    const int tks[4] = {tk.x, tk.y, tk.z, tk.w};
+                    const uint32_t rows[4] = {rw.x, rw.y, rw.z, rw.w};
                     const float ws[4] = {wr.x, wr.y, wr.z, wr.w};
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const float val = ws[e] * O[t2][4 * q4 + e];
-                        const int64_t row = (int64_t)tok_of(tks[e]) * H + h;
+                        const uint32_t off = rows[e] * (uint32_t)(DV * 4) + col4;
                         if constexpr (MODE == kModeShared) {
-                            const bool valid = tks[e] >= 0;
-                            float* base = valid ? a.o : a.trash;
-                            base[(valid ? row * DV : 0) + col] = val;
+                            const bool valid = is_real(ws[e]);
+                            char* base = reinterpret_cast<char*>(valid ? a.o : a.trash);
+                            *reinterpret_cast<float*>(base + (valid ? off : col4)) = val;
                         } else {
-                            atomic_add_f32(a.o + row * DV + col, val);
+                            atomic_add_f32(reinterpret_cast<float*>(reinterpret_cast<char*>(a.o) + off), val);
                         }
                     }
                 }
         }
     };
 
+
     // ---------------- pipeline ----------------
+    // Per chunk n (two blocks share a CU and fill each other's stalls):
+    //   prepare chunk n from registers; start the q/k/log_alpha loads of
+    //   chunk n+1 (a whole iteration ahead, and ahead of this chunk's output
+    //   stores, so waiting for them never waits for stores) and the metadata
+    //   loads of n+2; barrier; store chunk n operands and start the v loads
+    //   of n+1; barrier; causal A tiles; barrier; MFMA phase with the outputs
+    //   of chunk n.
     if (nchunks > 0) {
         int mt = 0;
         float mc = 0.f, mwv = 0.f;
@@ -575,33 +600,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(const ChunkArgs a) {
         meta_load(1, mt, mc, mwv);
         if (tid < C) meta_store(1, 1, mt, mc, mwv);
         lds_barrier();
-        raw_load(0);
-        prep(0);
-        prep_store();
-        lds_barrier();
-        if constexpr (!kLocal) {
-            a_tiles();
-            lds_barrier();
-        }
-        for (int64_t c = 0; c + 1 < nchunks; c++) {
+        raw_load_qkl(0);
+        raw_load_v(0);
+        for (int64_t c = 0; c < nchunks; c++) {
             const int cur = (int)(c % 3), nxt = (int)((c + 1) % 3), nn = (int)((c + 2) % 3);
-            raw_load(nxt);
+            const bool more = c + 1 < nchunks;  // uniform
+            prep(cur);
+            if (more) raw_load_qkl(nxt);  // q, k, log_alpha registers are free now
             meta_load(c + 2, mt, mc, mwv);
-            if (col_wave) mma();
-            prep(nxt);
-            if (col_wave) outputs(cur);
-            lds_barrier();
+            lds_barrier();  // previous chunk's MFMA phase is done with the tiles
             prep_store();
+            if (more) raw_load_v(nxt);    // v registers are free after the V^T store
             if (tid < C) meta_store(c + 2, nn, mt, mc, mwv);
             lds_barrier();
             if constexpr (!kLocal) {
                 a_tiles();
                 lds_barrier();
             }
-        }
-        if (col_wave) {
-            mma();
-            outputs((int)((nchunks - 1) % 3));
+            if (col_wave) {
+                mma_out();
+                outputs(cur);
+                mma_state();
+            }
         }
     }
 
@@ -664,17 +684,17 @@ bool launch_shape(const ChunkArgs& a, int c, int d, hipStream_t st) {
 template <int MODE>
 hipError_t launch_mode(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
     if ((int64_t)a.num_seqs * a.H == 0) return hipSuccess;
-    // bf16 inputs: 64-record chunks, 2 bf16 terms; fp32 inputs: 32-record
-    // chunks (3-term operands need 1.5x the LDS), 3 bf16 terms.
+    // bf16 inputs: 32-record chunks (two blocks per CU), 2 bf16 terms; fp32
+    // inputs: 32-record chunks, 3 bf16 terms.
     const bool ok = dtype == kF32 ? launch_shape<32, 3, 3, float, MODE>(a, c, d, st)
-                                  : launch_shape<64, 2, 1, bf16_t, MODE>(a, c, d, st);
+                                  : launch_shape<SSE_BF16_CHUNK, 2, 1, bf16_t, MODE>(a, c, d, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 }  // namespace
 
-int chunk_piece_len(int dtype) { return dtype == kF32 ? 1024 : 2048; }
+int chunk_piece_len(int dtype) { return dtype == kF32 ? 1024 : SSE_SHARED_PIECE; }
 
 int chunk_max_pieces(int max_seqlen, int dtype) {
     const int p = chunk_piece_len(dtype);

@@ -115,7 +115,8 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     FwdLayout L;
     if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L))
         return SSE_ERR_UNSUPPORTED;
-    if (total_tokens * H * (c > d ? c : d) >= INT_MAX) return SSE_ERR_UNSUPPORTED;
+    // byte offsets of token rows must fit in 32 bits (fp32 worst case)
+    if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -34,6 +34,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (RNE) packed low/high in one 32-bit word (one
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Split a pair (a, b) into L packed bf16 terms: level l holds the RNE bf16 of
+// what the previous levels left (every subtraction is exact in fp32).
+template <int L>
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t (&out)[L]) {
+#pragma unroll
+    for (int l = 0; l < L; l++) {
+        const uint32_t p = pack_bf16x2(a, b);
+        out[l] = p;
+        if (l + 1 < L) {
+            a -= bf16_lo_f32(p);
+            b -= bf16_hi_f32(p);
+        }
+    }
+}
+
 // Split x into L bf16 terms x ~= t0 + t1 + ... (each term is the RNE bf16 of
 // what the previous terms left; every subtraction is exact in fp32).
 template <int L>
