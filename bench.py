@@ -8,10 +8,13 @@ inputs already resident in HBM.  The decode step (256 sequences x H=16,
 c=d=128, N=16, k=2, 64 consecutive steps) is timed in the same run and
 reported under "decode".
 
-roofline: the dominant kernel is the chunked GLA kernel; its duration comes
-from HIP events recorded around it on the library's stream during the timed
-steps (sse_trace_*).  Its algorithmic bytes per launch are the token inputs
-read once, o written once and the final states written once.
+roofline: the dominant kernel is the chunked GLA pass with the longest
+time (the routed pass); its duration comes from HIP events recorded around it
+on the library's stream during the timed steps (sse_trace_*).  Its
+algorithmic bytes per launch are the token inputs read once, o written once
+and the pass's final states written once; "traffic" is the HBM bytes the
+committed FETCH_SIZE/WRITE_SIZE counter runs measured for it (null if the
+kernel source changed since).
 
 cpu_baseline: the fp64 oracle (untuned) on a bounded sample of the same
 workload: a number of (sequence, head) units, over the host cores.
@@ -175,6 +178,43 @@ def cpu_baseline(args, w, si):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_gla_main_bf16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_state_linear_amd", "csrc", "chunk_gla.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the dominant kernel from the committed
+    FETCH_SIZE/WRITE_SIZE counter runs (scaled by the copy-kernel
+    calibration), or None when the kernel source changed since then."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(stage)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def calib_copy(torch, mib=1024, reps=3):
+    """A plain device copy of known size, run under the same counters as the
+    benchmark to calibrate FETCH_SIZE / WRITE_SIZE."""
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +224,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,14 +237,17 @@ def main():
     import sse_inputs as si
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy:
+        calib_copy(torch)
+        return
     w = si.WORKLOADS["main_bf16"]
     log("forward", w.notes)
     T, S, total_ms, stages, calls = run_forward(args, w, si, sse, torch)
     ms = total_ms / args.steps
     tokens_per_s = T / (ms * 1e-3)
     # dominant kernel: the routed pass (k of the k+1 partition reads)
-    kern = {"routed": ("chunk_kernel<64,128,128,2,1,bf16,routed>", w.N, T * w.H * w.topk),
-            "shared": ("chunk_kernel<64,128,128,2,1,bf16,shared>", 1, T * w.H)}
+    kern = {"routed": ("chunk_kernel<32,128,128,2,1,bf16,routed>", w.N, T * w.H * w.topk),
+            "shared": ("chunk_kernel<32,128,128,2,1,bf16,shared>", 1, T * w.H)}
     dom = max(kern, key=lambda k: stages[k])
     kname, parts, records = kern[dom]
     kb = pass_bytes(T, S, w.H, w.c, w.d, parts)
@@ -251,7 +296,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(dom),
             "kernel_ms": k_ms,
             "algorithmic_bytes_per_launch": kb,
             "algorithmic_flops_per_launch": kf,
