@@ -178,8 +178,8 @@ def cpu_baseline(args, w, si):
     }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_gla_main_bf16_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "sparse_state_linear_amd", "csrc", "chunk_gla.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_ws_main_bf16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_state_linear_amd", "csrc", "chunk_ws.hip")
 
 
 def kernel_source_hash() -> str:
@@ -246,8 +246,8 @@ def main():
     ms = total_ms / args.steps
     tokens_per_s = T / (ms * 1e-3)
     # dominant kernel: the routed pass (k of the k+1 partition reads)
-    kern = {"routed": ("chunk_kernel<32,128,128,2,1,bf16,routed>", w.N, T * w.H * w.topk),
-            "shared": ("chunk_kernel<32,128,128,2,1,bf16,shared>", 1, T * w.H)}
+    kern = {"routed": ("chunk_ws_kernel<128,128,routed>", w.N, T * w.H * w.topk),
+            "shared": ("chunk_ws_kernel<128,128,shared>", 1, T * w.H)}
     dom = max(kern, key=lambda k: stages[k])
     kname, parts, records = kern[dom]
     kb = pass_bytes(T, S, w.H, w.c, w.d, parts)

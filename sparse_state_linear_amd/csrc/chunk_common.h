@@ -1,0 +1,166 @@
+// chunk_common.h -- pieces shared by the chunked gated-linear-attention
+// kernels of this library: modes, input vectors, the element-wise
+// preparation layout, bf16 term splitting, LDS helpers, MFMA term sums.
+#pragma once
+
+#include <type_traits>
+
+#include "sse_launch.h"
+
+namespace sse {
+
+// Warp-specialised kernel for bf16 inputs (chunk_ws.hip); mode is one of
+// the chunk modes below.  Returns hipErrorInvalidValue for a shape it has no
+// instance for.
+hipError_t launch_chunk_ws(int mode, const ChunkArgs& a, int c, int d, hipStream_t st);
+
+namespace {
+
+constexpr int kNW = 4;        // waves per block
+constexpr int kThreads = kNW * kWave;
+constexpr int kPC = 4;        // columns per lane in the preparation layout
+#ifndef SSE_SHARED_PIECE
+#define SSE_SHARED_PIECE 1024
+#endif
+
+enum { kModeLocal = 0, kModeShared = 1, kModeRouted = 2 };
+
+// Four consecutive input values of one row.
+template <typename TIn>
+struct Vec4;
+template <>
+struct Vec4<bf16_t> {
+    uint2 u;
+    __device__ __forceinline__ void load(const void* base, uint32_t byte_off) {
+        u = *reinterpret_cast<const uint2*>(static_cast<const char*>(base) + byte_off);
+    }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = (e < 2) ? u.x : u.y;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ __forceinline__ uint16_t bits(int e) const {
+        const uint32_t w = (e < 2) ? u.x : u.y;
+        return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+};
+template <>
+struct Vec4<float> {
+    float4 f;
+    __device__ __forceinline__ void load(const void* base, uint32_t byte_off) {
+        f = *reinterpret_cast<const float4*>(static_cast<const char*>(base) + byte_off);
+    }
+    __device__ __forceinline__ float get(int e) const {
+        return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
+    }
+    __device__ __forceinline__ uint16_t bits(int) const { return 0; }
+};
+
+// Preparation layout: CW columns per wave, NCG groups of 4 columns, NG
+// groups of RPG consecutive records.
+template <int C, int CKD>
+struct Geo {
+    static constexpr int CW = CKD / kNW;
+    static constexpr int NCG = CW / kPC;
+    static constexpr int NG = kWave / NCG;
+    static constexpr int RPG = C / NG;
+    static_assert(CW % kPC == 0 && RPG >= 1 && C % NG == 0, "unsupported shape");
+};
+
+template <int L>
+__device__ __forceinline__ void split4(const float (&x)[kPC], uint2 (&out)[L]) {
+    uint32_t lo[L], hi[L];
+    split_pair<L>(x[0], x[1], lo);
+    split_pair<L>(x[2], x[3], hi);
+#pragma unroll
+    for (int l = 0; l < L; l++) out[l] = make_uint2(lo[l], hi[l]);
+}
+
+__device__ __forceinline__ uint16_t elem(const uint2& v, int e) {
+    const uint32_t w = (e < 2) ? v.x : v.y;
+    return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// Store R consecutive 16-bit values (R in {1, 2, 4, 8}).
+template <int R>
+__device__ __forceinline__ void store_run(uint16_t* p, const uint16_t (&v)[R]) {
+    if constexpr (R == 1) {
+        p[0] = v[0];
+    } else if constexpr (R == 2) {
+        *reinterpret_cast<uint32_t*>(p) = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+    } else if constexpr (R == 4) {
+        uint2 x;
+        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+        *reinterpret_cast<uint2*>(p) = x;
+    } else {
+        uint4 x;
+        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+        x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+        x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+        *reinterpret_cast<uint4*>(p) = x;
+    }
+}
+
+__device__ __forceinline__ u16x8 lds8(const uint16_t* p) {
+    return *reinterpret_cast<const u16x8*>(p);
+}
+__device__ __forceinline__ u16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) {
+    const u16x4 a = *reinterpret_cast<const u16x4*>(p0);
+    const u16x4 b = *reinterpret_cast<const u16x4*>(p1);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// sum over term pairs (x, y) with x + y < max(LA, LB) of A_x B_y
+template <int LA, int LB>
+__device__ __forceinline__ void mma32_terms(const u16x8 (&a)[LA], const u16x8 (&b)[LB], f32x16& c) {
+    constexpr int L = LA > LB ? LA : LB;
+#pragma unroll
+    for (int x = 0; x < LA; x++)
+#pragma unroll
+        for (int y = 0; y < LB; y++)
+            if (x + y < L) c = mfma32(a[x], b[y], c);
+}
+template <int LA, int LB>
+__device__ __forceinline__ void mma16_terms(const u16x8 (&a)[LA], const u16x8 (&b)[LB], f32x4& c) {
+    constexpr int L = LA > LB ? LA : LB;
+#pragma unroll
+    for (int x = 0; x < LA; x++)
+#pragma unroll
+        for (int y = 0; y < LB; y++)
+            if (x + y < L) c = mfma16(a[x], b[y], c);
+}
+
+// f(std::integral_constant<int, i>) for i = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Barrier for LDS hazards only: global loads and atomics may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Causal 16x16 tile ti of A^T (s-tile st, r-tile rt).  The first nt(nt+1)/2
+// tiles have st <= rt; the remaining nt/2 are the tiles just above the
+// diagonal inside each 32-record block, stored as zeros.
+template <int C>
+__device__ __forceinline__ void a_tile(int ti, int& st, int& rt) {
+    constexpr int nt = C / 16, ncausal = nt * (nt + 1) / 2;
+    if (ti < ncausal) {
+        rt = 0;
+        while ((rt + 1) * (rt + 2) / 2 <= ti) rt++;
+        st = ti - rt * (rt + 1) / 2;
+    } else {
+        rt = 2 * (ti - ncausal);
+        st = rt + 1;
+    }
+}
+
+}  // namespace
+
+}  // namespace sse

@@ -1,0 +1,704 @@
+// chunk_ws.hip -- warp-specialised chunked gated linear attention for bf16
+// inputs on gfx950 (the routed, shared and local-state passes).
+//
+// Method: "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记",
+// §2.3 eqs. 12-14 (gated write and read of a partition state), §2.1 eq. 6
+// (diagonal decay), §2.5 (shared partition), §2.6 (each partition runs over
+// its own records, identity transition elsewhere; outputs summed back to the
+// token).  The chunked form is the one in chunk_gla.hip:
+//   Qt = q exp(b),  Kh = w kappa exp(-b),  A = (Qt Kh^T) masked to s <= r,
+//   O = w_r (A V + Qt S_in),  S_out = diag(exp(b_C)) (S_in + Kh^T V),
+// with b the in-chunk cumulative log decay, chunks of 32 records.
+//
+// Block = 8 waves.  Waves 0-3 consume: wave w keeps columns [32w, 32w+32) of
+// the fp32 state in MFMA accumulator registers and runs every MFMA of the
+// chunk.  Waves 4-7 produce: they load the records' rows, form the decayed
+// operands, split them into bf16 terms and store them in one of two LDS
+// stages.  Iteration n:
+//   producers: issue the row loads of chunk n+3 and the metadata loads of
+//              chunk n+5, prepare chunk n+1 into stage (n+1)%2, store the
+//              metadata of chunk n+4;
+//   consumers: finish chunk n-1 (O += A V with A from the previous
+//              iteration, then the output stores/atomics), compute the causal
+//              A tiles of chunk n, O = Qt S_in, and S = D (S + Kh^T V);
+//   one barrier.
+// The A tiles of chunk n are written by three waves and read by all four, so
+// their product with V waits one iteration (the barrier orders it); the V
+// operand of chunk n stays in registers meanwhile.
+//
+// LDS layouts (all reads are 16-byte, conflict-free for 8-lane groups):
+//   Qt, Kh record-major [r][j]: inside every 16 columns the 4-column blocks
+//     are stored in the order 0,2,1,3, so the 8 columns a lane needs as the
+//     MFMA partner of the state registers (rows 4h..4h+3 and 8+4h..8+4h+3 of
+//     each 16) are contiguous.
+//   Kh^T [j][s] and V^T [col][s]: the four 8-record blocks of a row are
+//     permuted by XOR with bits 3-4 of the row index, which spreads the
+//     producers' transposed 8-byte stores over all banks.
+#include "chunk_common.h"
+
+namespace sse {
+
+namespace {
+
+constexpr int kWsC = 32;          // records per chunk
+constexpr int kCons = 4;          // consumer waves
+constexpr int kProd = 4;          // producer waves
+constexpr int kWsThreads = (kCons + kProd) * kWave;
+constexpr int kRing = 8;          // metadata ring slots (6 are live at a time)
+constexpr int kL = 2;             // bf16 terms of Qt, Kh, A and S
+
+static_assert(kProd == kNW, "the preparation layout assumes four producer waves");
+
+template <int CK, int DV>
+struct WsStage {
+    static constexpr int QS = CK + 8;
+    static constexpr int TS = kWsC + 8;
+    uint16_t q[kL][kWsC][QS];     // Qt terms [r][perm(j)]
+    uint16_t kr[kL][kWsC][QS];    // Kh terms [s][perm(j)]
+    uint16_t kt[kL][CK][TS];      // Kh terms [j][swz(j, s)]
+    uint16_t vt[DV][TS];          // V (exact in bf16) [col][swz(col, s)]
+};
+
+template <int CK, int DV>
+struct WsSmem {
+    WsStage<CK, DV> st[2];
+    uint16_t a[2][kL][kWsC][kWsC + 8];  // A terms [r][s]
+    float ebc[3][CK];                   // exp(b_C) per state row, ring by chunk % 3
+    uint32_t mrow[kRing][kWsC];         // record row t*H + h (a real row even if padded)
+    float mcr[kRing][kWsC];             // lnz2 - log2 w (+inf if padded)
+    float mw[kRing][kWsC];              // read gate; -0.0 marks a padded record
+};
+
+// Storage column of the 4-column block starting at j (j % 4 == 0).
+__device__ __forceinline__ int perm_col(int j) {
+    const int b = (j >> 2) & 3;
+    return (j & ~15) | ((((b & 1) << 1) | (b >> 1)) << 2);
+}
+// Storage position of record s in row `row` of Kh^T / V^T.
+__device__ __forceinline__ int swz(int row, int s) {
+    return ((((s >> 3) ^ (row >> 3)) & 3) << 3) | (s & 7);
+}
+
+struct Meta {
+    int tok;
+    float cr, w;
+};
+
+}  // namespace
+
+template <int CK, int DV, int MODE>
+__global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs a) {
+    using SM = WsSmem<CK, DV>;
+    using GK = Geo<kWsC, CK>;
+    using GV = Geo<kWsC, DV>;
+    constexpr bool kLocal = MODE == kModeLocal;
+    constexpr int NS = DV / 32;       // consumer waves that own state columns
+    constexpr int RT_N = CK / 32;     // 32-row tiles of the state
+    constexpr int RPG = GK::RPG, RPGV = GV::RPG;
+    __shared__ __attribute__((aligned(16))) SM sm;
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+    const bool producer = wv >= kCons;
+    const int pw = wv - kCons;                                   // producer index
+    const int hh = lane / 32, l32 = lane % 32;
+    const int H = a.H, N = a.N;
+    const bool col_wave = !producer && (NS == kCons || wv < NS);
+
+    // ---------------- which records this block runs ----------------
+    int s, h, part, piece = 0, npieces = 1;
+    int64_t lo, n;
+    if constexpr (MODE == kModeRouted) {
+        // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD
+        // b % 8).  Map the N partitions of one (sequence, head) to the same
+        // XCD, dispatched together: they walk the same tokens at about the
+        // same pace, so the k reads of a token's rows and the k additions to
+        // its output row meet in that XCD's L2.
+        int g = blockIdx.x;
+        const int U = a.num_seqs * H;
+        if ((U & 7) == 0) {
+            const int x = g & 7, j = g >> 3;
+            g = ((j / N) * 8 + x) * N + j % N;
+        }
+        part = g % N;
+        s = g / N / H;
+        h = g / N % H;
+        lo = a.seg_offsets[g];
+        n = a.seg_offsets[g + 1] - lo;
+    } else {
+        const int sh = blockIdx.x;
+        s = sh / H;
+        h = sh % H;
+        part = N;
+        piece = blockIdx.y;
+        const int64_t t0 = a.cu[s], len = a.cu[s + 1] - t0;
+        npieces = len > 0 ? (int)((len + a.piece_len - 1) / a.piece_len) : 1;
+        if (piece >= npieces - (kLocal ? 1 : 0)) return;  // uniform
+        lo = t0 + (int64_t)piece * a.piece_len;
+        n = min<int64_t>(a.piece_len, len - (int64_t)piece * a.piece_len);
+        if (n < 0) n = 0;
+    }
+    const int64_t nchunks = (n + kWsC - 1) / kWsC;
+    const bool last_piece = piece == npieces - 1;
+    const int64_t sbase = (((int64_t)s * H + h) * (N + 1) + part) * CK * DV;
+    const int64_t abase = ((int64_t)s * H + h) * a.max_pieces;
+
+    const bf16_t* __restrict__ gq = static_cast<const bf16_t*>(a.q);
+    const bf16_t* __restrict__ gk = static_cast<const bf16_t*>(a.kl);
+    const bf16_t* __restrict__ gv = static_cast<const bf16_t*>(a.v);
+    const bf16_t* __restrict__ gl = static_cast<const bf16_t*>(a.la);
+
+    // ---------------- consumer state ----------------
+    // rows 32 rt + 8 (i/4) + 4 hh + i%4, column 32 wv + l32
+    const int col = 32 * wv + l32;
+    const uint32_t col4 = 4u * (uint32_t)col;
+    f32x16 S[RT_N];
+#pragma unroll
+    for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) S[rt][i] = 0.f;
+    if (col_wave && !kLocal) {
+        if (a.init) {
+#pragma unroll
+            for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    S[rt][i] = a.init[sbase + (int64_t)row * DV + col];
+                }
+        }
+        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the local-state pass
+        for (int p = 0; p < piece; p++) {
+            const int64_t ab = abase + p;
+#pragma unroll
+            for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    S[rt][i] = a.agg_D[ab * CK + row] * S[rt][i] +
+                               a.agg_S[(ab * CK + row) * DV + col];
+                }
+        }
+    }
+
+    // ---------------- producer: metadata ----------------
+    // Producer wave 0 loads the metadata of one chunk (lane % 32 = record,
+    // clamped into the segment so every load is valid) and stores it into the
+    // ring one iteration later.  Padded records keep a real row and carry a
+    // read gate of -0.0 and an exponent offset of +inf (so Kh = 0).
+    auto meta_load = [&](int64_t chunk, Meta& m) {
+        const int64_t idx = chunk * kWsC + (lane % kWsC);
+        const int64_t ci = idx < n ? idx : n - 1;
+        if constexpr (MODE == kModeRouted) {
+            m.tok = a.seg_tok[lo + ci];
+            m.cr = a.seg_cr[lo + ci];
+            m.w = a.seg_w[lo + ci];
+        } else {
+            m.tok = (int)(lo + ci);
+            m.cr = a.lnz2[((int64_t)m.tok) * H + h];
+            m.w = 1.f;
+        }
+    };
+    auto meta_store = [&](int64_t chunk, const Meta& m) {
+        if (lane < kWsC) {
+            const int slot = (int)(chunk % kRing);
+            const bool valid = chunk * kWsC + lane < n;
+            sm.mrow[slot][lane] = (uint32_t)m.tok * (uint32_t)H + (uint32_t)h;
+            sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
+            sm.mw[slot][lane] = valid ? m.w : -0.f;
+        }
+    };
+    auto is_real = [](float w) { return (__float_as_uint(w) >> 31) == 0u; };
+
+    // ---------------- producer: row loads ----------------
+    // lane = (group cg of 4 columns, group gk of RPG consecutive records)
+    const int cg = lane % GK::NCG, gk_ = lane / GK::NCG;
+    const int j0 = pw * GK::CW + cg * kPC, r0 = gk_ * RPG;
+    const int cgv = lane % GV::NCG, gv_ = lane / GV::NCG;
+    const int c0v = pw * GV::CW + cgv * kPC, r0v = gv_ * RPGV;
+    struct Raw {
+        Vec4<bf16_t> q[RPG], k[RPG], l[RPG], v[RPGV];
+    };
+    auto raw_load = [&](int64_t chunk, Raw& R) {
+        const int slot = (int)(chunk % kRing);
+        // byte offsets fit in 32 bits (checked on the host)
+#pragma unroll
+        for (int i = 0; i < RPG; i++) {
+            const uint32_t off = sm.mrow[slot][r0 + i] * (uint32_t)(CK * 2) + (uint32_t)(j0 * 2);
+            if constexpr (!kLocal) R.q[i].load(gq, off);
+            R.k[i].load(gk, off);
+            R.l[i].load(gl, off);
+        }
+#pragma unroll
+        for (int i = 0; i < RPGV; i++)
+            R.v[i].load(gv, sm.mrow[slot][r0v + i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+    };
+
+    // ---------------- producer: preparation of one chunk ----------------
+    float btot[kPC] = {0.f, 0.f, 0.f, 0.f};
+    auto prep = [&](int64_t chunk, const Raw& R) {
+        const int slot = (int)(chunk % kRing);
+        auto& st = sm.st[chunk & 1];
+        float run[kPC] = {0.f, 0.f, 0.f, 0.f};
+        float bb[RPG][kPC];
+#pragma unroll
+        for (int i = 0; i < RPG; i++) {
+            const bool valid = is_real(sm.mw[slot][r0 + i]);
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                const float x = valid ? R.l[i].get(e) : 0.f;
+                run[e] = fmaf(x, kLog2e, run[e]);
+                bb[i][e] = run[e];
+            }
+        }
+        float excl[kPC], ebc_own[kPC];
+#pragma unroll
+        for (int e = 0; e < kPC; e++) {
+            float inc = run[e];
+#pragma unroll
+            for (int off = GK::NCG; off < kWave; off <<= 1) {
+                const float y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            excl[e] = inc - run[e];
+            const float tot = __shfl(inc, kWave - GK::NCG + cg, kWave);
+            ebc_own[e] = __builtin_amdgcn_exp2f(tot);
+            if constexpr (kLocal) btot[e] += tot;
+        }
+        uint2 pk[RPG][kL];
+        const int jp = perm_col(j0);
+#pragma unroll
+        for (int i = 0; i < RPG; i++) {
+            const float cr = sm.mcr[slot][r0 + i];
+            float xq[kPC], xk[kPC];
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                const float b = bb[i][e] + excl[e];
+                if constexpr (!kLocal) xq[e] = R.q[i].get(e) * __builtin_amdgcn_exp2f(b);
+                xk[e] = __builtin_amdgcn_exp2f(fmaf(R.k[i].get(e), kLog2e, -cr) - b);
+            }
+            split4<kL>(xk, pk[i]);
+            if constexpr (!kLocal) {
+                uint2 pq[kL];
+                split4<kL>(xq, pq);
+#pragma unroll
+                for (int l = 0; l < kL; l++) {
+                    *reinterpret_cast<uint2*>(&st.q[l][r0 + i][jp]) = pq[l];
+                    *reinterpret_cast<uint2*>(&st.kr[l][r0 + i][jp]) = pk[i][l];
+                }
+            }
+        }
+        // Kh^T: the lane's RPG records of each of its 4 columns
+#pragma unroll
+        for (int e = 0; e < kPC; e++)
+#pragma unroll
+            for (int l = 0; l < kL; l++) {
+                uint16_t rr[RPG];
+#pragma unroll
+                for (int i = 0; i < RPG; i++) rr[i] = elem(pk[i][l], e);
+                store_run<RPG>(&st.kt[l][j0 + e][swz(j0 + e, r0)], rr);
+            }
+        // V^T
+#pragma unroll
+        for (int e = 0; e < kPC; e++) {
+            uint16_t rr[RPGV];
+#pragma unroll
+            for (int i = 0; i < RPGV; i++) rr[i] = R.v[i].bits(e);
+            store_run<RPGV>(&st.vt[c0v + e][swz(c0v + e, r0v)], rr);
+        }
+        if (gk_ == 0)
+#pragma unroll
+            for (int e = 0; e < kPC; e++) sm.ebc[chunk % 3][j0 + e] = ebc_own[e];
+    };
+
+    // ---------------- consumer: one software-pipelined iteration ----------------
+    // The MFMA work of iteration nn is a fixed list of steps:
+    //   F        finish chunk nn-1: Op += A V (A from the previous iteration,
+    //            V operand kept in registers); its outputs follow later
+    //   A0 ..    this wave's causal 16x16 A tile of chunk nn, one 32-wide k-step
+    //            each (waves 0, 1, 2 compute (s-tile, r-tile) = (0,0), (0,1),
+    //            (1,1); wave 3 repeats (1,1) and stores the same bits, so no
+    //            wave branches; the (1,0) tile is zero and written once)
+    //   R0 ..    Oc = Qt S_in, one 16-row k-step each: the B operand is the
+    //            state registers (rows 16 kk + {4 hh + e, 8 + 4 hh + e}, e < 4,
+    //            = registers 8 (kk%2) + 0..7 of tile kk/2), split into bf16
+    //            terms on the fly; the permuted Qt storage puts the matching 8
+    //            columns side by side
+    //   U0 ..    S += Kh^T V, one (row tile, 16-record k-step) each
+    // The decay diag(exp(b_C)) of a chunk is applied lazily: between
+    // iterations S holds S_in + Kh^T V of the last chunk, and the readout
+    // steps of the next chunk scale each group of 8 state registers just
+    // before splitting them (the local-state pass, which has no readout,
+    // scales the whole state before its first update).
+    // The LDS operands of step s+2 are read while step s runs (three register
+    // slots) and scheduling fences keep that order, so LDS latency hides
+    // behind the MFMA pipeline.
+    const int g16 = lane / 16, l16 = lane % 16;
+    const int sT = wv >= 2 ? 1 : 0, rT = wv == 0 ? 0 : 1;
+    constexpr int nA = CK / 32, nR = CK / 16, nU = RT_N * 2;
+    constexpr int sF = 0, sA = 1, sR = sA + nA, sU = sR + nR, sEnd = sU + nU;
+    constexpr int sOut = sA + (nA > 1 ? 1 : 0);   // outputs of chunk nn-1 after this step
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    // operands of step s of iteration nn
+    auto fetch = [&](auto sI, int64_t nn, u16x8(&o)[4]) {
+        constexpr int s = decltype(sI)::value;
+        const auto& st = sm.st[nn & 1];
+        if (!(s >= sA && s < sR) && !col_wave) return;  // waves without state columns
+        if constexpr (s == sF) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int l = 0; l < kL; l++)
+                    o[2 * ks + l] = lds8(&sm.a[(nn - 1) & 1][l][l32][16 * ks + 8 * hh]);
+        } else if constexpr (s < sR) {
+            constexpr int kk = s - sA;
+#pragma unroll
+            for (int l = 0; l < kL; l++) {
+                o[l] = lds8(&st.kr[l][16 * sT + l16][32 * kk + 8 * g16]);
+                o[2 + l] = lds8(&st.q[l][16 * rT + l16][32 * kk + 8 * g16]);
+            }
+        } else if constexpr (s < sU) {
+            constexpr int kk = s - sR;
+#pragma unroll
+            for (int l = 0; l < kL; l++) o[l] = lds8(&st.q[l][l32][16 * kk + 8 * hh]);
+            // exp(b_C) of chunk nn-1 for the 8 state rows of this k-step
+            const float* d = sm.ebc[(nn + 2) % 3];
+            o[2] = *reinterpret_cast<const u16x8*>(&d[16 * kk + 4 * hh]);
+            o[3] = *reinterpret_cast<const u16x8*>(&d[16 * kk + 8 + 4 * hh]);
+        } else {
+            constexpr int u = s - sU, rt = u / 2, ks = u % 2;
+            const int j = 32 * rt + l32;
+#pragma unroll
+            for (int l = 0; l < kL; l++) o[l] = lds8(&st.kt[l][j][swz(j, 16 * ks + 8 * hh)]);
+        }
+    };
+
+    // outputs of the finished chunk: o[token] (+)= w_r Op[r], branch-free.
+    // Routed: a padded record adds 0 * O to a real row.  Shared: a padded
+    // record's store goes to the dummy row.
+    auto outputs = [&](const f32x16& Op, const uint4 (&mr)[4], const float4 (&mw4)[4]) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const uint32_t rows[4] = {mr[q4].x, mr[q4].y, mr[q4].z, mr[q4].w};
+            const float ws[4] = {mw4[q4].x, mw4[q4].y, mw4[q4].z, mw4[q4].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float val = ws[e] * Op[4 * q4 + e];
+                const uint32_t off = rows[e] * (uint32_t)(DV * 4) + col4;
+                if constexpr (MODE == kModeShared) {
+                    const bool valid = is_real(ws[e]);
+                    char* base = reinterpret_cast<char*>(valid ? a.o : a.trash);
+                    *reinterpret_cast<float*>(base + (valid ? off : col4)) = val;
+                } else {
+                    atomic_add_f32(reinterpret_cast<float*>(reinterpret_cast<char*>(a.o) + off), val);
+                }
+            }
+        }
+    };
+    auto decay = [&](f32x16& Srt, const float4 (&e4)[4]) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            Srt[4 * q4 + 0] *= e4[q4].x;
+            Srt[4 * q4 + 1] *= e4[q4].y;
+            Srt[4 * q4 + 2] *= e4[q4].z;
+            Srt[4 * q4 + 3] *= e4[q4].w;
+        }
+    };
+
+    // Iteration nn (PREV: finish chunk nn-1; CUR: run chunk nn).  Op holds
+    // the readout of chunk nn-1 and Vp its V operand; Oc and Vc receive those
+    // of chunk nn.
+    auto iteration = [&](auto prevI, auto curI, int64_t nn, f32x16& Op, u16x8(&Vp)[2], f32x16& Oc,
+                         u16x8(&Vc)[2]) {
+        constexpr bool HASPREV = decltype(prevI)::value;   // S holds chunk nn-1 undecayed
+        constexpr bool PREV = HASPREV && !kLocal;
+        constexpr bool CUR = decltype(curI)::value;
+        const auto& st = sm.st[nn & 1];
+        u16x8 ob[3][4];
+        uint4 mr[4];
+        float4 mw4[4];
+        f32x4 Aacc = {0.f, 0.f, 0.f, 0.f};
+        auto fetch_extra = [&](auto sI) {
+            constexpr int s = decltype(sI)::value;
+            if (!col_wave) return;
+            if constexpr (s == sF && PREV) {
+                const int slot = (int)((nn - 1) % kRing);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) {
+                    mr[q4] = *reinterpret_cast<const uint4*>(&sm.mrow[slot][8 * q4 + 4 * hh]);
+                    mw4[q4] = *reinterpret_cast<const float4*>(&sm.mw[slot][8 * q4 + 4 * hh]);
+                }
+            }
+            if constexpr (CUR && s == (kLocal ? sU : sR)) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) Vc[ks] = lds8(&st.vt[col][swz(col, 16 * ks + 8 * hh)]);
+            }
+        };
+        auto compute = [&](auto sI, const u16x8(&o)[4]) {
+            constexpr int s = decltype(sI)::value;
+            if (!(s >= sA && s < sR) && !col_wave) return;  // waves without state columns
+            if constexpr (s == sF) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) {
+                    const u16x8 aa[kL] = {o[2 * ks], o[2 * ks + 1]};
+                    const u16x8 vb[1] = {Vp[ks]};
+                    mma32_terms<kL, 1>(aa, vb, Op);
+                }
+            } else if constexpr (s < sR) {
+                const u16x8 ka[kL] = {o[0], o[1]}, qb[kL] = {o[2], o[3]};
+                mma16_terms<kL, kL>(ka, qb, Aacc);
+            } else if constexpr (s < sU) {
+                constexpr int kk = s - sR;
+                if constexpr (kk == 0)
+#pragma unroll
+                    for (int i = 0; i < 16; i++) Oc[i] = 0.f;
+                if constexpr (HASPREV) {
+                    // S_in of this chunk = diag(exp(b_C) of chunk nn-1) S'
+                    const float4 d0 = __builtin_bit_cast(float4, o[2]);
+                    const float4 d1 = __builtin_bit_cast(float4, o[3]);
+                    const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; e++) S[kk / 2][8 * (kk % 2) + e] *= dd[e];
+                }
+                u16x8 sb[kL];
+                uint32_t pr[4][kL];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++)
+                    split_pair<kL>(S[kk / 2][8 * (kk % 2) + 2 * e2], S[kk / 2][8 * (kk % 2) + 2 * e2 + 1],
+                                   pr[e2]);
+#pragma unroll
+                for (int l = 0; l < kL; l++)
+                    sb[l] = __builtin_bit_cast(u16x8, make_uint4(pr[0][l], pr[1][l], pr[2][l], pr[3][l]));
+                const u16x8 qa[kL] = {o[0], o[1]};
+                mma32_terms<kL, kL>(qa, sb, Oc);
+            } else {
+                constexpr int u = s - sU, rt = u / 2, ks = u % 2;
+                if constexpr (kLocal && HASPREV && u == 0) {
+                    // no readout in this mode: apply the previous chunk's decay here
+                    const float* d = sm.ebc[(nn + 2) % 3];
+#pragma unroll
+                    for (int r2 = 0; r2 < RT_N; r2++) {
+                        float4 e4[4];
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; q4++)
+                            e4[q4] = *reinterpret_cast<const float4*>(&d[32 * r2 + 8 * q4 + 4 * hh]);
+                        decay(S[r2], e4);
+                    }
+                }
+                const u16x8 ka[kL] = {o[0], o[1]};
+                const u16x8 vb[1] = {Vc[ks]};
+                mma32_terms<kL, 1>(ka, vb, S[rt]);
+            }
+        };
+        // work that waits for an earlier step's MFMA results
+        auto after = [&](auto sI) {
+            constexpr int s = decltype(sI)::value;
+            if constexpr (PREV && s == (CUR ? sOut : sF))
+                if (col_wave) outputs(Op, mr, mw4);
+            if constexpr (CUR && !kLocal && s == sR) {
+                // causal mask, bf16 terms, store of this wave's A tile
+                const int r = 16 * rT + l16, s0 = 16 * sT + 4 * g16;
+                if (sT == rT) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (s0 + i > r) Aacc[i] = 0.f;
+                }
+                uint32_t p01[kL], p23[kL];
+                split_pair<kL>(Aacc[0], Aacc[1], p01);
+                split_pair<kL>(Aacc[2], Aacc[3], p23);
+#pragma unroll
+                for (int l = 0; l < kL; l++)
+                    *reinterpret_cast<uint2*>(&sm.a[nn & 1][l][r][s0]) = make_uint2(p01[l], p23[l]);
+            }
+        };
+        // Steps first .. last run in order (all of them enabled); the
+        // operands of step s+2 are read after step s is issued.
+        constexpr int first = PREV ? sF : (kLocal ? sU : sA);
+        constexpr int last = CUR ? sEnd - 1 : sF;
+        static_for<first, (first + 2 <= last + 1 ? first + 2 : last + 1)>([&](auto sI) {
+            constexpr int s = decltype(sI)::value;
+            fetch(sI, nn, ob[s % 3]);
+            fetch_extra(sI);
+        });
+        fence();
+        static_for<first, last + 1>([&](auto sI) {
+            constexpr int s = decltype(sI)::value;
+            compute(sI, ob[s % 3]);
+            after(sI);
+            if constexpr (s + 2 <= last) {
+                constexpr std::integral_constant<int, s + 2> nI{};
+                fetch(nI, nn, ob[(s + 2) % 3]);
+                fetch_extra(nI);
+            }
+            fence();
+        });
+    };
+
+    // ---------------- pipeline ----------------
+    // Producers and consumers run separate loops (so their registers are not
+    // live at the same time) with the same barriers: two in the prologue and
+    // one per iteration nn = 0 .. nchunks.
+    if (nchunks > 0) {
+        if (producer) {
+            // Every producer wave issues the same loads in every step (chunks
+            // past the end re-load clamped, valid rows), so the compiler can
+            // count the loads in flight and wait only for the ones it uses.
+            Raw R0, R1, R2;
+            Meta M0, M1, M2;
+            meta_load(0, M0);
+            if (pw == 0) meta_store(0, M0);
+            meta_load(1, M0);
+            if (pw == 0) meta_store(1, M0);
+            meta_load(2, M0);
+            if (pw == 0) meta_store(2, M0);
+            meta_load(3, M0);
+            if (pw == 0) meta_store(3, M0);
+            lds_barrier();
+            meta_load(4, M2);
+            raw_load(0, R0);
+            raw_load(1, R1);
+            raw_load(2, R2);
+            prep(0, R0);
+            lds_barrier();
+            // step nn: load the rows of nn+3 into Rl and the metadata of nn+5
+            // into Ml, prepare nn+1 from Rp, store the metadata of nn+4 from
+            // Ms.  Chunk c's rows live in R[c % 3], so every load has two
+            // steps to arrive.
+            // The metadata loads go first: the counter of outstanding loads is
+            // in order, so waiting for them next step must not also wait for
+            // this step's row loads.
+            auto step = [&](int64_t nn, Raw& Rl, const Raw& Rp, Meta& Ml, const Meta& Ms) {
+                meta_load(nn + 5, Ml);
+                raw_load(nn + 3, Rl);
+                if (nn + 1 < nchunks) prep(nn + 1, Rp);
+                if (pw == 0) meta_store(nn + 4, Ms);
+                lds_barrier();
+            };
+            int64_t nn = 0;
+            for (; nn + 2 <= nchunks; nn += 3) {
+                step(nn, R0, R1, M0, M2);
+                step(nn + 1, R1, R2, M1, M0);
+                step(nn + 2, R2, R0, M2, M1);
+            }
+            if (nn <= nchunks) step(nn, R0, R1, M0, M2);
+            if (nn + 1 <= nchunks) step(nn + 1, R1, R2, M1, M0);
+        } else {
+            if (!kLocal && wv == 3) {
+                // the zero (r-tile 0, s-tile 1) block of A in both buffers
+                for (int i = lane; i < 2 * kL * 16; i += kWave) {
+                    const int b = i / (kL * 16), l = (i / 16) % kL, r = i % 16;
+                    *reinterpret_cast<uint4*>(&sm.a[b][l][r][16]) = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(&sm.a[b][l][r][24]) = make_uint4(0, 0, 0, 0);
+                }
+            }
+            lds_barrier();
+            lds_barrier();
+            // iteration 0 runs chunk 0; iterations 1 .. nchunks-1 finish the
+            // previous chunk and run the next (unrolled by two so the readout
+            // and V registers alternate without copies); the last iteration
+            // finishes chunk nchunks-1.
+            using T_ = std::true_type;
+            using F_ = std::false_type;
+            f32x16 O0, O1;
+            u16x8 V0[2], V1[2];
+            iteration(F_{}, T_{}, 0, O1, V1, O0, V0);
+            lds_barrier();
+            int64_t nn = 1;
+            for (; nn + 1 < nchunks; nn += 2) {
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
+                lds_barrier();
+                iteration(T_{}, T_{}, nn + 1, O1, V1, O0, V0);
+                lds_barrier();
+            }
+            if (nn < nchunks) {
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
+                lds_barrier();
+                iteration(T_{}, F_{}, nn + 1, O1, V1, O0, V0);
+            } else {
+                iteration(T_{}, F_{}, nn, O0, V0, O1, V1);
+            }
+            lds_barrier();
+        }
+    }
+
+    // ---------------- results ----------------
+    // the state still lacks the decay of the last chunk
+    if (col_wave && nchunks > 0) {
+        const float* d = sm.ebc[(nchunks - 1) % 3];
+#pragma unroll
+        for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) S[rt][i] *= d[32 * rt + 8 * (i / 4) + 4 * hh + (i % 4)];
+    }
+    if constexpr (kLocal) {
+        // local state and decay product of this piece
+        if (col_wave) {
+#pragma unroll
+            for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                    a.agg_S[((abase + piece) * CK + row) * DV + col] = S[rt][i];
+                }
+        }
+        if (producer && gk_ == 0)
+#pragma unroll
+            for (int e = 0; e < kPC; e++)
+                a.agg_D[(abase + piece) * CK + j0 + e] = __builtin_amdgcn_exp2f(btot[e]);
+    } else if (col_wave && last_piece) {
+#pragma unroll
+        for (int rt = 0; rt < RT_N; rt++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
+                a.final_states[sbase + (int64_t)row * DV + col] = S[rt][i];
+            }
+    }
+}
+
+// ============================ launcher ============================
+namespace {
+
+template <int CK, int DV, int MODE>
+void launch_ws_cfg(const ChunkArgs& a, hipStream_t st) {
+    dim3 grid;
+    if (MODE == kModeRouted)
+        grid = dim3((unsigned)(a.num_seqs * a.H * a.N));
+    else
+        grid = dim3((unsigned)(a.num_seqs * a.H),
+                    (unsigned)(MODE == kModeLocal ? a.max_pieces - 1 : a.max_pieces));
+    if (grid.x == 0 || grid.y == 0) return;
+    chunk_ws_kernel<CK, DV, MODE><<<grid, kWsThreads, 0, st>>>(a);
+}
+
+template <int MODE>
+bool launch_ws_shape(const ChunkArgs& a, int c, int d, hipStream_t st) {
+#define SSE_WS_CASE(CC, DD)                      \
+    if (c == CC && d == DD) {                    \
+        launch_ws_cfg<CC, DD, MODE>(a, st);      \
+        return true;                             \
+    }
+    SSE_WS_CASE(32, 32) SSE_WS_CASE(32, 64) SSE_WS_CASE(32, 128)
+    SSE_WS_CASE(64, 32) SSE_WS_CASE(64, 64) SSE_WS_CASE(64, 128)
+    SSE_WS_CASE(128, 32) SSE_WS_CASE(128, 64) SSE_WS_CASE(128, 128)
+#undef SSE_WS_CASE
+    return false;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_ws(int mode, const ChunkArgs& a, int c, int d, hipStream_t st) {
+    if ((int64_t)a.num_seqs * a.H == 0) return hipSuccess;
+    bool ok = false;
+    if (mode == kModeLocal)
+        ok = launch_ws_shape<kModeLocal>(a, c, d, st);
+    else if (mode == kModeShared)
+        ok = launch_ws_shape<kModeShared>(a, c, d, st);
+    else if (mode == kModeRouted)
+        ok = launch_ws_shape<kModeRouted>(a, c, d, st);
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace sse
