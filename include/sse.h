@@ -29,7 +29,7 @@
  *     SSE_F32 (float) or SSE_BF16 (bfloat16, 2-byte bit patterns).  States,
  *     outputs and all accumulation are fp32.
  *   - Supported sizes: c, d in {32, 64, 128}; 1 <= topk <= N <= 64,
- *     topk <= 8; H >= 1.
+ *     topk <= 8; 1 <= H <= 256.
  *   - Argument checks run on the host before any launch.  They return
  *     SSE_ERR_INVALID_ARG (null pointer, negative or inconsistent size),
  *     SSE_ERR_UNSUPPORTED (size outside the supported set) or

@@ -16,8 +16,8 @@
 // operands, split them into bf16 terms and store them in one of two LDS
 // stages.  Iteration n:
 //   producers: issue the row loads of chunk n+3 and the metadata loads of
-//              chunk n+5, prepare chunk n+1 into stage (n+1)%2, store the
-//              metadata of chunk n+4;
+//              chunk n+6, prepare chunk n+1 into stage (n+1)%2, store the
+//              metadata of chunk n+5 into the ring;
 //   consumers: finish chunk n-1 (O += A V with A from the previous
 //              iteration, then the output stores/atomics), compute the causal
 //              A tiles of chunk n, O = Qt S_in, and S = D (S + Kh^T V);
@@ -44,7 +44,7 @@ constexpr int kWsC = 32;          // records per chunk
 constexpr int kCons = 4;          // consumer waves
 constexpr int kProd = 4;          // producer waves
 constexpr int kWsThreads = (kCons + kProd) * kWave;
-constexpr int kRing = 8;          // metadata ring slots (6 are live at a time)
+constexpr int kRing = 8;          // metadata ring slots (7 are live at a time)
 constexpr int kL = 2;             // bf16 terms of Qt, Kh, A and S
 
 static_assert(kProd == kNW, "the preparation layout assumes four producer waves");
@@ -219,31 +219,99 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     struct Raw {
         Vec4<bf16_t> q[RPG], k[RPG], l[RPG], v[RPGV];
     };
-    auto raw_load = [&](int64_t chunk, Raw& R) {
+    // row indices (from the metadata ring) of the next chunk to load, and the
+    // read gates / exponent offsets of the next chunk to prepare: read from
+    // LDS one step before they are needed
+    uint32_t rowq[RPG], rowv[RPGV];
+    float gw[RPG], gcr[RPG];
+    auto read_rows = [&](int64_t chunk) {
         const int slot = (int)(chunk % kRing);
+#pragma unroll
+        for (int i = 0; i < RPG; i++) rowq[i] = sm.mrow[slot][r0 + i];
+#pragma unroll
+        for (int i = 0; i < RPGV; i++) rowv[i] = sm.mrow[slot][r0v + i];
+    };
+    auto read_gates = [&](int64_t chunk) {
+        const int slot = (int)(chunk % kRing);
+#pragma unroll
+        for (int i = 0; i < RPG; i++) {
+            gw[i] = sm.mw[slot][r0 + i];
+            gcr[i] = sm.mcr[slot][r0 + i];
+        }
+    };
+    auto raw_load = [&](Raw& R) {
         // byte offsets fit in 32 bits (checked on the host)
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const uint32_t off = sm.mrow[slot][r0 + i] * (uint32_t)(CK * 2) + (uint32_t)(j0 * 2);
+            const uint32_t off = rowq[i] * (uint32_t)(CK * 2) + (uint32_t)(j0 * 2);
             if constexpr (!kLocal) R.q[i].load(gq, off);
             R.k[i].load(gk, off);
             R.l[i].load(gl, off);
         }
 #pragma unroll
         for (int i = 0; i < RPGV; i++)
-            R.v[i].load(gv, sm.mrow[slot][r0v + i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+            R.v[i].load(gv, rowv[i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+    };
+
+    // Inclusive scan of x over the record groups of this lane's column group
+    // (lanes cg, cg + NCG, ...), plus the total over all groups.  With 8
+    // column groups (c = 128) the groups are 8 lanes apart: two per 16-lane
+    // row, so the scan uses a DPP row shift inside rows and the row-swap
+    // permutations across rows, with no LDS traffic.
+    auto group_scan = [&](float x, float& incl, float& total) {
+        if constexpr (GK::NCG == 8) {
+            const int rowi = lane >> 4;
+            const bool hi8 = (lane & 8) != 0;
+            // within the row: the odd group adds the even one
+            const float a1 = x + __builtin_bit_cast(
+                                     float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                        0x118, 0xf, 0xf, false));
+            // row total for this column group (the odd group's value)
+            const float sh = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a1), 0x108, 0xf, 0xf, false));
+            const float rt = hi8 ? a1 : sh;
+            // The row swaps are written as inline assembly (the compiler's
+            // model of the swap builtins merges their two results, which
+            // loses the select between them below), padded with wait states
+            // on both sides since the compiler cannot see their hazards.
+            // v_permlane16_swap a, b: odd rows of a <-> even rows of b, so
+            // with a = b = rt, a's odd rows hold the even row's total and b's
+            // even rows hold the odd row's total.
+            unsigned e16 = __builtin_bit_cast(unsigned, rt), o16 = e16;
+            asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4" : "+v"(e16), "+v"(o16));
+            const float from_even = __builtin_bit_cast(float, e16);
+            const float from_odd = __builtin_bit_cast(float, o16);
+            const bool odd = (rowi & 1) != 0;
+            const float pair = rt + (odd ? from_even : from_odd);
+            // v_permlane32_swap a, b: upper half of a <-> lower half of b
+            unsigned l32v = __builtin_bit_cast(unsigned, pair), h32v = l32v;
+            asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(l32v), "+v"(h32v));
+            const float low_pair = __builtin_bit_cast(float, l32v);    // upper half: rows 0-1 total
+            const float high_pair = __builtin_bit_cast(float, h32v);   // lower half: rows 2-3 total
+            const bool upper = lane >= 32;
+            incl = a1 + (odd ? from_even : 0.f) + (upper ? low_pair : 0.f);
+            total = pair + (upper ? low_pair : high_pair);
+        } else {
+            float inc = x;
+#pragma unroll
+            for (int off = GK::NCG; off < kWave; off <<= 1) {
+                const float y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            incl = inc;
+            total = __shfl(inc, kWave - GK::NCG + cg, kWave);
+        }
     };
 
     // ---------------- producer: preparation of one chunk ----------------
     float btot[kPC] = {0.f, 0.f, 0.f, 0.f};
     auto prep = [&](int64_t chunk, const Raw& R) {
-        const int slot = (int)(chunk % kRing);
         auto& st = sm.st[chunk & 1];
         float run[kPC] = {0.f, 0.f, 0.f, 0.f};
         float bb[RPG][kPC];
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const bool valid = is_real(sm.mw[slot][r0 + i]);
+            const bool valid = is_real(gw[i]);
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
                 const float x = valid ? R.l[i].get(e) : 0.f;
@@ -254,14 +322,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         float excl[kPC], ebc_own[kPC];
 #pragma unroll
         for (int e = 0; e < kPC; e++) {
-            float inc = run[e];
-#pragma unroll
-            for (int off = GK::NCG; off < kWave; off <<= 1) {
-                const float y = __shfl_up(inc, off, kWave);
-                if (lane >= off) inc += y;
-            }
-            excl[e] = inc - run[e];
-            const float tot = __shfl(inc, kWave - GK::NCG + cg, kWave);
+            float incl, tot;
+            group_scan(run[e], incl, tot);
+            excl[e] = incl - run[e];
             ebc_own[e] = __builtin_amdgcn_exp2f(tot);
             if constexpr (kLocal) btot[e] += tot;
         }
@@ -269,7 +332,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         const int jp = perm_col(j0);
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const float cr = sm.mcr[slot][r0 + i];
+            const float cr = gcr[i];
             float xq[kPC], xk[kPC];
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
@@ -546,33 +609,38 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             // count the loads in flight and wait only for the ones it uses.
             Raw R0, R1, R2;
             Meta M0, M1, M2;
-            meta_load(0, M0);
-            if (pw == 0) meta_store(0, M0);
-            meta_load(1, M0);
-            if (pw == 0) meta_store(1, M0);
-            meta_load(2, M0);
-            if (pw == 0) meta_store(2, M0);
-            meta_load(3, M0);
-            if (pw == 0) meta_store(3, M0);
+            for (int c = 0; c < 5; c++) {
+                meta_load(c, M0);
+                if (pw == 0) meta_store(c, M0);
+            }
             lds_barrier();
-            meta_load(4, M2);
-            raw_load(0, R0);
-            raw_load(1, R1);
-            raw_load(2, R2);
+            meta_load(5, M2);
+            read_rows(0);
+            raw_load(R0);
+            read_rows(1);
+            raw_load(R1);
+            read_rows(2);
+            raw_load(R2);
+            read_rows(3);
+            read_gates(0);
             prep(0, R0);
+            read_gates(1);
             lds_barrier();
-            // step nn: load the rows of nn+3 into Rl and the metadata of nn+5
-            // into Ml, prepare nn+1 from Rp, store the metadata of nn+4 from
-            // Ms.  Chunk c's rows live in R[c % 3], so every load has two
-            // steps to arrive.
-            // The metadata loads go first: the counter of outstanding loads is
-            // in order, so waiting for them next step must not also wait for
-            // this step's row loads.
+            // Step nn: issue the metadata loads of chunk nn+6 (first: the
+            // counter of outstanding loads is in order, so waiting for them
+            // next step must not also wait for this step's row loads), the
+            // row loads of chunk nn+3 (rows read last step; chunk c's rows
+            // live in R[c % 3], so every load has two steps to arrive), read
+            // the rows of chunk nn+4, prepare chunk nn+1 (gates read last
+            // step), read the gates of chunk nn+2, store the metadata of chunk
+            // nn+5.
             auto step = [&](int64_t nn, Raw& Rl, const Raw& Rp, Meta& Ml, const Meta& Ms) {
-                meta_load(nn + 5, Ml);
-                raw_load(nn + 3, Rl);
+                meta_load(nn + 6, Ml);
+                raw_load(Rl);
+                read_rows(nn + 4);
                 if (nn + 1 < nchunks) prep(nn + 1, Rp);
-                if (pw == 0) meta_store(nn + 4, Ms);
+                read_gates(nn + 2);
+                if (pw == 0) meta_store(nn + 5, Ms);
                 lds_barrier();
             };
             int64_t nn = 0;

@@ -6,10 +6,12 @@
 // sample and partition, time order kept, new segment offsets).
 //
 // Grouping is a stable counting sort done in three launches:
-//   route_count  one block per (sequence*head, 256-token block): routes its
-//                tokens, counts records per partition in LDS, and stores the
-//                log2 normaliser of each token's key softmax (§2.3, eq. 11)
-//                so that later passes need no row reduction;
+//   route_count  one block per (sequence, 64-token block), all heads: routes
+//                the block's rows (one lane per row), counts records per
+//                (head, partition) in LDS, and stores the log2 normaliser of
+//                each row's key softmax (§2.3, eq. 11; 16 lanes per row,
+//                coalesced 16-byte loads) so that later passes need no row
+//                reduction;
 //   block_scan   one block per (sequence, head): exclusive scan over its
 //                N x blocks counts.  The records of (s, h) occupy a known
 //                contiguous range (every token contributes exactly k
@@ -20,40 +22,71 @@
 
 namespace sse {
 
-constexpr int kTokBlock = 256;  // tokens per grouping block (one per thread)
+constexpr int kTokBlock = 64;   // tokens per grouping block (one wave)
 
 // Router for one row of N logits: top-k by logit (descending, equal logits ->
 // lower index) and the softmax probability of each chosen partition.
+// Loads one row of N router logits as fp32 (-inf past N).
 template <int NMAX, typename TIn>
-__device__ __forceinline__ void route_row(const TIn* __restrict__ row, int N, int K,
-                                          int (&sel)[kMaxTopK], float (&w)[kMaxTopK]) {
-    float z[NMAX];
+__device__ __forceinline__ void load_router_row(const TIn* __restrict__ row, int N,
+                                                float (&z)[NMAX]) {
+    constexpr int kVec = 16 / (int)sizeof(TIn);  // values per 16-byte load
+    if (N == NMAX && NMAX % kVec == 0) {
+        // whole row in 16-byte loads (rows are 16-byte aligned when N is a
+        // multiple of kVec)
 #pragma unroll
-    for (int i = 0; i < NMAX; i++) z[i] = (i < N) ? to_f32(row[i]) : -INFINITY;
+        for (int u = 0; u < NMAX / kVec; u++) {
+            const uint4 v = reinterpret_cast<const uint4*>(row)[u];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if constexpr (sizeof(TIn) == 2) {
+                    z[kVec * u + 2 * e] = __uint_as_float(w4[e] << 16);
+                    z[kVec * u + 2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+                } else {
+                    z[kVec * u + e] = __uint_as_float(w4[e]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NMAX; i++) z[i] = (i < N) ? to_f32(row[i]) : -INFINITY;
+    }
+}
+
+// Router for one row of N logits (entries past N are -inf): top-k by logit
+// (descending, equal logits -> lower index: a strictly greater value is
+// needed to replace the current best) and the softmax probability of each
+// chosen partition.  Branch-free: every choice is a select.
+template <int NMAX>
+__device__ __forceinline__ void route_row(const float (&z)[NMAX], int N, int K,
+                                          int (&sel)[kMaxTopK], float (&w)[kMaxTopK]) {
     float m = z[0];
 #pragma unroll
     for (int i = 1; i < NMAX; i++) m = fmaxf(m, z[i]);
+    const float m2 = m * kLog2e;
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < NMAX; i++)
-        if (i < N) s += expf(z[i] - m);
-    uint64_t taken = 0;
+    for (int i = 0; i < NMAX; i++) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, -m2));
+    const float inv_s = 1.f / s;
+    float zz[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; i++) zz[i] = z[i];
 #pragma unroll
     for (int r = 0; r < kMaxTopK; r++) {
         if (r < K) {
-            int best = -1;
             float bv = -INFINITY;
+            int best = 0;
 #pragma unroll
             for (int i = 0; i < NMAX; i++) {
-                bool ok = (i < N) && !((taken >> i) & 1ull);
-                if (ok && (best < 0 || z[i] > bv)) {
-                    best = i;
-                    bv = z[i];
-                }
+                const bool gt = zz[i] > bv;
+                bv = gt ? zz[i] : bv;
+                best = gt ? i : best;
             }
-            taken |= 1ull << best;
+#pragma unroll
+            for (int i = 0; i < NMAX; i++) zz[i] = (i == best) ? -INFINITY : zz[i];
             sel[r] = best;
-            w[r] = expf(bv - m) / s;
+            w[r] = __builtin_amdgcn_exp2f(fmaf(bv, kLog2e, -m2)) * inv_s;
         }
     }
 }
@@ -67,7 +100,9 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const TIn* __restrict_
     if (r >= rows) return;
     int sel[kMaxTopK];
     float w[kMaxTopK];
-    route_row<NMAX, TIn>(z + r * N, N, K, sel, w);
+    float zr[NMAX];
+    load_router_row<NMAX, TIn>(z + r * N, N, zr);
+    route_row<NMAX>(zr, N, K, sel, w);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; j++)
         if (j < K) {
@@ -102,54 +137,127 @@ __device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
     }
 }
 
-// Route the tokens of one (sequence, head, token block), count the records
-// per partition, and store lnz2 = log2 of the key-softmax denominator
+// Reduce x over groups of L consecutive lanes (every lane gets the result).
+// A 16-lane group is one DPP row: four row rotations, no LDS traffic.
+template <int L, typename Op>
+__device__ __forceinline__ float row_reduce(float x, Op op) {
+    if constexpr (L == 16) {
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false)));
+        return x;
+    } else {
+#pragma unroll
+        for (int o = L / 2; o >= 1; o >>= 1) x = op(x, __shfl_xor(x, o, kWave));
+        return x;
+    }
+}
+
+// Route the rows of one (sequence, 64-token block) for all heads, count the
+// records per (head, partition) in LDS (cnt, H x N ints of dynamic shared
+// memory), and store lnz2 = log2 of the key-softmax denominator
 // sum_j 2^((kl_j - m) log2 e) plus m log2 e, so that kappa_j =
-// 2^(kl_j log2 e - lnz2).  Blocks of one token block are adjacent in launch
-// order across heads (they read neighbouring rows).
+// 2^(kl_j log2 e - lnz2).  The rows of a token block are one contiguous
+// range: the router reads one row per lane with 16-byte loads, the key
+// normaliser spreads each row over CK/8 (bf16) or CK/4 (fp32) lanes.
 template <int NMAX, int CK, typename TIn>
-__global__ __launch_bounds__(kTokBlock) void route_count_kernel(
+__global__ __launch_bounds__(256) void route_count_kernel(
     const TIn* __restrict__ z, const TIn* __restrict__ kl, const int32_t* __restrict__ cu, int H,
     int N, int K, int nblk, int32_t* __restrict__ idx, float* __restrict__ wout,
     int32_t* __restrict__ counts, float* __restrict__ lnz2) {
-    __shared__ int cnt[kMaxN];
-    const int h = blockIdx.x % H;
-    const int rest = blockIdx.x / H;
-    const int blk = rest % nblk, s = rest / nblk;
-    const int sh = s * H + h;
+    extern __shared__ int cnt[];  // [H][N]
+    const int blk = blockIdx.x, s = blockIdx.y;
     const int64_t t1 = cu[s + 1];
     const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
-    if (threadIdx.x < kMaxN) cnt[threadIdx.x] = 0;
+    const int64_t te = tb + kTokBlock < t1 ? tb + kTokBlock : t1;
+    const int64_t r0 = tb * H, r1 = te > tb ? te * H : r0;  // rows [r0, r1) (maybe none)
+    const int HN = H * N;
+    for (int i = threadIdx.x; i < HN; i += blockDim.x) cnt[i] = 0;
     __syncthreads();
-    const int64_t t = tb + threadIdx.x;
-    if (t < t1) {
-        int sel[kMaxTopK];
-        float w[kMaxTopK];
-        const int64_t row = t * H + h;
-        route_row<NMAX, TIn>(z + row * N, N, K, sel, w);
+    // kRB rows per thread and batch, loaded before any is routed
+    constexpr int kRB = 4;
+    for (int64_t rb = r0 + threadIdx.x; rb < r1; rb += (int64_t)kRB * blockDim.x) {
+        float zr[kRB][NMAX];
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; j++)
-            if (j < K) {
-                idx[row * K + j] = sel[j];
-                wout[row * K + j] = w[j];
-                atomicAdd(&cnt[sel[j]], 1);
+        for (int b = 0; b < kRB; b++) {
+            const int64_t r = rb + (int64_t)b * blockDim.x;
+            load_router_row<NMAX, TIn>(z + (r < r1 ? r : r0) * N, N, zr[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < kRB; b++) {
+            const int64_t r = rb + (int64_t)b * blockDim.x;
+            if (r >= r1) break;
+            const int h = (int)(r % H);
+            int sel[kMaxTopK];
+            float w[kMaxTopK];
+            route_row<NMAX>(zr[b], N, K, sel, w);
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; j++)
+                if (j < K) {
+                    idx[r * K + j] = sel[j];
+                    wout[r * K + j] = w[j];
+                    atomicAdd(&cnt[h * N + sel[j]], 1);
+                }
+        }
+    }
+    if (lnz2) {
+        constexpr int VPL = 16 / (int)sizeof(TIn);  // values per lane
+        constexpr int LPR = CK / VPL;                // lanes per row
+        constexpr int RPW = kWave / LPR;             // rows per wave and pass
+        const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+        const int nw = blockDim.x / kWave;
+        const int sub = lane % LPR, rr = lane / LPR;
+        // kB passes per batch: all their loads are issued before any of
+        // them is reduced, so the batch waits for memory once
+        constexpr int kB = 8;
+        const int64_t step = (int64_t)nw * RPW;
+        for (int64_t rb0 = r0 + (int64_t)wv * RPW; rb0 < r1; rb0 += kB * step) {
+        uint4 vb[kB];
+#pragma unroll
+        for (int b = 0; b < kB; b++) {
+            const int64_t r = rb0 + b * step + rr;
+            vb[b] = reinterpret_cast<const uint4*>(kl + (r < r1 ? r : r0) * CK)[sub];
+        }
+#pragma unroll
+        for (int b = 0; b < kB; b++) {
+            const int64_t r = rb0 + b * step + rr;
+            const bool ok = r < r1;
+            const uint4 v = vb[b];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            float x[VPL];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if constexpr (sizeof(TIn) == 2) {
+                    x[2 * e] = __uint_as_float(w4[e] << 16);
+                    x[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+                } else {
+                    x[e] = __uint_as_float(w4[e]);
+                }
             }
-        if (lnz2) {
-            float x[CK];
-            load_row<CK>(kl + row * CK, x);
             float m = x[0];
 #pragma unroll
-            for (int j = 1; j < CK; j++) m = fmaxf(m, x[j]);
+            for (int j = 1; j < VPL; j++) m = fmaxf(m, x[j]);
+            m = row_reduce<LPR>(m, [](float u, float v) { return fmaxf(u, v); });
             const float m2 = m * kLog2e;
             float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < CK; j++) sum += exp2f(fmaf(x[j], kLog2e, -m2));
-            lnz2[row] = m2 + log2f(sum);
+            for (int j = 0; j < VPL; j++) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
+            sum = row_reduce<LPR>(sum, [](float u, float v) { return u + v; });
+            if (ok && sub == 0) lnz2[r] = m2 + log2f(sum);
+        }
         }
     }
     __syncthreads();
-    if (counts && threadIdx.x < N)
-        counts[((int64_t)sh * N + threadIdx.x) * nblk + blk] = cnt[threadIdx.x];
+    if (counts)
+        for (int i = threadIdx.x; i < HN; i += blockDim.x) {
+            const int h = i / N, p = i % N;
+            counts[(((int64_t)s * H + h) * N + p) * nblk + blk] = cnt[i];
+        }
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and
@@ -204,23 +312,28 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
         seg_offsets[(int64_t)num_seqs * H * N] = (int32_t)(K * ((int64_t)H * cu[num_seqs]));
 }
 
-// Stable scatter of the records of one (sequence, head, token block).
+// Stable scatter of the records of one (sequence, head, token block): one
+// wave per 64-token block (a token block is exactly one wave, so a record's
+// rank among the block's records of its partition is a ballot popcount), four
+// token blocks per launch block.
 // When lnz2 is given, seg_cr[p] = lnz2[t, h] - log2(w) is stored too: the
 // exponent offset that turns 2^(kl log2 e - seg_cr) into w * kappa.
-__global__ __launch_bounds__(kTokBlock) void scatter_kernel(
+constexpr int kScatterWaves = 4;
+__global__ __launch_bounds__(kScatterWaves * kWave) void scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ win, const int32_t* __restrict__ cu,
     int H, int N, int K, int nblk, const int32_t* __restrict__ pos, int32_t* __restrict__ seg_tok,
     int32_t* __restrict__ seg_slot, float* __restrict__ seg_w, const float* __restrict__ lnz2,
     float* __restrict__ seg_cr) {
-    constexpr int NW = kTokBlock / kWave;
-    __shared__ int wcnt[NW][kMaxN];
-    const int sh = blockIdx.x, blk = blockIdx.y;
+    static_assert(kTokBlock == kWave, "one wave per token block");
+    const int sh = blockIdx.x;
+    const int blk = blockIdx.y * kScatterWaves + (int)(threadIdx.x / kWave);
+    if (blk >= nblk) return;  // wave-uniform
     const int s = sh / H, h = sh % H;
     const int64_t t1 = cu[s + 1];
     const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
-    if (tb >= t1) return;  // whole block past the sequence end (uniform)
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    const int64_t t = tb + threadIdx.x;
+    if (tb >= t1) return;  // wave-uniform
+    const int lane = threadIdx.x % kWave;
+    const int64_t t = tb + lane;
     const bool valid = t < t1;
     int sel[kMaxTopK];
     uint64_t mine = 0;
@@ -233,25 +346,21 @@ __global__ __launch_bounds__(kTokBlock) void scatter_kernel(
         }
     }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    int rank_in_wave[kMaxTopK];
+    int rank[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; j++) rank_in_wave[j] = 0;
+    for (int j = 0; j < kMaxTopK; j++) rank[j] = 0;
     for (int i = 0; i < N; i++) {
-        const uint64_t b = __ballot((mine >> i) & 1ull);
-        if (lane == 0) wcnt[wv][i] = __popcll(b);
+        const uint64_t bal = __ballot((mine >> i) & 1ull);
 #pragma unroll
         for (int j = 0; j < kMaxTopK; j++)
-            if (sel[j] == i) rank_in_wave[j] = __popcll(b & lt);
+            if (sel[j] == i) rank[j] = __popcll(bal & lt);
     }
-    __syncthreads();
     if (!valid) return;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; j++) {
         if (j < K) {
             const int i = sel[j];
-            int before = 0;
-            for (int w2 = 0; w2 < wv; w2++) before += wcnt[w2][i];
-            const int p = pos[((int64_t)sh * N + i) * nblk + blk] + before + rank_in_wave[j];
+            const int p = pos[((int64_t)sh * N + i) * nblk + blk] + rank[j];
             seg_tok[p] = (int32_t)t;
             if (seg_slot) seg_slot[p] = j;
             if (seg_w || seg_cr) {
@@ -292,12 +401,13 @@ template <int NMAX, typename TIn>
 static void launch_rc_n(dim3 grid, const TIn* z, const TIn* kl, const int32_t* cu, int H, int c,
                         int N, int K, int nblk, int32_t* idx, float* w, int32_t* counts,
                         float* lnz2, hipStream_t st) {
+    const size_t lds = sizeof(int) * (size_t)H * N;  // <= 64 KB for H <= 256, N <= 64
     if (c == 32)
-        route_count_kernel<NMAX, 32, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 32, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
     else if (c == 64)
-        route_count_kernel<NMAX, 64, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 64, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
     else
-        route_count_kernel<NMAX, 128, TIn><<<grid, kTokBlock, 0, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 128, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
 }
 
 template <typename TIn>
@@ -307,7 +417,8 @@ static hipError_t launch_route_count_t(const void* z, const void* kl, const int3
                                        hipStream_t st) {
     const int nblk = group_nblk(max_seqlen);
     if ((int64_t)num_seqs * H == 0) return hipSuccess;
-    dim3 grid((unsigned)((int64_t)num_seqs * nblk * H));
+    if (H > kMaxH) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nblk, (unsigned)num_seqs);
     const TIn* zz = static_cast<const TIn*>(z);
     const TIn* kk = static_cast<const TIn*>(kl);
     if (N <= 8)
@@ -369,8 +480,9 @@ hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, i
     block_scan_kernel<<<SH, 256, 0, st>>>(cu, H, N, K, nblk, counts, seg_offsets, num_seqs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    scatter_kernel<<<dim3(SH, nblk), kTokBlock, 0, st>>>(idx, w, cu, H, N, K, nblk, counts,
-                                                         seg_tok, seg_slot, seg_w, lnz2, seg_cr);
+    scatter_kernel<<<dim3(SH, (nblk + kScatterWaves - 1) / kScatterWaves), kScatterWaves * kWave,
+                     0, st>>>(idx, w, cu, H, N, K, nblk, counts, seg_tok, seg_slot, seg_w, lnz2,
+                              seg_cr);
     return hipGetLastError();
 }
 

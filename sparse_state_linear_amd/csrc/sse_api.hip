@@ -19,7 +19,7 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
     if (dtype != SSE_F32 && dtype != SSE_BF16) return SSE_ERR_INVALID_ARG;
     if (H < 1 || c < 1 || d < 1 || N < 1 || topk < 1 || topk > N) return SSE_ERR_INVALID_ARG;
     if (!supported_dim(c) || !supported_dim(d)) return SSE_ERR_UNSUPPORTED;
-    if (N > sse::kMaxN || topk > sse::kMaxTopK) return SSE_ERR_UNSUPPORTED;
+    if (N > sse::kMaxN || topk > sse::kMaxTopK || H > sse::kMaxH) return SSE_ERR_UNSUPPORTED;
     return SSE_OK;
 }
 
@@ -250,7 +250,7 @@ int sse_group_by_partition(const int32_t* topk_idx, const float* topk_w,
                            int32_t* seg_tok, int32_t* seg_slot, float* seg_w, void* workspace,
                            size_t workspace_bytes, void* stream) {
     if (H < 1 || N < 1 || topk < 1 || topk > N) return SSE_ERR_INVALID_ARG;
-    if (N > sse::kMaxN || topk > sse::kMaxTopK) return SSE_ERR_UNSUPPORTED;
+    if (N > sse::kMaxN || topk > sse::kMaxTopK || H > sse::kMaxH) return SSE_ERR_UNSUPPORTED;
     if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
     if (total_tokens > 0 && num_seqs == 0) return SSE_ERR_INVALID_ARG;
     if (!cu_seqlens || !seg_offsets) return SSE_ERR_INVALID_ARG;

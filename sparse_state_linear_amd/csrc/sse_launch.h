@@ -13,6 +13,7 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxN = 64;
 constexpr int kMaxTopK = 8;
+constexpr int kMaxH = 256;
 
 int group_nblk(int max_seqlen);
 
