@@ -104,9 +104,10 @@ size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_s
  *                             their router probabilities
  *   workspace                 device buffer of workspace_bytes >=
  *                             sse_forward_workspace_bytes(...)
- * o may not alias any input.  The shared partition's read is stored into o
- * first; the k routed reads are then added with fp32 atomics, so o may differ
- * between runs in the last bits.
+ * o may not alias any input.  Each routed read (e-gated) is stored into a
+ * workspace slot [total_tokens, H, topk, d]; the shared-partition pass then
+ * writes o = shared read + the topk slots of the token.  No atomics: o is the
+ * same, bit for bit, on every run.
  */
 int sse_forward(const void *q, const void *key_logits, const void *v, const void *log_alpha,
                 const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
@@ -172,8 +173,9 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  * every sse_forward records HIP events on its stream around its five
  * stages: 0 = routing + per-block counts + key-softmax normalisers,
  * 1 = grouping scan and scatter, 2 = local states of the pieces of long
- * shared chains, 3 = shared partition (stores o), 4 = routed partitions
- * (add into o).  Events of the last 256 calls are kept.  Tracing assumes
+ * shared chains, 3 = routed partitions (store their e-gated reads into the
+ * workspace slots), 4 = shared partition (writes o = shared read + slots).
+ * Events of the last 256 calls are kept.  Tracing assumes
  * one device per process.
  *   sse_trace_enable(1) creates the events (first time) and starts a fresh
  *   record; sse_trace_enable(0) stops recording.

@@ -61,6 +61,7 @@ struct Smem {
     uint16_t a[LV][C][TS];              // A terms [r][s]
     float ebc[CK];                      // exp(b_C) per state row
     uint32_t mrow[3][C];                // record row t*H + h (a real row even if padded)
+    uint32_t mout[3][C];                // output row: routed slot row or t*H + h
     float mcr[3][C];                    // exponent offset lnz2 - log2 w (+inf if padded)
     float mw[3][C];                     // read gate; -0.0 marks a padded record
 };
@@ -161,22 +162,26 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
     // loads carry no branch; threads < C store it after the next barrier.
     // Padded records keep a real row (so every address stays valid) and are
     // marked by a read gate of -0.0.
-    auto meta_load = [&](int64_t chunk, int& tok, float& cr, float& w) {
+    auto meta_load = [&](int64_t chunk, int& tok, float& cr, float& w, int& rank) {
         const int64_t idx = chunk * C + (tid % C);
         const int64_t ci = idx < n ? idx : (n > 0 ? n - 1 : 0);
         if constexpr (MODE == kModeRouted) {
             tok = a.seg_tok[lo + ci];
             cr = a.seg_cr[lo + ci];
             w = a.seg_w[lo + ci];
+            rank = a.seg_slot[lo + ci];
         } else {
             tok = (int)(lo + ci);
             cr = a.lnz2[((int64_t)tok) * H + h];
             w = 1.f;
+            rank = 0;
         }
     };
-    auto meta_store = [&](int64_t chunk, int buf, int tok, float cr, float w) {
+    auto meta_store = [&](int64_t chunk, int buf, int tok, float cr, float w, int rank) {
         const bool valid = chunk * C + tid < n;
-        sm.mrow[buf][tid] = (uint32_t)tok * (uint32_t)H + (uint32_t)h;
+        const uint32_t row = (uint32_t)tok * (uint32_t)H + (uint32_t)h;
+        sm.mrow[buf][tid] = row;
+        sm.mout[buf][tid] = MODE == kModeRouted ? row * (uint32_t)a.topk + (uint32_t)rank : row;
         sm.mcr[buf][tid] = valid ? cr : INFINITY;
         sm.mw[buf][tid] = valid ? w : -0.f;
     };
@@ -415,8 +420,8 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
             }
         }
     };
-    // o[token] (+)= w_r O[r], branch-free.  Routed: a padded record adds
-    // 0 * O to a real row.  Shared: a padded record's store goes to a dummy row.
+    // Routed: the record's slot row = w_r O[r].  Shared: o[token] = w_r O[r]
+    // + the token's routed slots.  A padded record's store goes to a dummy row.
     auto outputs = [&](int buf) {
         if constexpr (!kLocal) {
 #pragma unroll
@@ -424,20 +429,23 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++) {
                     const int rb = 32 * t2 + 8 * q4 + 4 * hh;
-                    const uint4 rw = *reinterpret_cast<const uint4*>(&sm.mrow[buf][rb]);
+                    const uint4 rw = *reinterpret_cast<const uint4*>(&sm.mout[buf][rb]);
                     const float4 wr = *reinterpret_cast<const float4*>(&sm.mw[buf][rb]);
                     const uint32_t rows[4] = {rw.x, rw.y, rw.z, rw.w};
                     const float ws[4] = {wr.x, wr.y, wr.z, wr.w};
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const float val = ws[e] * O[t2][4 * q4 + e];
+                        float val = ws[e] * O[t2][4 * q4 + e];
                         const uint32_t off = rows[e] * (uint32_t)(DV * 4) + col4;
+                        const bool valid = is_real(ws[e]);
                         if constexpr (MODE == kModeShared) {
-                            const bool valid = is_real(ws[e]);
+                            for (int j = 0; j < a.topk; j++)
+                                val += a.part[((int64_t)rows[e] * a.topk + j) * DV + col];
                             char* base = reinterpret_cast<char*>(valid ? a.o : a.trash);
                             *reinterpret_cast<float*>(base + (valid ? off : col4)) = val;
                         } else {
-                            atomic_add_f32(reinterpret_cast<float*>(reinterpret_cast<char*>(a.o) + off), val);
+                            char* base = reinterpret_cast<char*>(valid ? a.part : a.trash);
+                            *reinterpret_cast<float*>(base + (valid ? off : col4)) = val;
                         }
                     }
                 }
@@ -454,12 +462,12 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
     //   of n+1; barrier; causal A tiles; barrier; MFMA phase with the outputs
     //   of chunk n.
     if (nchunks > 0) {
-        int mt = 0;
+        int mt = 0, mrk = 0;
         float mc = 0.f, mwv = 0.f;
-        meta_load(0, mt, mc, mwv);
-        if (tid < C) meta_store(0, 0, mt, mc, mwv);
-        meta_load(1, mt, mc, mwv);
-        if (tid < C) meta_store(1, 1, mt, mc, mwv);
+        meta_load(0, mt, mc, mwv, mrk);
+        if (tid < C) meta_store(0, 0, mt, mc, mwv, mrk);
+        meta_load(1, mt, mc, mwv, mrk);
+        if (tid < C) meta_store(1, 1, mt, mc, mwv, mrk);
         lds_barrier();
         raw_load_qkl(0);
         raw_load_v(0);
@@ -468,11 +476,11 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
             const bool more = c + 1 < nchunks;  // uniform
             prep(cur);
             if (more) raw_load_qkl(nxt);  // q, k, log_alpha registers are free now
-            meta_load(c + 2, mt, mc, mwv);
+            meta_load(c + 2, mt, mc, mwv, mrk);
             lds_barrier();  // previous chunk's MFMA phase is done with the tiles
             prep_store();
             if (more) raw_load_v(nxt);    // v registers are free after the V^T store
-            if (tid < C) meta_store(c + 2, nn, mt, mc, mwv);
+            if (tid < C) meta_store(c + 2, nn, mt, mc, mwv, mrk);
             lds_barrier();
             if constexpr (!kLocal) {
                 a_tiles();

@@ -65,8 +65,12 @@ struct WsSmem {
     uint16_t a[2][kL][kWsC][kWsC + 8];  // A terms [r][s]
     float ebc[3][CK];                   // exp(b_C) per state row, ring by chunk % 3
     uint32_t mrow[kRing][kWsC];         // record row t*H + h (a real row even if padded)
+    uint32_t mout[kRing][kWsC];         // output row: slot row (t*H + h)*topk + rank
+                                        // (routed) or t*H + h (shared)
     float mcr[kRing][kWsC];             // lnz2 - log2 w (+inf if padded)
     float mw[kRing][kWsC];              // read gate; -0.0 marks a padded record
+    float xs[kCons][16][32];            // per consumer wave: half an output tile,
+                                        // transposed to whole-row 16-byte stores
 };
 
 // Storage column of the 4-column block starting at j (j % 4 == 0).
@@ -80,7 +84,7 @@ __device__ __forceinline__ int swz(int row, int s) {
 }
 
 struct Meta {
-    int tok;
+    int tok, slot;
     float cr, w;
 };
 
@@ -191,10 +195,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         const int64_t ci = idx < n ? idx : n - 1;
         if constexpr (MODE == kModeRouted) {
             m.tok = a.seg_tok[lo + ci];
+            m.slot = a.seg_slot[lo + ci];
             m.cr = a.seg_cr[lo + ci];
             m.w = a.seg_w[lo + ci];
         } else {
             m.tok = (int)(lo + ci);
+            m.slot = 0;
             m.cr = a.lnz2[((int64_t)m.tok) * H + h];
             m.w = 1.f;
         }
@@ -203,7 +209,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         if (lane < kWsC) {
             const int slot = (int)(chunk % kRing);
             const bool valid = chunk * kWsC + lane < n;
-            sm.mrow[slot][lane] = (uint32_t)m.tok * (uint32_t)H + (uint32_t)h;
+            const uint32_t row = (uint32_t)m.tok * (uint32_t)H + (uint32_t)h;
+            sm.mrow[slot][lane] = row;
+            sm.mout[slot][lane] =
+                MODE == kModeRouted ? row * (uint32_t)a.topk + (uint32_t)m.slot : row;
             sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
             sm.mw[slot][lane] = valid ? m.w : -0.f;
         }
@@ -239,18 +248,27 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             gcr[i] = sm.mcr[slot][r0 + i];
         }
     };
-    auto raw_load = [&](Raw& R) {
-        // byte offsets fit in 32 bits (checked on the host)
+    // part 0: log_alpha, 1: key logits, 2: q, 3: v.  Byte offsets fit in 32
+    // bits (checked on the host).
+    auto raw_load_part = [&](Raw& R, int part) {
+        if (part == 3) {
+#pragma unroll
+            for (int i = 0; i < RPGV; i++)
+                R.v[i].load(gv, rowv[i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
             const uint32_t off = rowq[i] * (uint32_t)(CK * 2) + (uint32_t)(j0 * 2);
-            if constexpr (!kLocal) R.q[i].load(gq, off);
-            R.k[i].load(gk, off);
-            R.l[i].load(gl, off);
+            if (part == 0) R.l[i].load(gl, off);
+            if (part == 1) R.k[i].load(gk, off);
+            if constexpr (!kLocal)
+                if (part == 2) R.q[i].load(gq, off);
         }
+    };
+    auto raw_load = [&](Raw& R) {
 #pragma unroll
-        for (int i = 0; i < RPGV; i++)
-            R.v[i].load(gv, rowv[i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+        for (int part = 0; part < 4; part++) raw_load_part(R, part);
     };
 
     // Inclusive scan of x over the record groups of this lane's column group
@@ -305,8 +323,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 
     // ---------------- producer: preparation of one chunk ----------------
     float btot[kPC] = {0.f, 0.f, 0.f, 0.f};
-    auto prep = [&](int64_t chunk, const Raw& R) {
+    // hook(k), k = 0..3, is called at four points spread over the
+    // preparation, so the next chunk's row loads issue between its phases
+    // instead of in one burst after the barrier
+    auto prep = [&](int64_t chunk, const Raw& R, auto&& hook) {
         auto& st = sm.st[chunk & 1];
+        hook(0);
         float run[kPC] = {0.f, 0.f, 0.f, 0.f};
         float bb[RPG][kPC];
 #pragma unroll
@@ -319,6 +341,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                 bb[i][e] = run[e];
             }
         }
+        hook(1);
         float excl[kPC], ebc_own[kPC];
 #pragma unroll
         for (int e = 0; e < kPC; e++) {
@@ -328,6 +351,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             ebc_own[e] = __builtin_amdgcn_exp2f(tot);
             if constexpr (kLocal) btot[e] += tot;
         }
+        hook(2);
         uint2 pk[RPG][kL];
         const int jp = perm_col(j0);
 #pragma unroll
@@ -351,6 +375,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                 }
             }
         }
+        hook(3);
         // Kh^T: the lane's RPG records of each of its 4 columns
 #pragma unroll
         for (int e = 0; e < kPC; e++)
@@ -437,28 +462,69 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         }
     };
 
-    // outputs of the finished chunk: o[token] (+)= w_r Op[r], branch-free.
-    // Routed: a padded record adds 0 * O to a real row.  Shared: a padded
-    // record's store goes to the dummy row.
-    auto outputs = [&](const f32x16& Op, const uint4 (&mr)[4], const float4 (&mw4)[4]) {
+    // Outputs of a finished chunk.  The wave's 32 x 32 tile (lane = column,
+    // 16 rows in registers) is scaled by the read gates and transposed
+    // through LDS, 16 rows at a time, so that each lane holds 4 consecutive
+    // columns of one record: tv[p][h2] is record 16 p + 8 h2 + lane / 8,
+    // columns 32 wv + 4 (lane % 8) .. +3, and one 16-byte store per value
+    // writes whole 128-byte row segments.
+    const int trow = lane / 8, tcol = 32 * wv + 4 * (lane % 8);
+    // half p (records 16 p .. 16 p + 15) of the transpose
+    auto transpose_half = [&](int p, const f32x16& Op, const float4 (&mw4)[4], float4 (&th)[2]) {
+        float* xs = &sm.xs[wv][0][0];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            const uint32_t rows[4] = {mr[q4].x, mr[q4].y, mr[q4].z, mr[q4].w};
-            const float ws[4] = {mw4[q4].x, mw4[q4].y, mw4[q4].z, mw4[q4].w};
+        for (int i = 8 * p; i < 8 * p + 8; i++) {
+            const float4 g = mw4[i / 4];
+            const float wr = (i % 4 == 0) ? g.x : (i % 4 == 1) ? g.y : (i % 4 == 2) ? g.z : g.w;
+            const int r = 8 * (i / 4) + 4 * hh + (i % 4) - 16 * p;
+            xs[r * 32 + l32] = wr * Op[i];
+        }
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float val = ws[e] * Op[4 * q4 + e];
-                const uint32_t off = rows[e] * (uint32_t)(DV * 4) + col4;
-                if constexpr (MODE == kModeShared) {
-                    const bool valid = is_real(ws[e]);
-                    char* base = reinterpret_cast<char*>(valid ? a.o : a.trash);
-                    *reinterpret_cast<float*>(base + (valid ? off : col4)) = val;
-                } else {
-                    atomic_add_f32(reinterpret_cast<float*>(reinterpret_cast<char*>(a.o) + off), val);
-                }
+        for (int h2 = 0; h2 < 2; h2++)
+            th[h2] = *reinterpret_cast<const float4*>(&xs[(8 * h2 + trow) * 32 + 4 * (lane % 8)]);
+    };
+    auto transpose = [&](const f32x16& Op, const float4 (&mw4)[4], float4 (&tv)[2][2]) {
+        float* xs = &sm.xs[wv][0][0];
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+#pragma unroll
+            for (int i = 8 * p; i < 8 * p + 8; i++) {
+                const float4 g = mw4[i / 4];
+                const float wr = (i % 4 == 0) ? g.x : (i % 4 == 1) ? g.y : (i % 4 == 2) ? g.z : g.w;
+                const int r = 8 * (i / 4) + 4 * hh + (i % 4) - 16 * p;
+                xs[r * 32 + l32] = wr * Op[i];
             }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+                tv[p][h2] = *reinterpret_cast<const float4*>(&xs[(8 * h2 + trow) * 32 + 4 * (lane % 8)]);
         }
     };
+    // output row and gate of the records this lane stores
+    auto out_rows = [&](int64_t chunk, uint32_t (&orow)[2][2], bool (&oval)[2][2]) {
+        const int slot = (int)(chunk % kRing);
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) {
+                const int r = 16 * p + 8 * h2 + trow;
+                orow[p][h2] = sm.mout[slot][r];
+                oval[p][h2] = is_real(sm.mw[slot][r]);
+            }
+    };
+    // 16-byte store of one value to its row (routed: the record's slot row;
+    // shared: o), or to the dummy row for a padded record
+    auto store_out = [&](float* dst, uint32_t orow, bool valid, const float4& v) {
+        const uint32_t off = orow * (uint32_t)(DV * 4) + (uint32_t)(tcol * 4);
+        char* base = reinterpret_cast<char*>(valid ? dst : a.trash);
+        *reinterpret_cast<float4*>(base + (valid ? off : (uint32_t)(tcol * 4))) = v;
+    };
+    // slot rows of record row `orow` (shared pass): [row][topk][d]
+    auto slot_ld = [&](uint32_t orow, int j) {
+        const uint32_t off = (orow * (uint32_t)a.topk + (uint32_t)j) * (uint32_t)(DV * 4) +
+                             (uint32_t)(tcol * 4);
+        return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(a.part) + off);
+    };
+    constexpr int kPre = 2;  // slots per record prefetched before the shared outputs
     auto decay = [&](f32x16& Srt, const float4 (&e4)[4]) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
@@ -479,20 +545,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         constexpr bool CUR = decltype(curI)::value;
         const auto& st = sm.st[nn & 1];
         u16x8 ob[3][4];
-        uint4 mr[4];
         float4 mw4[4];
+        uint32_t orow[2][2];
+        bool oval[2][2];
+        float4 tv[2][2];
+        float4 pre[2][2][kPre];
         f32x4 Aacc = {0.f, 0.f, 0.f, 0.f};
         auto fetch_extra = [&](auto sI) {
             constexpr int s = decltype(sI)::value;
             if (!col_wave) return;
-            if constexpr (s == sF && PREV) {
-                const int slot = (int)((nn - 1) % kRing);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; q4++) {
-                    mr[q4] = *reinterpret_cast<const uint4*>(&sm.mrow[slot][8 * q4 + 4 * hh]);
-                    mw4[q4] = *reinterpret_cast<const float4*>(&sm.mw[slot][8 * q4 + 4 * hh]);
-                }
-            }
+            // the shared pass needs the output rows early, for its slot loads
+            if constexpr (s == sF && PREV && MODE == kModeShared) out_rows(nn - 1, orow, oval);
             if constexpr (CUR && s == (kLocal ? sU : sR)) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) Vc[ks] = lds8(&st.vt[col][swz(col, 16 * ks + 8 * hh)]);
@@ -555,10 +618,68 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             }
         };
         // work that waits for an earlier step's MFMA results
+        // shared pass: o = shared read + the record's routed slots
+        auto shared_store = [&]() {
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    float4 v = tv[p][h2];
+#pragma unroll
+                    for (int j = 0; j < kPre; j++)
+                        if (j < a.topk) {
+                            v.x += pre[p][h2][j].x;
+                            v.y += pre[p][h2][j].y;
+                            v.z += pre[p][h2][j].z;
+                            v.w += pre[p][h2][j].w;
+                        }
+                    for (int j = kPre; j < a.topk; j++) {
+                        const float4 u = slot_ld(orow[p][h2], j);
+                        v.x += u.x;
+                        v.y += u.y;
+                        v.z += u.z;
+                        v.w += u.w;
+                    }
+                    store_out(a.o, orow[p][h2], oval[p][h2], v);
+                }
+        };
         auto after = [&](auto sI) {
             constexpr int s = decltype(sI)::value;
-            if constexpr (PREV && s == (CUR ? sOut : sF))
-                if (col_wave) outputs(Op, mr, mw4);
+            if constexpr (PREV && MODE == kModeShared && s == sF) {
+                // the first kPre slots of the finished records, consumed at
+                // the end of the iteration
+                if (col_wave)
+#pragma unroll
+                    for (int p = 0; p < 2; p++)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                            for (int j = 0; j < kPre; j++)
+                                pre[p][h2][j] = slot_ld(orow[p][h2], j < a.topk ? j : 0);
+            }
+            if constexpr (PREV && s == (CUR ? sOut : sF)) {
+                if (col_wave) {
+                    const int slot = (int)((nn - 1) % kRing);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; q4++)
+                        mw4[q4] = *reinterpret_cast<const float4*>(&sm.mw[slot][8 * q4 + 4 * hh]);
+                    if constexpr (MODE == kModeRouted) {
+                        out_rows(nn - 1, orow, oval);
+#pragma unroll
+                        for (int p = 0; p < 2; p++) {
+                            float4 th[2];
+                            transpose_half(p, Op, mw4, th);
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; h2++) store_out(a.part, orow[p][h2], oval[p][h2], th[h2]);
+                        }
+                    } else {
+                        transpose(Op, mw4, tv);
+                        if constexpr (!CUR) shared_store();
+                    }
+                }
+            }
+            if constexpr (PREV && CUR && MODE == kModeShared && s == sEnd - 1)
+                if (col_wave) shared_store();
             if constexpr (CUR && !kLocal && s == sR) {
                 // causal mask, bf16 terms, store of this wave's A tile
                 const int r = 16 * rT + l16, s0 = 16 * sT + 4 * g16;
@@ -623,22 +744,29 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             raw_load(R2);
             read_rows(3);
             read_gates(0);
-            prep(0, R0);
+            prep(0, R0, [](int) {});
             read_gates(1);
             lds_barrier();
             // Step nn: issue the metadata loads of chunk nn+6 (first: the
             // counter of outstanding loads is in order, so waiting for them
-            // next step must not also wait for this step's row loads), the
-            // row loads of chunk nn+3 (rows read last step; chunk c's rows
-            // live in R[c % 3], so every load has two steps to arrive), read
-            // the rows of chunk nn+4, prepare chunk nn+1 (gates read last
-            // step), read the gates of chunk nn+2, store the metadata of chunk
-            // nn+5.
+            // next step must not also wait for this step's row loads);
+            // prepare chunk nn+1 (gates read last step) while issuing the row
+            // loads of chunk nn+3 between its phases (rows read last step;
+            // chunk c's rows live in R[c % 3], so every load has two steps to
+            // arrive); read the rows of chunk nn+4 and the gates of chunk
+            // nn+2; store the metadata of chunk nn+5.
             auto step = [&](int64_t nn, Raw& Rl, const Raw& Rp, Meta& Ml, const Meta& Ms) {
                 meta_load(nn + 6, Ml);
-                raw_load(Rl);
+                auto hook = [&](int part) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    raw_load_part(Rl, part);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                if (nn + 1 < nchunks)
+                    prep(nn + 1, Rp, hook);
+                else
+                    raw_load(Rl);
                 read_rows(nn + 4);
-                if (nn + 1 < nchunks) prep(nn + 1, Rp);
                 read_gates(nn + 2);
                 if (pw == 0) meta_store(nn + 5, Ms);
                 lds_barrier();

@@ -24,7 +24,8 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
 }
 
 struct FwdLayout {
-    size_t idx, w, counts, seg_off, seg_tok, seg_w, seg_cr, lnz2, agg_S, agg_D, trash, total;
+    size_t idx, w, counts, seg_off, seg_tok, seg_w, seg_cr, seg_slot, lnz2, agg_S, agg_D, trash,
+        part, total;
 };
 
 // Workspace carving.  c, d = 0 sizes the grouping part only.  Returns false
@@ -50,10 +51,12 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     L.seg_tok = off; off += align_up(sizeof(int32_t) * (size_t)recs);
     L.seg_w = off;   off += align_up(sizeof(float) * (size_t)recs);
     L.seg_cr = off;  off += align_up(sizeof(float) * (size_t)recs);
+    L.seg_slot = off; off += align_up(sizeof(int32_t) * (size_t)recs);
     L.lnz2 = off;    off += align_up(sizeof(float) * (size_t)(T * H));
     L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
     L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
     L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? d : 1));
+    L.part = off;    off += align_up(sizeof(float) * (size_t)recs * (size_t)d);
     L.total = off;
     return true;
 }
@@ -115,8 +118,10 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     FwdLayout L;
     if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L))
         return SSE_ERR_UNSUPPORTED;
-    // byte offsets of token rows must fit in 32 bits (fp32 worst case)
+    // byte offsets of token rows (fp32 worst case) and of the routed slots
+    // [T, H, topk, d] fp32 must fit in 32 bits
     if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
+    if (total_tokens * H * topk * d >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -129,6 +134,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     float* seg_w = reinterpret_cast<float*>(ws + L.seg_w);
     float* seg_cr = reinterpret_cast<float*>(ws + L.seg_cr);
     float* lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
+    int32_t* seg_slot = reinterpret_cast<int32_t*>(ws + L.seg_slot);
 
     // 1. router + per-block counts + key-softmax normaliser
     trace_mark(0, s);
@@ -138,7 +144,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     // 2. grouping into (sequence, head, partition) segments
     trace_mark(1, s);
     e = sse::launch_group(idx, w, cu_seqlens, num_seqs, max_seqlen, H, N, topk, true, counts,
-                          seg_off, seg_tok, nullptr, seg_w, lnz2, seg_cr, s);
+                          seg_off, seg_tok, seg_slot, seg_w, lnz2, seg_cr, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(2, s);
     sse::ChunkArgs a;
@@ -151,6 +157,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.seg_tok = seg_tok;
     a.seg_w = seg_w;
     a.seg_cr = seg_cr;
+    a.seg_slot = seg_slot;
     a.lnz2 = lnz2;
     a.init = initial_states;
     a.o = o;
@@ -158,21 +165,23 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.agg_S = reinterpret_cast<float*>(ws + L.agg_S);
     a.agg_D = reinterpret_cast<float*>(ws + L.agg_D);
     a.trash = reinterpret_cast<float*>(ws + L.trash);
+    a.part = reinterpret_cast<float*>(ws + L.part);
     a.num_seqs = num_seqs;
     a.H = H;
     a.N = N;
+    a.topk = topk;
     a.piece_len = sse::chunk_piece_len(dtype);
     a.max_pieces = sse::chunk_max_pieces(max_seqlen, dtype);
     // 3. local states of the shared pieces (all but the last of a sequence)
     e = sse::launch_chunk_local(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(3, s);
-    // 4. shared partition: stores o
-    e = sse::launch_chunk_shared(a, dtype, c, d, s);
+    // 4. routed partitions: e-gated reads into the workspace slots
+    e = sse::launch_chunk_routed(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(4, s);
-    // 5. routed partitions: add into o
-    e = sse::launch_chunk_routed(a, dtype, c, d, s);
+    // 5. shared partition: o = shared read + the token's routed slots
+    e = sse::launch_chunk_shared(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(5, s);
     if (g_trace.on) g_trace.calls++;

@@ -41,6 +41,7 @@ struct ChunkArgs {
     const int32_t* seg_tok;
     const float* seg_w;
     const float* seg_cr;
+    const int32_t* seg_slot;     // rank of each routed record in its token's top-k
     const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
     const float* init;           // [S, H, N+1, c, d] or null
     float* o;
@@ -48,7 +49,9 @@ struct ChunkArgs {
     float* agg_S;                // [S*H, max_pieces, c, d] local piece states
     float* agg_D;                // [S*H, max_pieces, c] piece decay products
     float* trash;                // one dummy output row for padded records
-    int num_seqs, H, N;
+    float* part;                 // [T, H, topk, d] e-gated routed reads (routed
+                                 // pass writes, shared pass adds into o)
+    int num_seqs, H, N, topk;
     int piece_len;               // records per shared piece
     int max_pieces;
 };
