@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         float bb[RPG][kPC];
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const bool valid = is_real(gw[i]);
+            const bool valid = is_real(gw[i]);  // padded records' log decay must not count
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
                 const float x = valid ? R.l[i].get(e) : 0.f;
@@ -376,23 +376,41 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             }
         }
         hook(3);
-        // Kh^T: the lane's RPG records of each of its 4 columns
+        // Kh^T and V^T: the lane's records of each of its 4 columns, two
+        // records per 32-bit word (one byte permutation per word)
+        auto pair = [](uint32_t w_lo, uint32_t w_hi, int e) {
+            // 16-bit element e%2 of w_lo and of w_hi -> low / high half
+            return __builtin_amdgcn_perm(w_hi, w_lo, (e & 1) ? 0x07060302u : 0x05040100u);
+        };
 #pragma unroll
         for (int e = 0; e < kPC; e++)
 #pragma unroll
             for (int l = 0; l < kL; l++) {
-                uint16_t rr[RPG];
+                if constexpr (RPG == 4) {
+                    const uint32_t w0 = (e < 2) ? pk[0][l].x : pk[0][l].y, w1 = (e < 2) ? pk[1][l].x : pk[1][l].y;
+                    const uint32_t w2 = (e < 2) ? pk[2][l].x : pk[2][l].y, w3 = (e < 2) ? pk[3][l].x : pk[3][l].y;
+                    *reinterpret_cast<uint2*>(&st.kt[l][j0 + e][swz(j0 + e, r0)]) =
+                        make_uint2(pair(w0, w1, e), pair(w2, w3, e));
+                } else {
+                    uint16_t rr[RPG];
 #pragma unroll
-                for (int i = 0; i < RPG; i++) rr[i] = elem(pk[i][l], e);
-                store_run<RPG>(&st.kt[l][j0 + e][swz(j0 + e, r0)], rr);
+                    for (int i = 0; i < RPG; i++) rr[i] = elem(pk[i][l], e);
+                    store_run<RPG>(&st.kt[l][j0 + e][swz(j0 + e, r0)], rr);
+                }
             }
-        // V^T
 #pragma unroll
         for (int e = 0; e < kPC; e++) {
-            uint16_t rr[RPGV];
+            if constexpr (RPGV == 4) {
+                const uint32_t w0 = (e < 2) ? R.v[0].u.x : R.v[0].u.y, w1 = (e < 2) ? R.v[1].u.x : R.v[1].u.y;
+                const uint32_t w2 = (e < 2) ? R.v[2].u.x : R.v[2].u.y, w3 = (e < 2) ? R.v[3].u.x : R.v[3].u.y;
+                *reinterpret_cast<uint2*>(&st.vt[c0v + e][swz(c0v + e, r0v)]) =
+                    make_uint2(pair(w0, w1, e), pair(w2, w3, e));
+            } else {
+                uint16_t rr[RPGV];
 #pragma unroll
-            for (int i = 0; i < RPGV; i++) rr[i] = R.v[i].bits(e);
-            store_run<RPGV>(&st.vt[c0v + e][swz(c0v + e, r0v)], rr);
+                for (int i = 0; i < RPGV; i++) rr[i] = R.v[i].bits(e);
+                store_run<RPGV>(&st.vt[c0v + e][swz(c0v + e, r0v)], rr);
+            }
         }
         if (gk_ == 0)
 #pragma unroll
