@@ -571,7 +571,9 @@ int chunk_max_pieces(int max_seqlen, int dtype) {
 }
 
 hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
-    if (a.max_pieces <= 1) return hipSuccess;
+    // fp32: nothing to do without a second piece; bf16: the pass also
+    // computes every token's key-softmax normaliser, so it always runs
+    if (dtype == kF32 && a.max_pieces <= 1) return hipSuccess;
     return launch_mode<kModeLocal>(a, dtype, c, d, st);
 }
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         piece = blockIdx.y;
         const int64_t t0 = a.cu[s], len = a.cu[s + 1] - t0;
         npieces = len > 0 ? (int)((len + a.piece_len - 1) / a.piece_len) : 1;
-        if (piece >= npieces - (kLocal ? 1 : 0)) return;  // uniform
+        if (piece >= npieces) return;  // uniform
         lo = t0 + (int64_t)piece * a.piece_len;
         n = min<int64_t>(a.piece_len, len - (int64_t)piece * a.piece_len);
         if (n < 0) n = 0;
@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         } else {
             m.tok = (int)(lo + ci);
             m.slot = 0;
-            m.cr = a.lnz2[((int64_t)m.tok) * H + h];
+            // the local-state pass computes the normaliser itself (below)
+            m.cr = kLocal ? 0.f : a.lnz2[((int64_t)m.tok) * H + h];
             m.w = 1.f;
         }
     };
@@ -213,11 +214,85 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             sm.mrow[slot][lane] = row;
             sm.mout[slot][lane] =
                 MODE == kModeRouted ? row * (uint32_t)a.topk + (uint32_t)m.slot : row;
-            sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
+            if constexpr (!kLocal) sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
             sm.mw[slot][lane] = valid ? m.w : -0.f;
         }
     };
     auto is_real = [](float w) { return (__float_as_uint(w) >> 31) == 0u; };
+
+    // ---------------- local pass: key-softmax normalisers ----------------
+    // In the local-state pass (the first pass over every token) the consumer
+    // waves compute lnz2 = log2 of the key-softmax denominator of every
+    // record (max-shifted: m log2 e + log2 sum_j 2^((kl_j - m) log2 e), so
+    // kappa_j = 2^(kl_j log2 e - lnz2)), three chunks before the producers
+    // prepare that chunk: into the metadata ring for this pass and into
+    // lnz2_out for the later passes.  Consumer wave ws takes records
+    // 8 ws .. 8 ws + 7 of a chunk, CK/8 lanes per record (16-byte loads).
+    constexpr int kLPR = CK / 8;                         // lanes per record
+    constexpr int kRPI = kWave / kLPR;                   // records per load
+    constexpr int kRecW = kWsC / kCons;                  // records per wave and chunk
+    constexpr int kNKl = (kRecW + kRPI - 1) / kRPI;      // loads per wave and chunk
+    struct KlRaw {
+        uint4 v[kNKl];
+    };
+    const int ksub = lane % kLPR;
+    auto kl_load = [&](int64_t chunk, int ws, KlRaw& K) {
+#pragma unroll
+        for (int i = 0; i < kNKl; i++) {
+            const int rr = min(lane / kLPR + kRPI * i, kRecW - 1);
+            const int64_t idx = chunk * kWsC + ws * kRecW + rr;
+            const int64_t ci = idx < n ? idx : n - 1;  // a valid row (n >= 1)
+            const uint32_t off =
+                ((uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h) * (uint32_t)(CK * 2) + (uint32_t)(ksub * 16);
+            K.v[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(gk) + off);
+        }
+    };
+    auto kl_norm = [&](int64_t chunk, int ws, const KlRaw& K, bool to_ring) {
+#pragma unroll
+        for (int i = 0; i < kNKl; i++) {
+            const uint32_t w4[4] = {K.v[i].x, K.v[i].y, K.v[i].z, K.v[i].w};
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                x[2 * e] = __uint_as_float(w4[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+            }
+            float m = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; j++) m = fmaxf(m, x[j]);
+            m = row_reduce<kLPR>(m, [](float u, float v) { return fmaxf(u, v); });
+            const float m2 = m * kLog2e;
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
+            sum = row_reduce<kLPR>(sum, [](float u, float v) { return u + v; });
+            const float l2 = m2 + __builtin_amdgcn_logf(sum);  // sum >= 1
+            const int rr = lane / kLPR + kRPI * i;
+            if (ksub == 0 && rr < kRecW) {
+                const int r = ws * kRecW + rr;
+                const int64_t idx = chunk * kWsC + r;
+                const bool valid = idx < n;
+                if (to_ring) sm.mcr[chunk % kRing][r] = valid ? l2 : INFINITY;
+                if (valid) a.lnz2_out[(lo + idx) * H + h] = l2;
+            }
+        }
+    };
+    if constexpr (kLocal) {
+        if (last_piece) {
+            // the last piece's local state is never used: only its
+            // normalisers are needed (all eight waves, four chunks per batch)
+            const int ws = wv % kCons;
+            for (int64_t c0 = wv / kCons; c0 < nchunks; c0 += 8) {
+                KlRaw K[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) kl_load(c0 + 2 * u, ws, K[u]);
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (c0 + 2 * u < nchunks) kl_norm(c0 + 2 * u, ws, K[u], false);
+            }
+            return;
+        }
+    }
 
     // ---------------- producer: row loads ----------------
     // lane = (group cg of 4 columns, group gk of RPG consecutive records)
@@ -557,11 +632,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     // the readout of chunk nn-1 and Vp its V operand; Oc and Vc receive those
     // of chunk nn.
     auto iteration = [&](auto prevI, auto curI, int64_t nn, f32x16& Op, u16x8(&Vp)[2], f32x16& Oc,
-                         u16x8(&Vc)[2]) {
+                         u16x8(&Vc)[2], KlRaw& Kl, const KlRaw& Kn) {
         constexpr bool HASPREV = decltype(prevI)::value;   // S holds chunk nn-1 undecayed
         constexpr bool PREV = HASPREV && !kLocal;
         constexpr bool CUR = decltype(curI)::value;
         const auto& st = sm.st[nn & 1];
+        if constexpr (kLocal) {
+            // key normalisers: load chunk nn+4, finish chunk nn+3 (loaded
+            // one iteration ago)
+            kl_load(nn + 4, wv, Kl);
+            kl_norm(nn + 3, wv, Kn, true);
+        }
         u16x8 ob[3][4];
         float4 mw4[4];
         uint32_t orow[2][2];
@@ -798,6 +879,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             if (nn <= nchunks) step(nn, R0, R1, M0, M2);
             if (nn + 1 <= nchunks) step(nn + 1, R1, R2, M1, M0);
         } else {
+            // local pass: the normalisers of chunks 0 and 1 are in the ring
+            // before the producers' first read of it (after the first
+            // barrier), chunk 2's before the second; chunk 3 is loaded
+            KlRaw K0, K1;
+            if constexpr (kLocal) {
+                kl_load(0, wv, K0);
+                kl_load(1, wv, K1);
+                kl_norm(0, wv, K0, true);
+                kl_norm(1, wv, K1, true);
+            }
             if (!kLocal && wv == 3) {
                 // the zero (r-tile 0, s-tile 1) block of A in both buffers
                 for (int i = lane; i < 2 * kL * 16; i += kWave) {
@@ -807,6 +898,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                 }
             }
             lds_barrier();
+            if constexpr (kLocal) {
+                kl_load(2, wv, K0);
+                kl_load(3, wv, K1);
+                kl_norm(2, wv, K0, true);
+            }
             lds_barrier();
             // iteration 0 runs chunk 0; iterations 1 .. nchunks-1 finish the
             // previous chunk and run the next (unrolled by two so the readout
@@ -816,21 +912,23 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             using F_ = std::false_type;
             f32x16 O0, O1;
             u16x8 V0[2], V1[2];
-            iteration(F_{}, T_{}, 0, O1, V1, O0, V0);
+            // (iteration nn loads normaliser rows into K[nn % 2] and finishes
+            // the chunk held in K[(nn + 1) % 2])
+            iteration(F_{}, T_{}, 0, O1, V1, O0, V0, K0, K1);
             lds_barrier();
             int64_t nn = 1;
             for (; nn + 1 < nchunks; nn += 2) {
-                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1, K1, K0);
                 lds_barrier();
-                iteration(T_{}, T_{}, nn + 1, O1, V1, O0, V0);
+                iteration(T_{}, T_{}, nn + 1, O1, V1, O0, V0, K0, K1);
                 lds_barrier();
             }
             if (nn < nchunks) {
-                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1, K1, K0);
                 lds_barrier();
-                iteration(T_{}, F_{}, nn + 1, O1, V1, O0, V0);
+                iteration(T_{}, F_{}, nn + 1, O1, V1, O0, V0, K0, K1);
             } else {
-                iteration(T_{}, F_{}, nn, O0, V0, O1, V1);
+                iteration(T_{}, F_{}, nn, O0, V0, O1, V1, K1, K0);
             }
             lds_barrier();
         }
@@ -880,8 +978,7 @@ void launch_ws_cfg(const ChunkArgs& a, hipStream_t st) {
     if (MODE == kModeRouted)
         grid = dim3((unsigned)(a.num_seqs * a.H * a.N));
     else
-        grid = dim3((unsigned)(a.num_seqs * a.H),
-                    (unsigned)(MODE == kModeLocal ? a.max_pieces - 1 : a.max_pieces));
+        grid = dim3((unsigned)(a.num_seqs * a.H), (unsigned)a.max_pieces);
     if (grid.x == 0 || grid.y == 0) return;
     chunk_ws_kernel<CK, DV, MODE><<<grid, kWsThreads, 0, st>>>(a);
 }

@@ -137,27 +137,6 @@ __device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
     }
 }
 
-// Reduce x over groups of L consecutive lanes (every lane gets the result).
-// A 16-lane group is one DPP row: four row rotations, no LDS traffic.
-template <int L, typename Op>
-__device__ __forceinline__ float row_reduce(float x, Op op) {
-    if constexpr (L == 16) {
-        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false)));
-        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false)));
-        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false)));
-        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false)));
-        return x;
-    } else {
-#pragma unroll
-        for (int o = L / 2; o >= 1; o >>= 1) x = op(x, __shfl_xor(x, o, kWave));
-        return x;
-    }
-}
-
 // Route the rows of one (sequence, 64-token block) for all heads, count the
 // records per (head, partition) in LDS (cnt, H x N ints of dynamic shared
 // memory), and store lnz2 = log2 of the key-softmax denominator

@@ -136,17 +136,6 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     float* lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
     int32_t* seg_slot = reinterpret_cast<int32_t*>(ws + L.seg_slot);
 
-    // 1. router + per-block counts + key-softmax normaliser
-    trace_mark(0, s);
-    hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
-                                           max_seqlen, H, c, N, topk, idx, w, counts, lnz2, s);
-    if (e != hipSuccess) return SSE_ERR_HIP;
-    // 2. grouping into (sequence, head, partition) segments
-    trace_mark(1, s);
-    e = sse::launch_group(idx, w, cu_seqlens, num_seqs, max_seqlen, H, N, topk, true, counts,
-                          seg_off, seg_tok, seg_slot, seg_w, lnz2, seg_cr, s);
-    if (e != hipSuccess) return SSE_ERR_HIP;
-    trace_mark(2, s);
     sse::ChunkArgs a;
     a.q = q;
     a.kl = key_logits;
@@ -159,6 +148,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.seg_cr = seg_cr;
     a.seg_slot = seg_slot;
     a.lnz2 = lnz2;
+    a.lnz2_out = lnz2;
     a.init = initial_states;
     a.o = o;
     a.final_states = final_states;
@@ -172,8 +162,22 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.topk = topk;
     a.piece_len = sse::chunk_piece_len(dtype);
     a.max_pieces = sse::chunk_max_pieces(max_seqlen, dtype);
-    // 3. local states of the shared pieces (all but the last of a sequence)
+
+    // 1. router + per-block counts (+ the key-softmax normaliser for fp32
+    //    inputs; for bf16 inputs the local-state pass computes it)
+    trace_mark(0, s);
+    hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
+                                           max_seqlen, H, c, N, topk, idx, w, counts,
+                                           dtype == SSE_F32 ? lnz2 : nullptr, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    // 2. local states of the shared pieces
+    trace_mark(1, s);
     e = sse::launch_chunk_local(a, dtype, c, d, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    // 3. grouping into (sequence, head, partition) segments
+    trace_mark(2, s);
+    e = sse::launch_group(idx, w, cu_seqlens, num_seqs, max_seqlen, H, N, topk, true, counts,
+                          seg_off, seg_tok, seg_slot, seg_w, lnz2, seg_cr, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(3, s);
     // 4. routed partitions: e-gated reads into the workspace slots

@@ -100,6 +100,28 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Reduce x over groups of L consecutive lanes (L a power of two <= 64; every
+// lane gets its group's result).  A 16-lane group is one DPP row: four row
+// rotations, no LDS traffic.
+template <int L, typename Op>
+__device__ __forceinline__ float row_reduce(float x, Op op) {
+    if constexpr (L == 16) {
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false)));
+        x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false)));
+        return x;
+    } else {
+#pragma unroll
+        for (int o = L / 2; o >= 1; o >>= 1) x = op(x, __shfl_xor(x, o, kWave));
+        return x;
+    }
+}
+
 // fp32 atomic add that maps to the hardware instruction (no CAS loop).
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
 

@@ -43,6 +43,7 @@ struct ChunkArgs {
     const float* seg_cr;
     const int32_t* seg_slot;     // rank of each routed record in its token's top-k
     const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
+    float* lnz2_out;             // where the bf16 local-state pass stores lnz2
     const float* init;           // [S, H, N+1, c, d] or null
     float* o;
     float* final_states;
