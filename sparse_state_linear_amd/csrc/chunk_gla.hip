@@ -162,26 +162,26 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
     // loads carry no branch; threads < C store it after the next barrier.
     // Padded records keep a real row (so every address stays valid) and are
     // marked by a read gate of -0.0.
-    auto meta_load = [&](int64_t chunk, int& tok, float& cr, float& w, int& rank) {
+    auto meta_load = [&](int64_t chunk, uint32_t& row, uint32_t& orow, float& cr, float& w) {
         const int64_t idx = chunk * C + (tid % C);
         const int64_t ci = idx < n ? idx : (n > 0 ? n - 1 : 0);
         if constexpr (MODE == kModeRouted) {
-            tok = a.seg_tok[lo + ci];
-            cr = a.seg_cr[lo + ci];
-            w = a.seg_w[lo + ci];
-            rank = a.seg_slot[lo + ci];
+            const uint4 r = *reinterpret_cast<const uint4*>(a.seg_rec + (lo + ci));
+            row = r.x;
+            orow = r.y;
+            cr = __uint_as_float(r.z);
+            w = __uint_as_float(r.w);
         } else {
-            tok = (int)(lo + ci);
-            cr = a.lnz2[((int64_t)tok) * H + h];
+            row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
+            orow = row;
+            cr = a.lnz2[row];
             w = 1.f;
-            rank = 0;
         }
     };
-    auto meta_store = [&](int64_t chunk, int buf, int tok, float cr, float w, int rank) {
+    auto meta_store = [&](int64_t chunk, int buf, uint32_t row, uint32_t orow, float cr, float w) {
         const bool valid = chunk * C + tid < n;
-        const uint32_t row = (uint32_t)tok * (uint32_t)H + (uint32_t)h;
         sm.mrow[buf][tid] = row;
-        sm.mout[buf][tid] = MODE == kModeRouted ? row * (uint32_t)a.topk + (uint32_t)rank : row;
+        sm.mout[buf][tid] = orow;
         sm.mcr[buf][tid] = valid ? cr : INFINITY;
         sm.mw[buf][tid] = valid ? w : -0.f;
     };
@@ -462,12 +462,12 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
     //   of n+1; barrier; causal A tiles; barrier; MFMA phase with the outputs
     //   of chunk n.
     if (nchunks > 0) {
-        int mt = 0, mrk = 0;
+        uint32_t mrw = 0, mor = 0;
         float mc = 0.f, mwv = 0.f;
-        meta_load(0, mt, mc, mwv, mrk);
-        if (tid < C) meta_store(0, 0, mt, mc, mwv, mrk);
-        meta_load(1, mt, mc, mwv, mrk);
-        if (tid < C) meta_store(1, 1, mt, mc, mwv, mrk);
+        meta_load(0, mrw, mor, mc, mwv);
+        if (tid < C) meta_store(0, 0, mrw, mor, mc, mwv);
+        meta_load(1, mrw, mor, mc, mwv);
+        if (tid < C) meta_store(1, 1, mrw, mor, mc, mwv);
         lds_barrier();
         raw_load_qkl(0);
         raw_load_v(0);
@@ -476,11 +476,11 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<C, CK, DV, LV, LVV>)) void ch
             const bool more = c + 1 < nchunks;  // uniform
             prep(cur);
             if (more) raw_load_qkl(nxt);  // q, k, log_alpha registers are free now
-            meta_load(c + 2, mt, mc, mwv, mrk);
+            meta_load(c + 2, mrw, mor, mc, mwv);
             lds_barrier();  // previous chunk's MFMA phase is done with the tiles
             prep_store();
             if (more) raw_load_v(nxt);    // v registers are free after the V^T store
-            if (tid < C) meta_store(c + 2, nn, mt, mc, mwv, mrk);
+            if (tid < C) meta_store(c + 2, nn, mrw, mor, mc, mwv);
             lds_barrier();
             if constexpr (!kLocal) {
                 a_tiles();

@@ -84,7 +84,7 @@ __device__ __forceinline__ int swz(int row, int s) {
 }
 
 struct Meta {
-    int tok, slot;
+    uint32_t row, orow;  // input row t*H + h; output row (slot row or o row)
     float cr, w;
 };
 
@@ -194,15 +194,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         const int64_t idx = chunk * kWsC + (lane % kWsC);
         const int64_t ci = idx < n ? idx : n - 1;
         if constexpr (MODE == kModeRouted) {
-            m.tok = a.seg_tok[lo + ci];
-            m.slot = a.seg_slot[lo + ci];
-            m.cr = a.seg_cr[lo + ci];
-            m.w = a.seg_w[lo + ci];
+            const uint4 r = *reinterpret_cast<const uint4*>(a.seg_rec + (lo + ci));
+            m.row = r.x;
+            m.orow = r.y;
+            m.cr = __uint_as_float(r.z);
+            m.w = __uint_as_float(r.w);
         } else {
-            m.tok = (int)(lo + ci);
-            m.slot = 0;
+            m.row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
+            m.orow = m.row;
             // the local-state pass computes the normaliser itself (below)
-            m.cr = kLocal ? 0.f : a.lnz2[((int64_t)m.tok) * H + h];
+            m.cr = kLocal ? 0.f : a.lnz2[m.row];
             m.w = 1.f;
         }
     };
@@ -210,10 +211,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         if (lane < kWsC) {
             const int slot = (int)(chunk % kRing);
             const bool valid = chunk * kWsC + lane < n;
-            const uint32_t row = (uint32_t)m.tok * (uint32_t)H + (uint32_t)h;
-            sm.mrow[slot][lane] = row;
-            sm.mout[slot][lane] =
-                MODE == kModeRouted ? row * (uint32_t)a.topk + (uint32_t)m.slot : row;
+            sm.mrow[slot][lane] = m.row;
+            sm.mout[slot][lane] = m.orow;
             if constexpr (!kLocal) sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
             sm.mw[slot][lane] = valid ? m.w : -0.f;
         }

@@ -7,17 +7,23 @@
 //
 // Grouping is a stable counting sort done in three launches:
 //   route_count  one block per (sequence, 64-token block), all heads: routes
-//                the block's rows (one lane per row), counts records per
-//                (head, partition) in LDS, and stores the log2 normaliser of
-//                each row's key softmax (§2.3, eq. 11; 16 lanes per row,
-//                coalesced 16-byte loads) so that later passes need no row
-//                reduction;
+//                the block's rows (one lane per row), then one wave per head
+//                (lane = token) ranks every record among the block's records
+//                of its partition with wave ballots (time order kept), writes
+//                the per-(head, partition) block counts and a head-major
+//                (partition, rank, weight) record per routed token; for fp32
+//                inputs it also stores the log2 normaliser of each row's key
+//                softmax (section 2.3, eq. 11; 16 lanes per row, coalesced
+//                16-byte loads) so that later passes need no row reduction;
 //   block_scan   one block per (sequence, head): exclusive scan over its
 //                N x blocks counts.  The records of (s, h) occupy a known
 //                contiguous range (every token contributes exactly k
 //                records), so no scan across (s, h) is needed;
-//   scatter      one block per (sequence*head, token block): ranks each
-//                record inside its block with wave ballots and writes it.
+//   scatter      one wave per (sequence, head, token block): reads the
+//                head-major records (contiguous) and writes each as one
+//                16-byte segment record at its block start + rank.
+// The standalone grouping entry point (from a given top-k choice) counts
+// with LDS atomics and ranks with ballots in its scatter instead.
 #include "sse_launch.h"
 
 namespace sse {
@@ -137,59 +143,101 @@ __device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
     }
 }
 
-// Route the rows of one (sequence, 64-token block) for all heads, count the
-// records per (head, partition) in LDS (cnt, H x N ints of dynamic shared
-// memory), and store lnz2 = log2 of the key-softmax denominator
+// Route the rows of one (sequence, 64-token block) for all heads, in groups
+// of kHG heads: phase 1 routes the group's rows (one lane per row; the rows of
+// a token block are one contiguous range) into LDS, phase 2 gives each head
+// to one wave (lane = token), ranks the records of every partition by ballot
+// (stable: lower token first), writes the block counts counts[s, h, i, blk]
+// and the head-major records rinfo[(h T + t) K + j] = (i | rank << 16, w).
+// With lnz2 given, it also stores lnz2 = log2 of the key-softmax denominator
 // sum_j 2^((kl_j - m) log2 e) plus m log2 e, so that kappa_j =
-// 2^(kl_j log2 e - lnz2).  The rows of a token block are one contiguous
-// range: the router reads one row per lane with 16-byte loads, the key
-// normaliser spreads each row over CK/8 (bf16) or CK/4 (fp32) lanes.
+// 2^(kl_j log2 e - lnz2); the key normaliser spreads each row over CK/8
+// (bf16) or CK/4 (fp32) lanes.
+constexpr int kHG = 16;  // heads per routing group
 template <int NMAX, int CK, typename TIn>
 __global__ __launch_bounds__(256) void route_count_kernel(
-    const TIn* __restrict__ z, const TIn* __restrict__ kl, const int32_t* __restrict__ cu, int H,
-    int N, int K, int nblk, int32_t* __restrict__ idx, float* __restrict__ wout,
-    int32_t* __restrict__ counts, float* __restrict__ lnz2) {
-    extern __shared__ int cnt[];  // [H][N]
+    const TIn* __restrict__ z, const TIn* __restrict__ kl, const int32_t* __restrict__ cu,
+    int64_t T, int H, int N, int K, int nblk, int32_t* __restrict__ idx, float* __restrict__ wout,
+    int32_t* __restrict__ counts, uint2* __restrict__ rinfo, float* __restrict__ lnz2) {
+    extern __shared__ float swt[];  // [kHG][kTokBlock][K] weights, then the choices as bytes
+    uint8_t* ssel = reinterpret_cast<uint8_t*>(swt + kHG * kTokBlock * K);
     const int blk = blockIdx.x, s = blockIdx.y;
     const int64_t t1 = cu[s + 1];
     const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
-    const int64_t te = tb + kTokBlock < t1 ? tb + kTokBlock : t1;
-    const int64_t r0 = tb * H, r1 = te > tb ? te * H : r0;  // rows [r0, r1) (maybe none)
-    const int HN = H * N;
-    for (int i = threadIdx.x; i < HN; i += blockDim.x) cnt[i] = 0;
-    __syncthreads();
-    // kRB rows per thread and batch, loaded before any is routed
-    constexpr int kRB = 4;
-    for (int64_t rb = r0 + threadIdx.x; rb < r1; rb += (int64_t)kRB * blockDim.x) {
-        float zr[kRB][NMAX];
+    const int ntok = (int)(t1 - tb < 0 ? 0 : (t1 - tb > kTokBlock ? kTokBlock : t1 - tb));
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    constexpr int kRB = 4;  // rows per thread and batch, loaded before any is routed
+    for (int hg0 = 0; hg0 < H; hg0 += kHG) {
+        const int hgc = H - hg0 < kHG ? H - hg0 : kHG;
+        const int rows = ntok * hgc;
+        for (int rb = threadIdx.x; rb < rows; rb += kRB * (int)blockDim.x) {
+            float zr[kRB][NMAX];
 #pragma unroll
-        for (int b = 0; b < kRB; b++) {
-            const int64_t r = rb + (int64_t)b * blockDim.x;
-            load_router_row<NMAX, TIn>(z + (r < r1 ? r : r0) * N, N, zr[b]);
+            for (int b = 0; b < kRB; b++) {
+                const int rl = rb + b * (int)blockDim.x;
+                const int rr = rl < rows ? rl : rb;
+                const int64_t row = (tb + rr / hgc) * H + hg0 + rr % hgc;
+                load_router_row<NMAX, TIn>(z + row * N, N, zr[b]);
+            }
+#pragma unroll
+            for (int b = 0; b < kRB; b++) {
+                const int rl = rb + b * (int)blockDim.x;
+                if (rl >= rows) break;
+                const int tl = rl / hgc, hi = rl % hgc;
+                const int64_t row = (tb + tl) * H + hg0 + hi;
+                int sel[kMaxTopK];
+                float w[kMaxTopK];
+                route_row<NMAX>(zr[b], N, K, sel, w);
+#pragma unroll
+                for (int j = 0; j < kMaxTopK; j++)
+                    if (j < K) {
+                        idx[row * K + j] = sel[j];
+                        wout[row * K + j] = w[j];
+                        swt[(hi * kTokBlock + tl) * K + j] = w[j];
+                        ssel[(hi * kTokBlock + tl) * K + j] = (uint8_t)sel[j];
+                    }
+            }
         }
+        __syncthreads();
+        const bool valid = lane < ntok;
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+        for (int hi = wv; hi < hgc; hi += nw) {
+            const int h = hg0 + hi;
+            int sel[kMaxTopK], rank[kMaxTopK];
+            uint64_t mine = 0;
 #pragma unroll
-        for (int b = 0; b < kRB; b++) {
-            const int64_t r = rb + (int64_t)b * blockDim.x;
-            if (r >= r1) break;
-            const int h = (int)(r % H);
-            int sel[kMaxTopK];
-            float w[kMaxTopK];
-            route_row<NMAX>(zr[b], N, K, sel, w);
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; j++)
-                if (j < K) {
-                    idx[r * K + j] = sel[j];
-                    wout[r * K + j] = w[j];
-                    atomicAdd(&cnt[h * N + sel[j]], 1);
+            for (int j = 0; j < kMaxTopK; j++) {
+                sel[j] = -1;
+                rank[j] = 0;
+                if (j < K && valid) {
+                    sel[j] = ssel[(hi * kTokBlock + lane) * K + j];
+                    mine |= 1ull << sel[j];
                 }
+            }
+            int mycount = 0;
+            for (int i = 0; i < N; i++) {
+                const uint64_t bal = __ballot((mine >> i) & 1ull);
+#pragma unroll
+                for (int j = 0; j < kMaxTopK; j++)
+                    if (sel[j] == i) rank[j] = __popcll(bal & lt);
+                if (lane == i) mycount = __popcll(bal);
+            }
+            if (lane < N) counts[(((int64_t)s * H + h) * N + lane) * nblk + blk] = mycount;
+            if (valid)
+#pragma unroll
+                for (int j = 0; j < kMaxTopK; j++)
+                    if (j < K)
+                        rinfo[((int64_t)h * T + tb + lane) * K + j] =
+                            make_uint2((uint32_t)sel[j] | ((uint32_t)rank[j] << 16),
+                                       __float_as_uint(swt[(hi * kTokBlock + lane) * K + j]));
         }
+        __syncthreads();
     }
     if (lnz2) {
+        const int64_t r0 = tb * H, r1 = ntok > 0 ? (tb + ntok) * H : r0;  // rows [r0, r1)
         constexpr int VPL = 16 / (int)sizeof(TIn);  // values per lane
         constexpr int LPR = CK / VPL;                // lanes per row
         constexpr int RPW = kWave / LPR;             // rows per wave and pass
-        const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-        const int nw = blockDim.x / kWave;
         const int sub = lane % LPR, rr = lane / LPR;
         // kB passes per batch: all their loads are issued before any of
         // them is reduced, so the batch waits for memory once
@@ -231,12 +279,6 @@ __global__ __launch_bounds__(256) void route_count_kernel(
         }
         }
     }
-    __syncthreads();
-    if (counts)
-        for (int i = threadIdx.x; i < HN; i += blockDim.x) {
-            const int h = i / N, p = i % N;
-            counts[(((int64_t)s * H + h) * N + p) * nblk + blk] = cnt[i];
-        }
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and
@@ -263,7 +305,10 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int& total)
 }
 
 // counts[(sh*N + i)*nblk + blk] -> start position of that block's records of
-// partition i (in place); seg_offsets[sh*N + i] = start of segment.
+// partition i (in place); seg_offsets[sh*N + i] = start of segment.  Each
+// thread scans kScanE consecutive counts, so a tile of 256 kScanE counts
+// costs one round of loads.
+constexpr int kScanE = 8;
 __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restrict__ cu, int H,
                                                          int N, int K, int nblk,
                                                          int32_t* __restrict__ counts,
@@ -276,14 +321,25 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
     int carry = (int)((int64_t)K * ((int64_t)H * cu[s] + h * len));
     const int M = N * nblk;
     int32_t* c = counts + (int64_t)sh * M;
-    for (int base = 0; base < M; base += blockDim.x) {
-        const int e = base + threadIdx.x;
-        const int x = e < M ? c[e] : 0;
+    for (int base = 0; base < M; base += (int)blockDim.x * kScanE) {
+        const int e0 = base + (int)threadIdx.x * kScanE;
+        int x[kScanE];
+        int tsum = 0;
+#pragma unroll
+        for (int u = 0; u < kScanE; u++) {
+            x[u] = e0 + u < M ? c[e0 + u] : 0;
+            tsum += x[u];
+        }
         int total;
-        const int ex = block_exclusive_scan(x, tmp, total);
-        if (e < M) {
-            c[e] = carry + ex;
-            if (e % nblk == 0) seg_offsets[(int64_t)sh * N + e / nblk] = carry + ex;
+        int run = carry + block_exclusive_scan(tsum, tmp, total);
+#pragma unroll
+        for (int u = 0; u < kScanE; u++) {
+            const int e = e0 + u;
+            if (e < M) {
+                c[e] = run;
+                if (e % nblk == 0) seg_offsets[(int64_t)sh * N + e / nblk] = run;
+            }
+            run += x[u];
         }
         carry += total;
     }
@@ -291,18 +347,54 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
         seg_offsets[(int64_t)num_seqs * H * N] = (int32_t)(K * ((int64_t)H * cu[num_seqs]));
 }
 
-// Stable scatter of the records of one (sequence, head, token block): one
-// wave per 64-token block (a token block is exactly one wave, so a record's
-// rank among the block's records of its partition is a ballot popcount), four
-// token blocks per launch block.
-// When lnz2 is given, seg_cr[p] = lnz2[t, h] - log2(w) is stored too: the
-// exponent offset that turns 2^(kl log2 e - seg_cr) into w * kappa.
+// Forward scatter: one wave per (sequence, head, 64-token block) reads the
+// head-major records of route_count (lane = token) and writes each routed
+// record as one 16-byte SegRec at its block start (after block_scan) + rank.
 constexpr int kScatterWaves = 4;
+__global__ __launch_bounds__(kScatterWaves * kWave) void scatter_fwd_kernel(
+    const uint2* __restrict__ rinfo, const int32_t* __restrict__ cu, int64_t T, int H, int N,
+    int K, int nblk, const int32_t* __restrict__ pos, const float* __restrict__ lnz2,
+    SegRec* __restrict__ seg) {
+    static_assert(kTokBlock == kWave, "one wave per token block");
+    const int sh = blockIdx.x;
+    const int blk = blockIdx.y * kScatterWaves + (int)(threadIdx.x / kWave);
+    if (blk >= nblk) return;  // wave-uniform
+    const int s = sh / H, h = sh % H;
+    const int64_t t1 = cu[s + 1];
+    const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
+    if (tb >= t1) return;  // wave-uniform
+    const int lane = threadIdx.x % kWave;
+    const bool valid = tb + lane < t1;
+    const int64_t t = valid ? tb + lane : tb;  // invalid lanes re-read a valid token
+    const int start = lane < N ? pos[((int64_t)sh * N + lane) * nblk + blk] : 0;
+    const uint32_t row = (uint32_t)t * (uint32_t)H + (uint32_t)h;
+    const float l2 = lnz2[row];
+    uint2 inf[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; j++)
+        if (j < K) inf[j] = rinfo[((int64_t)h * T + t) * K + j];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; j++) {
+        if (j < K) {
+            const int i = (int)(inf[j].x & 0xffffu), rank = (int)(inf[j].x >> 16);
+            const int p = __shfl(start, i, kWave) + rank;  // all lanes active here
+            const float wj = __uint_as_float(inf[j].y);
+            if (valid)
+                *reinterpret_cast<uint4*>(seg + p) =
+                    make_uint4(row, row * (uint32_t)K + (uint32_t)j,
+                               __float_as_uint(l2 - log2f(wj)), inf[j].y);
+        }
+    }
+}
+
+// Stable scatter of the records of one (sequence, head, token block) for
+// the standalone grouping entry point: one wave per 64-token block (a token
+// block is exactly one wave, so a record's rank among the block's records of
+// its partition is a ballot popcount), four token blocks per launch block.
 __global__ __launch_bounds__(kScatterWaves * kWave) void scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ win, const int32_t* __restrict__ cu,
     int H, int N, int K, int nblk, const int32_t* __restrict__ pos, int32_t* __restrict__ seg_tok,
-    int32_t* __restrict__ seg_slot, float* __restrict__ seg_w, const float* __restrict__ lnz2,
-    float* __restrict__ seg_cr) {
+    int32_t* __restrict__ seg_slot, float* __restrict__ seg_w) {
     static_assert(kTokBlock == kWave, "one wave per token block");
     const int sh = blockIdx.x;
     const int blk = blockIdx.y * kScatterWaves + (int)(threadIdx.x / kWave);
@@ -342,11 +434,7 @@ __global__ __launch_bounds__(kScatterWaves * kWave) void scatter_kernel(
             const int p = pos[((int64_t)sh * N + i) * nblk + blk] + rank[j];
             seg_tok[p] = (int32_t)t;
             if (seg_slot) seg_slot[p] = j;
-            if (seg_w || seg_cr) {
-                const float wj = win[(t * H + h) * K + j];
-                if (seg_w) seg_w[p] = wj;
-                if (seg_cr) seg_cr[p] = lnz2[t * H + h] - log2f(wj);
-            }
+            if (seg_w) seg_w[p] = win[(t * H + h) * K + j];
         }
     }
 }
@@ -377,48 +465,49 @@ hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int
 int group_nblk(int max_seqlen) { return max_seqlen <= 0 ? 1 : (max_seqlen + kTokBlock - 1) / kTokBlock; }
 
 template <int NMAX, typename TIn>
-static void launch_rc_n(dim3 grid, const TIn* z, const TIn* kl, const int32_t* cu, int H, int c,
-                        int N, int K, int nblk, int32_t* idx, float* w, int32_t* counts,
-                        float* lnz2, hipStream_t st) {
-    const size_t lds = sizeof(int) * (size_t)H * N;  // <= 64 KB for H <= 256, N <= 64
+static void launch_rc_n(dim3 grid, const TIn* z, const TIn* kl, const int32_t* cu, int64_t T,
+                        int H, int c, int N, int K, int nblk, int32_t* idx, float* w,
+                        int32_t* counts, uint2* rinfo, float* lnz2, hipStream_t st) {
+    const size_t lds = (sizeof(float) + 1) * (size_t)kHG * kTokBlock * K;  // <= 40 KB
     if (c == 32)
-        route_count_kernel<NMAX, 32, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 32, TIn><<<grid, 256, lds, st>>>(z, kl, cu, T, H, N, K, nblk, idx, w, counts, rinfo, lnz2);
     else if (c == 64)
-        route_count_kernel<NMAX, 64, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 64, TIn><<<grid, 256, lds, st>>>(z, kl, cu, T, H, N, K, nblk, idx, w, counts, rinfo, lnz2);
     else
-        route_count_kernel<NMAX, 128, TIn><<<grid, 256, lds, st>>>(z, kl, cu, H, N, K, nblk, idx, w, counts, lnz2);
+        route_count_kernel<NMAX, 128, TIn><<<grid, 256, lds, st>>>(z, kl, cu, T, H, N, K, nblk, idx, w, counts, rinfo, lnz2);
 }
 
 template <typename TIn>
 static hipError_t launch_route_count_t(const void* z, const void* kl, const int32_t* cu,
-                                       int num_seqs, int max_seqlen, int H, int c, int N, int K,
-                                       int32_t* idx, float* w, int32_t* counts, float* lnz2,
-                                       hipStream_t st) {
+                                       int num_seqs, int max_seqlen, int64_t T, int H, int c,
+                                       int N, int K, int32_t* idx, float* w, int32_t* counts,
+                                       uint2* rinfo, float* lnz2, hipStream_t st) {
     const int nblk = group_nblk(max_seqlen);
     if ((int64_t)num_seqs * H == 0) return hipSuccess;
-    if (H > kMaxH) return hipErrorInvalidValue;
+    if (H > kMaxH || N > kMaxN || K > kMaxTopK) return hipErrorInvalidValue;
     dim3 grid((unsigned)nblk, (unsigned)num_seqs);
     const TIn* zz = static_cast<const TIn*>(z);
     const TIn* kk = static_cast<const TIn*>(kl);
     if (N <= 8)
-        launch_rc_n<8, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
+        launch_rc_n<8, TIn>(grid, zz, kk, cu, T, H, c, N, K, nblk, idx, w, counts, rinfo, lnz2, st);
     else if (N <= 16)
-        launch_rc_n<16, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
+        launch_rc_n<16, TIn>(grid, zz, kk, cu, T, H, c, N, K, nblk, idx, w, counts, rinfo, lnz2, st);
     else if (N <= 32)
-        launch_rc_n<32, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
+        launch_rc_n<32, TIn>(grid, zz, kk, cu, T, H, c, N, K, nblk, idx, w, counts, rinfo, lnz2, st);
     else
-        launch_rc_n<64, TIn>(grid, zz, kk, cu, H, c, N, K, nblk, idx, w, counts, lnz2, st);
+        launch_rc_n<64, TIn>(grid, zz, kk, cu, T, H, c, N, K, nblk, idx, w, counts, rinfo, lnz2, st);
     return hipGetLastError();
 }
 
 hipError_t launch_route_count(const void* z, const void* kl, int dtype, const int32_t* cu,
-                              int num_seqs, int max_seqlen, int H, int c, int N, int K,
-                              int32_t* idx, float* w, int32_t* counts, float* lnz2,
+                              int num_seqs, int max_seqlen, int64_t T, int H, int c, int N, int K,
+                              int32_t* idx, float* w, int32_t* counts, uint2* rinfo, float* lnz2,
                               hipStream_t st) {
-    return dtype == kF32 ? launch_route_count_t<float>(z, kl, cu, num_seqs, max_seqlen, H, c, N,
-                                                       K, idx, w, counts, lnz2, st)
-                         : launch_route_count_t<bf16_t>(z, kl, cu, num_seqs, max_seqlen, H, c,
-                                                        N, K, idx, w, counts, lnz2, st);
+    return dtype == kF32
+               ? launch_route_count_t<float>(z, kl, cu, num_seqs, max_seqlen, T, H, c, N, K, idx,
+                                             w, counts, rinfo, lnz2, st)
+               : launch_route_count_t<bf16_t>(z, kl, cu, num_seqs, max_seqlen, T, H, c, N, K,
+                                              idx, w, counts, rinfo, lnz2, st);
 }
 
 // Count records per (segment, token block) from an existing top-k choice.
@@ -441,9 +530,9 @@ __global__ __launch_bounds__(kTokBlock) void count_kernel(const int32_t* __restr
 __global__ void zero_int_kernel(int32_t* p) { *p = 0; }
 
 hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, int num_seqs,
-                        int max_seqlen, int H, int N, int K, bool counts_ready, int32_t* counts,
+                        int max_seqlen, int H, int N, int K, int32_t* counts,
                         int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot, float* seg_w,
-                        const float* lnz2, float* seg_cr, hipStream_t st) {
+                        hipStream_t st) {
     const int nblk = group_nblk(max_seqlen);
     const unsigned SH = (unsigned)(num_seqs * H);
     if (SH == 0) {
@@ -451,17 +540,32 @@ hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, i
         zero_int_kernel<<<1, 1, 0, st>>>(seg_offsets);
         return hipGetLastError();
     }
-    if (!counts_ready) {
-        count_kernel<<<dim3(SH, nblk), kTokBlock, 0, st>>>(idx, cu, H, N, K, nblk, counts);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    count_kernel<<<dim3(SH, nblk), kTokBlock, 0, st>>>(idx, cu, H, N, K, nblk, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    block_scan_kernel<<<SH, 256, 0, st>>>(cu, H, N, K, nblk, counts, seg_offsets, num_seqs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scatter_kernel<<<dim3(SH, (nblk + kScatterWaves - 1) / kScatterWaves), kScatterWaves * kWave,
+                     0, st>>>(idx, w, cu, H, N, K, nblk, counts, seg_tok, seg_slot, seg_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_fwd(const uint2* rinfo, const int32_t* cu, int num_seqs, int max_seqlen,
+                            int64_t T, int H, int N, int K, int32_t* counts, int32_t* seg_offsets,
+                            const float* lnz2, SegRec* seg, hipStream_t st) {
+    const int nblk = group_nblk(max_seqlen);
+    const unsigned SH = (unsigned)(num_seqs * H);
+    if (SH == 0) {
+        zero_int_kernel<<<1, 1, 0, st>>>(seg_offsets);
+        return hipGetLastError();
     }
     block_scan_kernel<<<SH, 256, 0, st>>>(cu, H, N, K, nblk, counts, seg_offsets, num_seqs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    scatter_kernel<<<dim3(SH, (nblk + kScatterWaves - 1) / kScatterWaves), kScatterWaves * kWave,
-                     0, st>>>(idx, w, cu, H, N, K, nblk, counts, seg_tok, seg_slot, seg_w, lnz2,
-                              seg_cr);
+    scatter_fwd_kernel<<<dim3(SH, (nblk + kScatterWaves - 1) / kScatterWaves),
+                         kScatterWaves * kWave, 0, st>>>(rinfo, cu, T, H, N, K, nblk, counts, lnz2,
+                                                         seg);
     return hipGetLastError();
 }
 

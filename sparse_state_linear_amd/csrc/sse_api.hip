@@ -24,8 +24,7 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
 }
 
 struct FwdLayout {
-    size_t idx, w, counts, seg_off, seg_tok, seg_w, seg_cr, seg_slot, lnz2, agg_S, agg_D, trash,
-        part, total;
+    size_t idx, w, counts, seg_off, rinfo, seg_rec, lnz2, agg_S, agg_D, trash, part, total;
 };
 
 // Workspace carving.  c, d = 0 sizes the grouping part only.  Returns false
@@ -48,10 +47,8 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     L.w = off;       off += align_up(sizeof(float) * (size_t)recs);
     L.counts = off;  off += align_up(sizeof(int32_t) * (size_t)cnt);
     L.seg_off = off; off += align_up(sizeof(int32_t) * (size_t)((int64_t)S * H * N + 1));
-    L.seg_tok = off; off += align_up(sizeof(int32_t) * (size_t)recs);
-    L.seg_w = off;   off += align_up(sizeof(float) * (size_t)recs);
-    L.seg_cr = off;  off += align_up(sizeof(float) * (size_t)recs);
-    L.seg_slot = off; off += align_up(sizeof(int32_t) * (size_t)recs);
+    L.rinfo = off;   off += align_up(sizeof(uint2) * (size_t)recs);
+    L.seg_rec = off; off += align_up(sizeof(sse::SegRec) * (size_t)recs);
     L.lnz2 = off;    off += align_up(sizeof(float) * (size_t)(T * H));
     L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
     L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
@@ -130,11 +127,9 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
     int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
-    int32_t* seg_tok = reinterpret_cast<int32_t*>(ws + L.seg_tok);
-    float* seg_w = reinterpret_cast<float*>(ws + L.seg_w);
-    float* seg_cr = reinterpret_cast<float*>(ws + L.seg_cr);
+    uint2* rinfo = reinterpret_cast<uint2*>(ws + L.rinfo);
+    sse::SegRec* seg_rec = reinterpret_cast<sse::SegRec*>(ws + L.seg_rec);
     float* lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
-    int32_t* seg_slot = reinterpret_cast<int32_t*>(ws + L.seg_slot);
 
     sse::ChunkArgs a;
     a.q = q;
@@ -143,10 +138,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.la = log_alpha;
     a.cu = cu_seqlens;
     a.seg_offsets = seg_off;
-    a.seg_tok = seg_tok;
-    a.seg_w = seg_w;
-    a.seg_cr = seg_cr;
-    a.seg_slot = seg_slot;
+    a.seg_rec = seg_rec;
     a.lnz2 = lnz2;
     a.lnz2_out = lnz2;
     a.init = initial_states;
@@ -167,8 +159,8 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     //    inputs; for bf16 inputs the local-state pass computes it)
     trace_mark(0, s);
     hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
-                                           max_seqlen, H, c, N, topk, idx, w, counts,
-                                           dtype == SSE_F32 ? lnz2 : nullptr, s);
+                                           max_seqlen, total_tokens, H, c, N, topk, idx, w,
+                                           counts, rinfo, dtype == SSE_F32 ? lnz2 : nullptr, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     // 2. local states of the shared pieces
     trace_mark(1, s);
@@ -176,8 +168,8 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     if (e != hipSuccess) return SSE_ERR_HIP;
     // 3. grouping into (sequence, head, partition) segments
     trace_mark(2, s);
-    e = sse::launch_group(idx, w, cu_seqlens, num_seqs, max_seqlen, H, N, topk, true, counts,
-                          seg_off, seg_tok, seg_slot, seg_w, lnz2, seg_cr, s);
+    e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N, topk,
+                              counts, seg_off, lnz2, seg_rec, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(3, s);
     // 4. routed partitions: e-gated reads into the workspace slots
@@ -275,9 +267,8 @@ int sse_group_by_partition(const int32_t* topk_idx, const float* topk_w,
     const size_t need = L.seg_off - L.counts;
     if (workspace_bytes < need || (need > 0 && !workspace)) return SSE_ERR_WORKSPACE;
     return hip_status(sse::launch_group(topk_idx, topk_w, cu_seqlens, num_seqs, max_seqlen, H, N,
-                                        topk, false, static_cast<int32_t*>(workspace),
-                                        seg_offsets, seg_tok, seg_slot, seg_w, nullptr, nullptr,
-                                        static_cast<hipStream_t>(stream)));
+                                        topk, static_cast<int32_t*>(workspace), seg_offsets,
+                                        seg_tok, seg_slot, seg_w, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -20,15 +20,33 @@ int group_nblk(int max_seqlen);
 hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int K, int32_t* idx,
                               float* w, hipStream_t st);
 
+// One routed record of a partition segment (16 bytes): input row t*H + h,
+// slot row (t*H + h)*topk + rank, exponent offset lnz2 - log2 w (so that
+// 2^(kl log2 e - cr) = w kappa), read gate w.
+struct SegRec {
+    uint32_t row, orow;
+    float cr, w;
+};
+
+// Routing of the forward: top-k + weights into idx / w ([T, H, K]), block
+// counts, head-major (partition | rank << 16, w) records in rinfo
+// ([H, T, K]), and with lnz2 non-null the key-softmax log2 normalisers.
 hipError_t launch_route_count(const void* z, const void* kl, int dtype, const int32_t* cu,
-                              int num_seqs, int max_seqlen, int H, int c, int N, int K,
-                              int32_t* idx, float* w, int32_t* counts, float* lnz2,
+                              int num_seqs, int max_seqlen, int64_t T, int H, int c, int N, int K,
+                              int32_t* idx, float* w, int32_t* counts, uint2* rinfo, float* lnz2,
                               hipStream_t st);
 
+// Standalone grouping from a given top-k choice (separate output arrays).
 hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, int num_seqs,
-                        int max_seqlen, int H, int N, int K, bool counts_ready, int32_t* counts,
+                        int max_seqlen, int H, int N, int K, int32_t* counts,
                         int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot, float* seg_w,
-                        const float* lnz2, float* seg_cr, hipStream_t st);
+                        hipStream_t st);
+
+// Grouping of the forward from route_count's counts and records into packed
+// segment records.
+hipError_t launch_group_fwd(const uint2* rinfo, const int32_t* cu, int num_seqs, int max_seqlen,
+                            int64_t T, int H, int N, int K, int32_t* counts, int32_t* seg_offsets,
+                            const float* lnz2, SegRec* seg, hipStream_t st);
 
 // Arguments of the chunked GLA passes (see chunk_gla.hip).
 struct ChunkArgs {
@@ -38,10 +56,7 @@ struct ChunkArgs {
     const void* la;
     const int32_t* cu;
     const int32_t* seg_offsets;  // routed segments
-    const int32_t* seg_tok;
-    const float* seg_w;
-    const float* seg_cr;
-    const int32_t* seg_slot;     // rank of each routed record in its token's top-k
+    const SegRec* seg_rec;       // routed records, segment by segment
     const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
     float* lnz2_out;             // where the bf16 local-state pass stores lnz2
     const float* init;           // [S, H, N+1, c, d] or null
