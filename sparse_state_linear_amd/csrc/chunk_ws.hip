@@ -610,11 +610,61 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         char* base = reinterpret_cast<char*>(valid ? dst : a.trash);
         *reinterpret_cast<float4*>(base + (valid ? off : (uint32_t)(tcol * 4))) = v;
     };
-    // slot rows of record row `orow` (shared pass): [row][topk][d]
+    // Routed slots in block floating point: slot row r holds DV int16 values
+    // (a.part, [r][DV]) and one fp32 step per 32-column group (a.part_scale,
+    // [r][DV/32]): value = int16 * step.  A group is one consumer wave's
+    // columns of one record, 8 lanes x 4 values; with 2^e the smallest power
+    // of two above the group's largest magnitude, the values are scaled by
+    // 2^-e into (-1, 1) and converted to normalised int16, step 2^e/32767, so
+    // every value is stored within one step, below 2^-14 of that magnitude.
+    struct SlotQ {
+        uint2 q;      // 4 int16 values
+        float step;
+    };
+    auto slot_encode = [&](const float4& v) {
+        // largest magnitude over the 8 lanes of the group (quad swaps, then
+        // the half-row mirror), compared as bit patterns (non-negative floats
+        // order like their bits)
+        uint32_t m = __float_as_uint(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        auto dpp = [](uint32_t x, auto ctrl) {
+            return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xf, 0xf, false);
+        };
+        m = max(m, dpp(m, std::integral_constant<int, 0xb1>{}));
+        m = max(m, dpp(m, std::integral_constant<int, 0x4e>{}));
+        m = max(m, dpp(m, std::integral_constant<int, 0x141>{}));
+        const int e = __builtin_amdgcn_frexp_expf(__uint_as_float(m));  // max < 2^e (e = 0 for 0)
+        SlotQ r;
+        r.q.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(
+                                                 __builtin_amdgcn_ldexpf(v.x, -e), __builtin_amdgcn_ldexpf(v.y, -e)));
+        r.q.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(
+                                                 __builtin_amdgcn_ldexpf(v.z, -e), __builtin_amdgcn_ldexpf(v.w, -e)));
+        r.step = __builtin_amdgcn_ldexpf(1.f / 32767.f, e);
+        return r;
+    };
+    // slot row of record row `orow` and rank j (shared pass): orow*topk + j
     auto slot_ld = [&](uint32_t orow, int j) {
-        const uint32_t off = (orow * (uint32_t)a.topk + (uint32_t)j) * (uint32_t)(DV * 4) +
-                             (uint32_t)(tcol * 4);
-        return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(a.part) + off);
+        const uint32_t srow = orow * (uint32_t)a.topk + (uint32_t)j;
+        SlotQ r;
+        r.q = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(a.part) +
+                                              srow * (uint32_t)(DV * 2) + (uint32_t)(tcol * 2));
+        r.step = a.part_scale[srow * (uint32_t)(DV / 32) + (uint32_t)wv];
+        return r;
+    };
+    auto slot_add = [](float4& v, const SlotQ& r) {
+        v.x = fmaf((float)(int)(int16_t)(r.q.x & 0xffffu), r.step, v.x);
+        v.y = fmaf((float)((int)r.q.x >> 16), r.step, v.y);
+        v.z = fmaf((float)(int)(int16_t)(r.q.y & 0xffffu), r.step, v.z);
+        v.w = fmaf((float)((int)r.q.y >> 16), r.step, v.w);
+    };
+    // routed pass: the record's slot row, or the spare row past the last
+    // one when the record is padding; the 8 lanes of a group all store its
+    // step (same value, same address)
+    auto slot_store = [&](uint32_t orow, bool valid, const float4& v) {
+        const SlotQ r = slot_encode(v);
+        const uint32_t srow = valid ? orow : a.slot_rows;
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.part) + srow * (uint32_t)(DV * 2) +
+                                  (uint32_t)(tcol * 2)) = r.q;
+        a.part_scale[srow * (uint32_t)(DV / 32) + (uint32_t)wv] = r.step;
     };
     constexpr int kPre = 2;  // slots per record prefetched before the shared outputs
     auto decay = [&](f32x16& Srt, const float4 (&e4)[4]) {
@@ -647,7 +697,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         uint32_t orow[2][2];
         bool oval[2][2];
         float4 tv[2][2];
-        float4 pre[2][2][kPre];
+        SlotQ pre[2][2][kPre];
         f32x4 Aacc = {0.f, 0.f, 0.f, 0.f};
         auto fetch_extra = [&](auto sI) {
             constexpr int s = decltype(sI)::value;
@@ -725,19 +775,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                     float4 v = tv[p][h2];
 #pragma unroll
                     for (int j = 0; j < kPre; j++)
-                        if (j < a.topk) {
-                            v.x += pre[p][h2][j].x;
-                            v.y += pre[p][h2][j].y;
-                            v.z += pre[p][h2][j].z;
-                            v.w += pre[p][h2][j].w;
-                        }
-                    for (int j = kPre; j < a.topk; j++) {
-                        const float4 u = slot_ld(orow[p][h2], j);
-                        v.x += u.x;
-                        v.y += u.y;
-                        v.z += u.z;
-                        v.w += u.w;
-                    }
+                        if (j < a.topk) slot_add(v, pre[p][h2][j]);
+                    for (int j = kPre; j < a.topk; j++) slot_add(v, slot_ld(orow[p][h2], j));
                     store_out(a.o, orow[p][h2], oval[p][h2], v);
                 }
         };
@@ -768,7 +807,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                             float4 th[2];
                             transpose_half(p, Op, mw4, th);
 #pragma unroll
-                            for (int h2 = 0; h2 < 2; h2++) store_out(a.part, orow[p][h2], oval[p][h2], th[h2]);
+                            for (int h2 = 0; h2 < 2; h2++) slot_store(orow[p][h2], oval[p][h2], th[h2]);
                         }
                     } else {
                         transpose(Op, mw4, tv);

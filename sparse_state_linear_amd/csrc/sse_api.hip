@@ -52,8 +52,10 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     L.lnz2 = off;    off += align_up(sizeof(float) * (size_t)(T * H));
     L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
     L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
-    L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? d : 1));
-    L.part = off;    off += align_up(sizeof(float) * (size_t)recs * (size_t)d);
+    L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? 2 * d : 1));
+    // fp32 slots: recs rows of d floats; bf16 slots: recs + 1 rows of d int16
+    // values, then recs + 1 rows of d/32 fp32 steps
+    L.part = off;    off += align_up(sizeof(float) * (size_t)(recs + 1) * (size_t)d);
     L.total = off;
     return true;
 }
@@ -148,6 +150,11 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.agg_D = reinterpret_cast<float*>(ws + L.agg_D);
     a.trash = reinterpret_cast<float*>(ws + L.trash);
     a.part = reinterpret_cast<float*>(ws + L.part);
+    // bf16 inputs: int16 slot values, then their steps, inside the fp32-sized
+    // slot area (2 d + d/8 <= 4 d bytes per slot row)
+    a.slot_rows = (uint32_t)(total_tokens * H * topk);
+    a.part_scale = reinterpret_cast<float*>(ws + L.part + sizeof(int16_t) * ((size_t)a.slot_rows + 1) *
+                                                             (size_t)d);
     a.num_seqs = num_seqs;
     a.H = H;
     a.N = N;

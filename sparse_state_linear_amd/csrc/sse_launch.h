@@ -66,7 +66,10 @@ struct ChunkArgs {
     float* agg_D;                // [S*H, max_pieces, c] piece decay products
     float* trash;                // one dummy output row for padded records
     float* part;                 // [T, H, topk, d] e-gated routed reads (routed
-                                 // pass writes, shared pass adds into o)
+                                 // pass writes, shared pass adds into o): fp32
+                                 // for fp32 inputs, int16 steps for bf16 inputs
+    float* part_scale;           // bf16 inputs: [T, H, topk, d/32] fp32 steps
+    uint32_t slot_rows;          // T H topk; bf16 slots have one spare row past it
     int num_seqs, H, N, topk;
     int piece_len;               // records per shared piece
     int max_pieces;
