@@ -26,14 +26,16 @@
 // their product with V waits one iteration (the barrier orders it); the V
 // operand of chunk n stays in registers meanwhile.
 //
-// LDS layouts (all reads are 16-byte, conflict-free for 8-lane groups):
+// LDS layouts (all operand reads are 16-byte):
 //   Qt, Kh record-major [r][j]: inside every 16 columns the 4-column blocks
 //     are stored in the order 0,2,1,3, so the 8 columns a lane needs as the
 //     MFMA partner of the state registers (rows 4h..4h+3 and 8+4h..8+4h+3 of
 //     each 16) are contiguous.
-//   Kh^T [j][s] and V^T [col][s]: the four 8-record blocks of a row are
-//     permuted by XOR with bits 3-4 of the row index, which spreads the
-//     producers' transposed 8-byte stores over all banks.
+//   Kh^T [j][s] and V^T [col][s], 80-byte rows: the four 8-record blocks of
+//     a row are permuted by XOR with (j >> 2) ^ (j >> 4).  The producers'
+//     transposed 8-byte stores (rows 4 apart) then spread over all banks, and
+//     of the layouts measured on gfx950 this one also costs the consumers'
+//     32-row 16-byte reads the fewest bank conflicts.
 #include "chunk_common.h"
 
 namespace sse {
@@ -80,7 +82,7 @@ __device__ __forceinline__ int perm_col(int j) {
 }
 // Storage position of record s in row `row` of Kh^T / V^T.
 __device__ __forceinline__ int swz(int row, int s) {
-    return ((((s >> 3) ^ (row >> 3)) & 3) << 3) | (s & 7);
+    return ((((s >> 3) ^ (row >> 2) ^ (row >> 4)) & 3) << 3) | (s & 7);
 }
 
 struct Meta {
