@@ -179,13 +179,18 @@ def cpu_baseline(args, w, si):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_ws_main_bf16_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "sparse_state_linear_amd", "csrc", "chunk_ws.hip")
+# the dominant kernel's source and the headers it includes
+KERNEL_SRC = [os.path.join(ROOT, "sparse_state_linear_amd", "csrc", f)
+              for f in ("chunk_ws.hip", "chunk_common.h", "sse_device.h", "sse_launch.h")]
 
 
 def kernel_source_hash() -> str:
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(stage):
