@@ -34,6 +34,10 @@ struct Vec4<bf16_t> {
     __device__ __forceinline__ void load(const void* base, uint32_t byte_off) {
         u = *reinterpret_cast<const uint2*>(static_cast<const char*>(base) + byte_off);
     }
+    // buffer load: an offset past the resource's size reads zeros
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t w = (e < 2) ? u.x : u.y;
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -54,6 +58,12 @@ struct Vec4<float> {
     }
     __device__ __forceinline__ uint16_t bits(int) const { return 0; }
 };
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zeros (gfx9 descriptor word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Preparation layout: CW columns per wave, NCG groups of 4 columns, NG
 // groups of RPG consecutive records.

@@ -48,6 +48,8 @@ constexpr int kProd = 4;          // producer waves
 constexpr int kWsThreads = (kCons + kProd) * kWave;
 constexpr int kRing = 8;          // metadata ring slots (7 are live at a time)
 constexpr int kL = 2;             // bf16 terms of Qt, Kh, A and S
+constexpr uint32_t kPadOff = 0x80000000u;  // row offset of padded records: past every
+                                           // input (inputs are < 2^31 bytes)
 
 static_assert(kProd == kNW, "the preparation layout assumes four producer waves");
 
@@ -66,7 +68,9 @@ struct WsSmem {
     WsStage<CK, DV> st[2];
     uint16_t a[2][kL][kWsC][kWsC + 8];  // A terms [r][s]
     float ebc[3][CK];                   // exp(b_C) per state row, ring by chunk % 3
-    uint32_t mrow[kRing][kWsC];         // record row t*H + h (a real row even if padded)
+    uint32_t mrow[kRing][kWsC];         // byte offset of the record's q / key / log_alpha
+                                        // row, past every input for a padded record
+    uint32_t mrv[kRing][kWsC];          // the same for its v row
     uint32_t mout[kRing][kWsC];         // output row: slot row (t*H + h)*topk + rank
                                         // (routed) or t*H + h (shared)
     float mcr[kRing][kWsC];             // lnz2 - log2 w (+inf if padded)
@@ -213,7 +217,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         if (lane < kWsC) {
             const int slot = (int)(chunk % kRing);
             const bool valid = chunk * kWsC + lane < n;
-            sm.mrow[slot][lane] = m.row;
+            // padded records read zeros (buffer loads past the end): no log
+            // decay, no key, no value
+            sm.mrow[slot][lane] = valid ? m.row * (uint32_t)(CK * 2) : kPadOff;
+            sm.mrv[slot][lane] = valid ? m.row * (uint32_t)(DV * 2) : kPadOff;
             sm.mout[slot][lane] = m.orow;
             if constexpr (!kLocal) sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
             sm.mw[slot][lane] = valid ? m.w : -0.f;
@@ -308,38 +315,38 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     // read gates / exponent offsets of the next chunk to prepare: read from
     // LDS one step before they are needed
     uint32_t rowq[RPG], rowv[RPGV];
-    float gw[RPG], gcr[RPG];
+    float gcr[RPG];
     auto read_rows = [&](int64_t chunk) {
         const int slot = (int)(chunk % kRing);
 #pragma unroll
         for (int i = 0; i < RPG; i++) rowq[i] = sm.mrow[slot][r0 + i];
 #pragma unroll
-        for (int i = 0; i < RPGV; i++) rowv[i] = sm.mrow[slot][r0v + i];
+        for (int i = 0; i < RPGV; i++) rowv[i] = sm.mrv[slot][r0v + i];
     };
     auto read_gates = [&](int64_t chunk) {
         const int slot = (int)(chunk % kRing);
 #pragma unroll
-        for (int i = 0; i < RPG; i++) {
-            gw[i] = sm.mw[slot][r0 + i];
-            gcr[i] = sm.mcr[slot][r0 + i];
-        }
+        for (int i = 0; i < RPG; i++) gcr[i] = sm.mcr[slot][r0 + i];
     };
-    // part 0: log_alpha, 1: key logits, 2: q, 3: v.  Byte offsets fit in 32
-    // bits (checked on the host).
+    // part 0: log_alpha, 1: key logits, 2: q, 3: v.  Buffer loads at byte
+    // offsets (< 2^31, checked on the host), so the rows of padded records
+    // (offsets past the end) read as zeros.
+    const uint32_t bk = a.rows * (uint32_t)(CK * 2), bv = a.rows * (uint32_t)(DV * 2);
+    const __amdgpu_buffer_rsrc_t rsq = make_rsrc(a.q, bk), rsk = make_rsrc(a.kl, bk);
+    const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.la, bk), rsv = make_rsrc(a.v, bv);
     auto raw_load_part = [&](Raw& R, int part) {
         if (part == 3) {
 #pragma unroll
-            for (int i = 0; i < RPGV; i++)
-                R.v[i].load(gv, rowv[i] * (uint32_t)(DV * 2) + (uint32_t)(c0v * 2));
+            for (int i = 0; i < RPGV; i++) R.v[i].load(rsv, rowv[i] + (uint32_t)(c0v * 2));
             return;
         }
 #pragma unroll
         for (int i = 0; i < RPG; i++) {
-            const uint32_t off = rowq[i] * (uint32_t)(CK * 2) + (uint32_t)(j0 * 2);
-            if (part == 0) R.l[i].load(gl, off);
-            if (part == 1) R.k[i].load(gk, off);
+            const uint32_t off = rowq[i] + (uint32_t)(j0 * 2);
+            if (part == 0) R.l[i].load(rsl, off);
+            if (part == 1) R.k[i].load(rsk, off);
             if constexpr (!kLocal)
-                if (part == 2) R.q[i].load(gq, off);
+                if (part == 2) R.q[i].load(rsq, off);
         }
     };
     auto raw_load = [&](Raw& R) {
@@ -347,53 +354,61 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         for (int part = 0; part < 4; part++) raw_load_part(R, part);
     };
 
-    // Inclusive scan of x over the record groups of this lane's column group
-    // (lanes cg, cg + NCG, ...), plus the total over all groups.  With 8
-    // column groups (c = 128) the groups are 8 lanes apart: two per 16-lane
-    // row, so the scan uses a DPP row shift inside rows and the row-swap
-    // permutations across rows, with no LDS traffic.
-    auto group_scan = [&](float x, float& incl, float& total) {
+    // Inclusive scans of x[e] (e < 4, independent columns) over the record
+    // groups of this lane's column group (lanes cg, cg + NCG, ...), plus the
+    // totals over all groups.  With 8 column groups (c = 128) the groups are
+    // 8 lanes apart, two per 16-lane row: a DPP row shift adds inside rows,
+    // then the row-pair and half-wave swaps (v_permlane16/32_swap with one
+    // register as both operands: each lane receives its partner row's value)
+    // add across rows, with no LDS traffic.  The swaps are inline assembly,
+    // four per block with wait states on both sides, since the compiler's
+    // model of the swap builtins merges their results and cannot see their
+    // hazards.
+    auto group_scan4 = [&](const float (&x)[kPC], float (&incl)[kPC], float (&total)[kPC]) {
         if constexpr (GK::NCG == 8) {
-            const int rowi = lane >> 4;
-            const bool hi8 = (lane & 8) != 0;
-            // within the row: the odd group adds the even one
-            const float a1 = x + __builtin_bit_cast(
-                                     float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                        0x118, 0xf, 0xf, false));
-            // row total for this column group (the odd group's value)
-            const float sh = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a1), 0x108, 0xf, 0xf, false));
-            const float rt = hi8 ? a1 : sh;
-            // The row swaps are written as inline assembly (the compiler's
-            // model of the swap builtins merges their two results, which
-            // loses the select between them below), padded with wait states
-            // on both sides since the compiler cannot see their hazards.
-            // v_permlane16_swap a, b: odd rows of a <-> even rows of b, so
-            // with a = b = rt, a's odd rows hold the even row's total and b's
-            // even rows hold the odd row's total.
-            unsigned e16 = __builtin_bit_cast(unsigned, rt), o16 = e16;
-            asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4" : "+v"(e16), "+v"(o16));
-            const float from_even = __builtin_bit_cast(float, e16);
-            const float from_odd = __builtin_bit_cast(float, o16);
-            const bool odd = (rowi & 1) != 0;
-            const float pair = rt + (odd ? from_even : from_odd);
-            // v_permlane32_swap a, b: upper half of a <-> lower half of b
-            unsigned l32v = __builtin_bit_cast(unsigned, pair), h32v = l32v;
-            asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(l32v), "+v"(h32v));
-            const float low_pair = __builtin_bit_cast(float, l32v);    // upper half: rows 0-1 total
-            const float high_pair = __builtin_bit_cast(float, h32v);   // lower half: rows 2-3 total
-            const bool upper = lane >= 32;
-            incl = a1 + (odd ? from_even : 0.f) + (upper ? low_pair : 0.f);
-            total = pair + (upper ? low_pair : high_pair);
-        } else {
-            float inc = x;
+            const bool hi8 = (lane & 8) != 0, odd = ((lane >> 4) & 1) != 0, upper = lane >= 32;
+            float a1[kPC], rt[kPC], pair[kPC];
+            unsigned s16[kPC], s32[kPC];
 #pragma unroll
-            for (int off = GK::NCG; off < kWave; off <<= 1) {
-                const float y = __shfl_up(inc, off, kWave);
-                if (lane >= off) inc += y;
+            for (int e = 0; e < kPC; e++) {
+                // within the row: the odd group adds the even one; the row
+                // total is the odd group's inclusive value
+                a1[e] = x[e] + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                             0, __builtin_bit_cast(int, x[e]), 0x118, 0xf, 0xf, false));
+                const float sh = __builtin_bit_cast(
+                    float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a1[e]), 0x108, 0xf, 0xf, false));
+                rt[e] = hi8 ? a1[e] : sh;
+                s16[e] = __builtin_bit_cast(unsigned, rt[e]);
             }
-            incl = inc;
-            total = __shfl(inc, kWave - GK::NCG + cg, kWave);
+            asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %0\n\tv_permlane16_swap_b32 %1, %1\n\t"
+                         "v_permlane16_swap_b32 %2, %2\n\tv_permlane16_swap_b32 %3, %3\n\ts_nop 4"
+                         : "+v"(s16[0]), "+v"(s16[1]), "+v"(s16[2]), "+v"(s16[3]));
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                pair[e] = rt[e] + __builtin_bit_cast(float, s16[e]);   // rows 0-1 or 2-3
+                s32[e] = __builtin_bit_cast(unsigned, pair[e]);
+            }
+            asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %0\n\tv_permlane32_swap_b32 %1, %1\n\t"
+                         "v_permlane32_swap_b32 %2, %2\n\tv_permlane32_swap_b32 %3, %3\n\ts_nop 4"
+                         : "+v"(s32[0]), "+v"(s32[1]), "+v"(s32[2]), "+v"(s32[3]));
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                const float other_half = __builtin_bit_cast(float, s32[e]);
+                total[e] = pair[e] + other_half;
+                incl[e] = a1[e] + (odd ? __builtin_bit_cast(float, s16[e]) : 0.f) + (upper ? other_half : 0.f);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kPC; e++) {
+                float inc = x[e];
+#pragma unroll
+                for (int off = GK::NCG; off < kWave; off <<= 1) {
+                    const float y = __shfl_up(inc, off, kWave);
+                    if (lane >= off) inc += y;
+                }
+                incl[e] = inc;
+                total[e] = __shfl(inc, kWave - GK::NCG + cg, kWave);
+            }
         }
     };
 
@@ -408,24 +423,20 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         float run[kPC] = {0.f, 0.f, 0.f, 0.f};
         float bb[RPG][kPC];
 #pragma unroll
-        for (int i = 0; i < RPG; i++) {
-            const bool valid = is_real(gw[i]);  // padded records' log decay must not count
+        for (int i = 0; i < RPG; i++)
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
-                const float x = valid ? R.l[i].get(e) : 0.f;
-                run[e] = fmaf(x, kLog2e, run[e]);
+                run[e] = fmaf(R.l[i].get(e), kLog2e, run[e]);  // zero for a padded record
                 bb[i][e] = run[e];
             }
-        }
         hook(1);
-        float excl[kPC], ebc_own[kPC];
+        float excl[kPC], ebc_own[kPC], incl[kPC], tot[kPC];
+        group_scan4(run, incl, tot);
 #pragma unroll
         for (int e = 0; e < kPC; e++) {
-            float incl, tot;
-            group_scan(run[e], incl, tot);
-            excl[e] = incl - run[e];
-            ebc_own[e] = __builtin_amdgcn_exp2f(tot);
-            if constexpr (kLocal) btot[e] += tot;
+            excl[e] = incl[e] - run[e];
+            ebc_own[e] = __builtin_amdgcn_exp2f(tot[e]);
+            if constexpr (kLocal) btot[e] += tot[e];
         }
         hook(2);
         uint2 pk[RPG][kL];

@@ -153,6 +153,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     // bf16 inputs: int16 slot values, then their steps, inside the fp32-sized
     // slot area (2 d + d/8 <= 4 d bytes per slot row)
     a.slot_rows = (uint32_t)(total_tokens * H * topk);
+    a.rows = (uint32_t)(total_tokens * H);
     a.part_scale = reinterpret_cast<float*>(ws + L.part + sizeof(int16_t) * ((size_t)a.slot_rows + 1) *
                                                              (size_t)d);
     a.num_seqs = num_seqs;

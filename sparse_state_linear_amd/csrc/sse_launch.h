@@ -70,6 +70,7 @@ struct ChunkArgs {
                                  // for fp32 inputs, int16 steps for bf16 inputs
     float* part_scale;           // bf16 inputs: [T, H, topk, d/32] fp32 steps
     uint32_t slot_rows;          // T H topk; bf16 slots have one spare row past it
+    uint32_t rows;               // T H: rows of every token input
     int num_seqs, H, N, topk;
     int piece_len;               // records per shared piece
     int max_pieces;
