@@ -5,129 +5,180 @@
 // §2.6 (decode recurs only on the selected states; unselected states keep an
 // identity transition).
 //
-// One block per (sequence*head, 32-column slice of d).  Each block routes its
-// token (wave 0), computes the key softmax and decay for the c rows, and then
-// streams the c x 32 slices of the k+1 active states: read, decay, rank-one
-// write, store back in place, and accumulate the gated read q S.  The other
-// N-k routed states are never touched.  The step is HBM-bound: per (b, h) it
-// moves 2 (k+1) c d fp32 values.
+// One block per (sequence*head, 32-column slice of d), four waves; wave w
+// owns rows [w c/4, (w+1) c/4) of the slice, lane = (4-column group, row
+// group), so each row's 128 bytes are read and written by 8 lanes.  The step
+// is HBM-bound (per (b, h) it moves 2 (k+1) c d fp32 values), so the kernel
+// is arranged to put state loads in flight as early as possible:
+//   1. the shared partition's slice does not depend on the routing and is
+//      loaded first, together with the token's inputs;
+//   2. every wave computes the key softmax (eq. 11) and the router (eqs.
+//      9-10) by itself with wave reductions, so no block barrier stands
+//      between the loads and the routing;
+//   3. the routed slices are loaded two partitions at a time, the first pair
+//      before the shared slice is processed.
+// The N - k unselected states are never read or written.  The gated reads
+// are reduced over rows inside each wave and across the four waves through
+// LDS, in a fixed order (deterministic).
 #include "sse_launch.h"
 
 namespace sse {
 
 constexpr int kDecCols = 32;     // columns of d per block
-constexpr int kDecThreads = 256;
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+
+// State slices are read once and written once per step, and a step touches
+// far more than the caches hold: nontemporal loads and stores (measured
+// a few per cent faster than plain ones on gfx950).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float* p) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(float* p, const float4& y) {
+    const f32x4v v = {y.x, y.y, y.z, y.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(p));
+}
 
 template <int CK, typename TIn>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ kl, const TIn* __restrict__ v,
     const TIn* __restrict__ la, const TIn* __restrict__ z, int H, int d, int N, int K,
     float* __restrict__ states, float* __restrict__ o, int32_t* __restrict__ topk_idx) {
-    constexpr int RG = kDecThreads / (kDecCols / 4);  // row groups (32)
-    constexpr int RPT = CK / RG > 0 ? CK / RG : 1;    // rows per thread
-    __shared__ float s_kappa[CK], s_alpha[CK], s_q[CK], s_v[kDecCols];
-    __shared__ float s_red[2][kDecThreads / kWave];
-    __shared__ float s_w[kMaxTopK + 1];
-    __shared__ int s_part[kMaxTopK + 1];
-    __shared__ float s_opart[kDecThreads / kWave][kDecCols];
+    constexpr int RW = CK / kDecWaves;         // rows per wave
+    constexpr int RG = kWave / (kDecCols / 4); // row groups per wave (8)
+    constexpr int RPT = RW / RG;               // rows per lane
+    constexpr int KPL = (CK + kWave - 1) / kWave;  // key logits per lane
+    static_assert(RPT >= 1 && RW % RG == 0, "rows must split evenly over the row groups");
+    __shared__ float s_o[kDecWaves][kDecCols];
 
-    const int bh = blockIdx.x, cb = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-    const int d0 = cb * kDecCols;
+    const int bh = blockIdx.x, cb = blockIdx.y, d0 = cb * kDecCols;
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c4 = lane % (kDecCols / 4), rg = lane / (kDecCols / 4);
+    const int64_t in_c = (int64_t)bh * CK;
+    const int64_t cd = (int64_t)CK * d;
+    // this lane's rows j = RW wv + rg + RG u and columns d0 + 4 c4 .. + 3
+    float* const Sbh = states + (int64_t)bh * (N + 1) * cd + (int64_t)(wv * RW + rg) * d + d0 + 4 * c4;
 
-    // ---- router (wave 0): eq. (9) softmax over N, eq. (10) top-k on logits
-    if (wv == 0) {
-        const float zi = lane < N ? to_f32(z[(int64_t)bh * N + lane]) : -INFINITY;
-        const float m = wave_max(zi);
-        const float den = wave_sum(lane < N ? expf(zi - m) : 0.f);
-        bool taken = false;
-        for (int r = 0; r < K; r++) {
-            float bv = (lane < N && !taken) ? zi : -INFINITY;
-            int bi = (lane < N && !taken) ? lane : kWave;
+    // ---- 1. shared slice and the token's inputs
+    float4 xs[RPT];
+    const float* Ssh = Sbh + (int64_t)N * cd;
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oi = __shfl_xor(bi, off, kWave);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (lane == bi) taken = true;
-            if (lane == 0) {
-                s_part[r] = bi;
-                s_w[r] = expf(bv - m) / den;
-                if (topk_idx && cb == 0) topk_idx[(int64_t)bh * K + r] = bi;
-            }
-        }
-        if (lane == 0) {
-            s_part[K] = N;   // shared partition, weight 1
-            s_w[K] = 1.f;
-        }
-    }
-    // ---- key softmax (eq. 11), decay (eq. 6), query, value slice
-    float kx = -INFINITY;
-    if (tid < CK) {
-        const int64_t off = (int64_t)bh * CK + tid;
-        kx = to_f32(kl[off]);
-        s_alpha[tid] = expf(to_f32(la[off]));
-        s_q[tid] = to_f32(q[off]);
-    }
-    if (tid < kDecCols) s_v[tid] = to_f32(v[(int64_t)bh * d + d0 + tid]);
-    float m = wave_max(kx);
-    if (lane == 0) s_red[0][wv] = m;
-    __syncthreads();
-    m = s_red[0][0];
-    for (int i = 1; i < kDecThreads / kWave; i++) m = fmaxf(m, s_red[0][i]);
-    const float ex = tid < CK ? expf(kx - m) : 0.f;
-    const float ssum = wave_sum(ex);
-    if (lane == 0) s_red[1][wv] = ssum;
-    __syncthreads();
-    float den = 0.f;
-    for (int i = 0; i < kDecThreads / kWave; i++) den += s_red[1][i];
-    if (tid < CK) s_kappa[tid] = ex / den;
-    __syncthreads();
-
-    // ---- stream the k+1 active state slices
-    const int c4 = tid % (kDecCols / 4);   // float4 column group
-    const int rg = tid / (kDecCols / 4);   // row group
-    const float4 vv = *reinterpret_cast<const float4*>(&s_v[4 * c4]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int64_t sbase = (int64_t)bh * (N + 1) * CK * d;
-    for (int r = 0; r <= K; r++) {
-        const int p = s_part[r];
-        const float w = s_w[r];
-        float* Sp = states + sbase + (int64_t)p * CK * d + d0 + 4 * c4;
-        float4 x[RPT];
+    for (int u = 0; u < RPT; u++) xs[u] = load_nt(Ssh + (int64_t)(RG * u) * d);
+    float qj[RPT], klj[RPT], laj[RPT];
 #pragma unroll
-        for (int u = 0; u < RPT; u++) {
-            const int j = rg + RG * u;
-            if (j < CK) x[u] = *reinterpret_cast<const float4*>(Sp + (int64_t)j * d);
-        }
+    for (int u = 0; u < RPT; u++) {
+        const int64_t j = in_c + wv * RW + rg + RG * u;
+        qj[u] = to_f32(q[j]);
+        klj[u] = to_f32(kl[j]);
+        laj[u] = to_f32(la[j]);
+    }
+    float4 vv;
+    {
+        const int64_t vo = (int64_t)bh * d + d0 + 4 * c4;
+        vv = make_float4(to_f32(v[vo]), to_f32(v[vo + 1]), to_f32(v[vo + 2]), to_f32(v[vo + 3]));
+    }
+    float kx[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; i++) kx[i] = lane + kWave * i < CK ? to_f32(kl[in_c + lane + kWave * i]) : -INFINITY;
+    const float zi = lane < N ? to_f32(z[(int64_t)bh * N + lane]) : -INFINITY;
+
+    // ---- 2. key softmax (eq. 11) and decay (eq. 6) of this lane's rows
+    float km = kx[0];
+#pragma unroll
+    for (int i = 1; i < KPL; i++) km = fmaxf(km, kx[i]);
+    km = wave_max(km);
+    float ks = 0.f;
+#pragma unroll
+    for (int i = 0; i < KPL; i++) ks += lane + kWave * i < CK ? expf(kx[i] - km) : 0.f;
+    const float kden = wave_sum(ks);
+    float kap[RPT], alp[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; u++) {
+        kap[u] = expf(klj[u] - km) / kden;
+        alp[u] = expf(laj[u]);
+    }
+    // router softmax (eq. 9): max and denominator over the N logits
+    const float zm = wave_max(zi);
+    const float zden = wave_sum(lane < N ? expf(zi - zm) : 0.f);
+
+    // S <- diag(alpha) S + w kappa^T v on this lane's rows, stored in place;
+    // returns q S over those rows (eqs. 12-13 for one partition)
+    auto update = [&](float* Sp, const float4 (&x)[RPT], float w) {
         float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int u = 0; u < RPT; u++) {
-            const int j = rg + RG * u;
-            if (j < CK) {
-                const float a = s_alpha[j], wk = w * s_kappa[j], qj = s_q[j];
-                float4 y;
-                y.x = a * x[u].x + wk * vv.x;
-                y.y = a * x[u].y + wk * vv.y;
-                y.z = a * x[u].z + wk * vv.z;
-                y.w = a * x[u].w + wk * vv.w;
-                *reinterpret_cast<float4*>(Sp + (int64_t)j * d) = y;
-                part.x += qj * y.x;
-                part.y += qj * y.y;
-                part.z += qj * y.z;
-                part.w += qj * y.w;
+            const float a = alp[u], wk = w * kap[u];
+            float4 y;
+            y.x = a * x[u].x + wk * vv.x;
+            y.y = a * x[u].y + wk * vv.y;
+            y.z = a * x[u].z + wk * vv.z;
+            y.w = a * x[u].w + wk * vv.w;
+            store_nt(Sp + (int64_t)(RG * u) * d, y);
+            part.x += qj[u] * y.x;
+            part.y += qj[u] * y.y;
+            part.z += qj[u] * y.z;
+            part.w += qj[u] * y.w;
+        }
+        return part;
+    };
+
+    // ---- 3. routed partitions, two at a time (eq. 10: descending logits,
+    //         equal logits -> lower index)
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), psh = acc;
+    bool taken = false;
+    for (int r0 = 0; r0 < K; r0 += 2) {
+        int p[2] = {0, 0};
+        float w[2] = {0.f, 0.f};
+        float4 x[2][RPT];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            const int r = r0 + h2;
+            if (r < K) {  // wave-uniform
+                float bv = (lane < N && !taken) ? zi : -INFINITY;
+                int bi = (lane < N && !taken) ? lane : kWave;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) {
+                    const float ov = __shfl_xor(bv, off, kWave);
+                    const int oi = __shfl_xor(bi, off, kWave);
+                    if (ov > bv || (ov == bv && oi < bi)) {
+                        bv = ov;
+                        bi = oi;
+                    }
+                }
+                if (lane == bi) taken = true;
+                // (bi < N for finite logits; the clamp keeps the address in
+                // range whatever the logits hold)
+                p[h2] = min(__builtin_amdgcn_readfirstlane(bi), N - 1);
+                w[h2] = expf(bv - zm) / zden;
+                if (topk_idx && cb == 0 && wv == 0 && lane == 0) topk_idx[(int64_t)bh * K + r] = bi;
+                const float* Sp = Sbh + (int64_t)p[h2] * cd;
+#pragma unroll
+                for (int u = 0; u < RPT; u++)
+                    x[h2][u] = load_nt(Sp + (int64_t)(RG * u) * d);
             }
         }
-        acc.x += w * part.x;
-        acc.y += w * part.y;
-        acc.z += w * part.z;
-        acc.w += w * part.w;
+        if (r0 == 0) psh = update(Sbh + (int64_t)N * cd, xs, 1.f);  // shared partition, weight 1
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            if (r0 + h2 < K) {
+                const float4 part = update(Sbh + (int64_t)p[h2] * cd, x[h2], w[h2]);
+                acc.x += w[h2] * part.x;
+                acc.y += w[h2] * part.y;
+                acc.z += w[h2] * part.z;
+                acc.w += w[h2] * part.w;
+            }
+        }
     }
-    // ---- reduce the partial reads over row groups
+    acc.x += psh.x;
+    acc.y += psh.y;
+    acc.z += psh.z;
+    acc.w += psh.w;
+
+    // ---- 4. o = sum of the gated reads: over the row groups of the wave,
+    //         then over the waves
 #pragma unroll
     for (int off = kDecCols / 4; off < kWave; off <<= 1) {
         acc.x += __shfl_xor(acc.x, off, kWave);
@@ -135,17 +186,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         acc.z += __shfl_xor(acc.z, off, kWave);
         acc.w += __shfl_xor(acc.w, off, kWave);
     }
-    if (lane < kDecCols / 4) {
-        s_opart[wv][4 * lane + 0] = acc.x;
-        s_opart[wv][4 * lane + 1] = acc.y;
-        s_opart[wv][4 * lane + 2] = acc.z;
-        s_opart[wv][4 * lane + 3] = acc.w;
-    }
+    if (lane < kDecCols / 4) *reinterpret_cast<float4*>(&s_o[wv][4 * lane]) = acc;
     __syncthreads();
-    if (tid < kDecCols) {
+    if (threadIdx.x < kDecCols) {
         float sum = 0.f;
-        for (int i = 0; i < kDecThreads / kWave; i++) sum += s_opart[i][tid];
-        o[(int64_t)bh * d + d0 + tid] = sum;
+#pragma unroll
+        for (int i = 0; i < kDecWaves; i++) sum += s_o[i][threadIdx.x];
+        o[(int64_t)bh * d + d0 + threadIdx.x] = sum;
     }
 }
 

@@ -230,7 +230,9 @@ int sse_decode_step(const void* q, const void* key_logits, const void* v, const 
     int st = check_common(dtype, H, c, d, N, topk);
     if (st != SSE_OK) return st;
     if (B < 0) return SSE_ERR_INVALID_ARG;
-    if ((int64_t)B * H >= INT_MAX) return SSE_ERR_UNSUPPORTED;
+    // one 256-thread block per (b, h, 32 columns): the grid's work-items must
+    // stay below 2^32
+    if ((int64_t)B * H * (d / 32) * 256 >= ((int64_t)1 << 32)) return SSE_ERR_UNSUPPORTED;
     if (B > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !states || !o))
         return SSE_ERR_INVALID_ARG;
     return hip_status(sse::launch_decode(q, key_logits, v, log_alpha, router_logits, dtype, B, H,
