@@ -574,6 +574,7 @@ hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipSt
     // fp32: nothing to do without a second piece; bf16: the pass also
     // computes every token's key-softmax normaliser, so it always runs
     if (dtype == kF32 && a.max_pieces <= 1) return hipSuccess;
+    if (dtype != kF32) return launch_piece_state(a, c, d, st);
     return launch_mode<kModeLocal>(a, dtype, c, d, st);
 }
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {

@@ -1,5 +1,5 @@
 // chunk_ws.hip -- warp-specialised chunked gated linear attention for bf16
-// inputs on gfx950 (the routed, shared and local-state passes).
+// inputs on gfx950 (the routed and shared passes).
 //
 // Method: "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记",
 // §2.3 eqs. 12-14 (gated write and read of a partition state), §2.1 eq. 6
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     using SM = WsSmem<CK, DV>;
     using GK = Geo<kWsC, CK>;
     using GV = Geo<kWsC, DV>;
-    constexpr bool kLocal = MODE == kModeLocal;
+    static_assert(MODE == kModeShared || MODE == kModeRouted, "routed and shared passes only");
     constexpr int NS = DV / 32;       // consumer waves that own state columns
     constexpr int RT_N = CK / 32;     // 32-row tiles of the state
     constexpr int RPG = GK::RPG, RPGV = GV::RPG;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     for (int rt = 0; rt < RT_N; rt++)
 #pragma unroll
         for (int i = 0; i < 16; i++) S[rt][i] = 0.f;
-    if (col_wave && !kLocal) {
+    if (col_wave) {
         if (a.init) {
 #pragma unroll
             for (int rt = 0; rt < RT_N; rt++)
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                     S[rt][i] = a.init[sbase + (int64_t)row * DV + col];
                 }
         }
-        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the local-state pass
+        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the piece-state pass
         for (int p = 0; p < piece; p++) {
             const int64_t ab = abase + p;
 #pragma unroll
@@ -208,8 +208,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         } else {
             m.row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
             m.orow = m.row;
-            // the local-state pass computes the normaliser itself (below)
-            m.cr = kLocal ? 0.f : a.lnz2[m.row];
+            m.cr = a.lnz2[m.row];
             m.w = 1.f;
         }
     };
@@ -222,85 +221,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             sm.mrow[slot][lane] = valid ? m.row * (uint32_t)(CK * 2) : kPadOff;
             sm.mrv[slot][lane] = valid ? m.row * (uint32_t)(DV * 2) : kPadOff;
             sm.mout[slot][lane] = m.orow;
-            if constexpr (!kLocal) sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
+            sm.mcr[slot][lane] = valid ? m.cr : INFINITY;
             sm.mw[slot][lane] = valid ? m.w : -0.f;
         }
     };
     auto is_real = [](float w) { return (__float_as_uint(w) >> 31) == 0u; };
-
-    // ---------------- local pass: key-softmax normalisers ----------------
-    // In the local-state pass (the first pass over every token) the consumer
-    // waves compute lnz2 = log2 of the key-softmax denominator of every
-    // record (max-shifted: m log2 e + log2 sum_j 2^((kl_j - m) log2 e), so
-    // kappa_j = 2^(kl_j log2 e - lnz2)), three chunks before the producers
-    // prepare that chunk: into the metadata ring for this pass and into
-    // lnz2_out for the later passes.  Consumer wave ws takes records
-    // 8 ws .. 8 ws + 7 of a chunk, CK/8 lanes per record (16-byte loads).
-    constexpr int kLPR = CK / 8;                         // lanes per record
-    constexpr int kRPI = kWave / kLPR;                   // records per load
-    constexpr int kRecW = kWsC / kCons;                  // records per wave and chunk
-    constexpr int kNKl = (kRecW + kRPI - 1) / kRPI;      // loads per wave and chunk
-    struct KlRaw {
-        uint4 v[kNKl];
-    };
-    const int ksub = lane % kLPR;
-    auto kl_load = [&](int64_t chunk, int ws, KlRaw& K) {
-#pragma unroll
-        for (int i = 0; i < kNKl; i++) {
-            const int rr = min(lane / kLPR + kRPI * i, kRecW - 1);
-            const int64_t idx = chunk * kWsC + ws * kRecW + rr;
-            const int64_t ci = idx < n ? idx : n - 1;  // a valid row (n >= 1)
-            const uint32_t off =
-                ((uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h) * (uint32_t)(CK * 2) + (uint32_t)(ksub * 16);
-            K.v[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(gk) + off);
-        }
-    };
-    auto kl_norm = [&](int64_t chunk, int ws, const KlRaw& K, bool to_ring) {
-#pragma unroll
-        for (int i = 0; i < kNKl; i++) {
-            const uint32_t w4[4] = {K.v[i].x, K.v[i].y, K.v[i].z, K.v[i].w};
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                x[2 * e] = __uint_as_float(w4[e] << 16);
-                x[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-            }
-            float m = x[0];
-#pragma unroll
-            for (int j = 1; j < 8; j++) m = fmaxf(m, x[j]);
-            m = row_reduce<kLPR>(m, [](float u, float v) { return fmaxf(u, v); });
-            const float m2 = m * kLog2e;
-            float sum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; j++) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
-            sum = row_reduce<kLPR>(sum, [](float u, float v) { return u + v; });
-            const float l2 = m2 + __builtin_amdgcn_logf(sum);  // sum >= 1
-            const int rr = lane / kLPR + kRPI * i;
-            if (ksub == 0 && rr < kRecW) {
-                const int r = ws * kRecW + rr;
-                const int64_t idx = chunk * kWsC + r;
-                const bool valid = idx < n;
-                if (to_ring) sm.mcr[chunk % kRing][r] = valid ? l2 : INFINITY;
-                if (valid) a.lnz2_out[(lo + idx) * H + h] = l2;
-            }
-        }
-    };
-    if constexpr (kLocal) {
-        if (last_piece) {
-            // the last piece's local state is never used: only its
-            // normalisers are needed (all eight waves, four chunks per batch)
-            const int ws = wv % kCons;
-            for (int64_t c0 = wv / kCons; c0 < nchunks; c0 += 8) {
-                KlRaw K[4];
-#pragma unroll
-                for (int u = 0; u < 4; u++) kl_load(c0 + 2 * u, ws, K[u]);
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    if (c0 + 2 * u < nchunks) kl_norm(c0 + 2 * u, ws, K[u], false);
-            }
-            return;
-        }
-    }
 
     // ---------------- producer: row loads ----------------
     // lane = (group cg of 4 columns, group gk of RPG consecutive records)
@@ -345,8 +270,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             const uint32_t off = rowq[i] + (uint32_t)(j0 * 2);
             if (part == 0) R.l[i].load(rsl, off);
             if (part == 1) R.k[i].load(rsk, off);
-            if constexpr (!kLocal)
-                if (part == 2) R.q[i].load(rsq, off);
+            if (part == 2) R.q[i].load(rsq, off);
         }
     };
     auto raw_load = [&](Raw& R) {
@@ -413,7 +337,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     };
 
     // ---------------- producer: preparation of one chunk ----------------
-    float btot[kPC] = {0.f, 0.f, 0.f, 0.f};
     // hook(k), k = 0..3, is called at four points spread over the
     // preparation, so the next chunk's row loads issue between its phases
     // instead of in one burst after the barrier
@@ -436,7 +359,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         for (int e = 0; e < kPC; e++) {
             excl[e] = incl[e] - run[e];
             ebc_own[e] = __builtin_amdgcn_exp2f(tot[e]);
-            if constexpr (kLocal) btot[e] += tot[e];
         }
         hook(2);
         uint2 pk[RPG][kL];
@@ -448,18 +370,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
                 const float b = bb[i][e] + excl[e];
-                if constexpr (!kLocal) xq[e] = R.q[i].get(e) * __builtin_amdgcn_exp2f(b);
+                xq[e] = R.q[i].get(e) * __builtin_amdgcn_exp2f(b);
                 xk[e] = __builtin_amdgcn_exp2f(fmaf(R.k[i].get(e), kLog2e, -cr) - b);
             }
             split4<kL>(xk, pk[i]);
-            if constexpr (!kLocal) {
-                uint2 pq[kL];
-                split4<kL>(xq, pq);
+            uint2 pq[kL];
+            split4<kL>(xq, pq);
 #pragma unroll
-                for (int l = 0; l < kL; l++) {
-                    *reinterpret_cast<uint2*>(&st.q[l][r0 + i][jp]) = pq[l];
-                    *reinterpret_cast<uint2*>(&st.kr[l][r0 + i][jp]) = pk[i][l];
-                }
+            for (int l = 0; l < kL; l++) {
+                *reinterpret_cast<uint2*>(&st.q[l][r0 + i][jp]) = pq[l];
+                *reinterpret_cast<uint2*>(&st.kr[l][r0 + i][jp]) = pk[i][l];
             }
         }
         hook(3);
@@ -521,8 +441,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     // The decay diag(exp(b_C)) of a chunk is applied lazily: between
     // iterations S holds S_in + Kh^T V of the last chunk, and the readout
     // steps of the next chunk scale each group of 8 state registers just
-    // before splitting them (the local-state pass, which has no readout,
-    // scales the whole state before its first update).
+    // before splitting them.
     // The LDS operands of step s+2 are read while step s runs (three register
     // slots) and scheduling fences keep that order, so LDS latency hides
     // behind the MFMA pipeline.
@@ -680,31 +599,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         a.part_scale[srow * (uint32_t)(DV / 32) + (uint32_t)wv] = r.step;
     };
     constexpr int kPre = 2;  // slots per record prefetched before the shared outputs
-    auto decay = [&](f32x16& Srt, const float4 (&e4)[4]) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            Srt[4 * q4 + 0] *= e4[q4].x;
-            Srt[4 * q4 + 1] *= e4[q4].y;
-            Srt[4 * q4 + 2] *= e4[q4].z;
-            Srt[4 * q4 + 3] *= e4[q4].w;
-        }
-    };
-
     // Iteration nn (PREV: finish chunk nn-1; CUR: run chunk nn).  Op holds
     // the readout of chunk nn-1 and Vp its V operand; Oc and Vc receive those
     // of chunk nn.
     auto iteration = [&](auto prevI, auto curI, int64_t nn, f32x16& Op, u16x8(&Vp)[2], f32x16& Oc,
-                         u16x8(&Vc)[2], KlRaw& Kl, const KlRaw& Kn) {
+                         u16x8(&Vc)[2]) {
         constexpr bool HASPREV = decltype(prevI)::value;   // S holds chunk nn-1 undecayed
-        constexpr bool PREV = HASPREV && !kLocal;
+        constexpr bool PREV = HASPREV;
         constexpr bool CUR = decltype(curI)::value;
         const auto& st = sm.st[nn & 1];
-        if constexpr (kLocal) {
-            // key normalisers: load chunk nn+4, finish chunk nn+3 (loaded
-            // one iteration ago)
-            kl_load(nn + 4, wv, Kl);
-            kl_norm(nn + 3, wv, Kn, true);
-        }
         u16x8 ob[3][4];
         float4 mw4[4];
         uint32_t orow[2][2];
@@ -717,7 +620,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             if (!col_wave) return;
             // the shared pass needs the output rows early, for its slot loads
             if constexpr (s == sF && PREV && MODE == kModeShared) out_rows(nn - 1, orow, oval);
-            if constexpr (CUR && s == (kLocal ? sU : sR)) {
+            if constexpr (CUR && s == sR) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) Vc[ks] = lds8(&st.vt[col][swz(col, 16 * ks + 8 * hh)]);
             }
@@ -761,18 +664,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                 mma32_terms<kL, kL>(qa, sb, Oc);
             } else {
                 constexpr int u = s - sU, rt = u / 2, ks = u % 2;
-                if constexpr (kLocal && HASPREV && u == 0) {
-                    // no readout in this mode: apply the previous chunk's decay here
-                    const float* d = sm.ebc[(nn + 2) % 3];
-#pragma unroll
-                    for (int r2 = 0; r2 < RT_N; r2++) {
-                        float4 e4[4];
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; q4++)
-                            e4[q4] = *reinterpret_cast<const float4*>(&d[32 * r2 + 8 * q4 + 4 * hh]);
-                        decay(S[r2], e4);
-                    }
-                }
                 const u16x8 ka[kL] = {o[0], o[1]};
                 const u16x8 vb[1] = {Vc[ks]};
                 mma32_terms<kL, 1>(ka, vb, S[rt]);
@@ -830,7 +721,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             }
             if constexpr (PREV && CUR && MODE == kModeShared && s == sEnd - 1)
                 if (col_wave) shared_store();
-            if constexpr (CUR && !kLocal && s == sR) {
+            if constexpr (CUR && s == sR) {
                 // causal mask, bf16 terms, store of this wave's A tile
                 const int r = 16 * rT + l16, s0 = 16 * sT + 4 * g16;
                 if (sT == rT) {
@@ -848,7 +739,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         };
         // Steps first .. last run in order (all of them enabled); the
         // operands of step s+2 are read after step s is issued.
-        constexpr int first = PREV ? sF : (kLocal ? sU : sA);
+        constexpr int first = PREV ? sF : sA;
         constexpr int last = CUR ? sEnd - 1 : sF;
         static_for<first, (first + 2 <= last + 1 ? first + 2 : last + 1)>([&](auto sI) {
             constexpr int s = decltype(sI)::value;
@@ -930,17 +821,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             if (nn <= nchunks) step(nn, R0, R1, M0, M2);
             if (nn + 1 <= nchunks) step(nn + 1, R1, R2, M1, M0);
         } else {
-            // local pass: the normalisers of chunks 0 and 1 are in the ring
-            // before the producers' first read of it (after the first
-            // barrier), chunk 2's before the second; chunk 3 is loaded
-            KlRaw K0, K1;
-            if constexpr (kLocal) {
-                kl_load(0, wv, K0);
-                kl_load(1, wv, K1);
-                kl_norm(0, wv, K0, true);
-                kl_norm(1, wv, K1, true);
-            }
-            if (!kLocal && wv == 3) {
+            if (wv == 3) {
                 // the zero (r-tile 0, s-tile 1) block of A in both buffers
                 for (int i = lane; i < 2 * kL * 16; i += kWave) {
                     const int b = i / (kL * 16), l = (i / 16) % kL, r = i % 16;
@@ -948,12 +829,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                     *reinterpret_cast<uint4*>(&sm.a[b][l][r][24]) = make_uint4(0, 0, 0, 0);
                 }
             }
+            // the producers' two prologue barriers
             lds_barrier();
-            if constexpr (kLocal) {
-                kl_load(2, wv, K0);
-                kl_load(3, wv, K1);
-                kl_norm(2, wv, K0, true);
-            }
             lds_barrier();
             // iteration 0 runs chunk 0; iterations 1 .. nchunks-1 finish the
             // previous chunk and run the next (unrolled by two so the readout
@@ -963,23 +840,21 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             using F_ = std::false_type;
             f32x16 O0, O1;
             u16x8 V0[2], V1[2];
-            // (iteration nn loads normaliser rows into K[nn % 2] and finishes
-            // the chunk held in K[(nn + 1) % 2])
-            iteration(F_{}, T_{}, 0, O1, V1, O0, V0, K0, K1);
+            iteration(F_{}, T_{}, 0, O1, V1, O0, V0);
             lds_barrier();
             int64_t nn = 1;
             for (; nn + 1 < nchunks; nn += 2) {
-                iteration(T_{}, T_{}, nn, O0, V0, O1, V1, K1, K0);
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
                 lds_barrier();
-                iteration(T_{}, T_{}, nn + 1, O1, V1, O0, V0, K0, K1);
+                iteration(T_{}, T_{}, nn + 1, O1, V1, O0, V0);
                 lds_barrier();
             }
             if (nn < nchunks) {
-                iteration(T_{}, T_{}, nn, O0, V0, O1, V1, K1, K0);
+                iteration(T_{}, T_{}, nn, O0, V0, O1, V1);
                 lds_barrier();
-                iteration(T_{}, F_{}, nn + 1, O1, V1, O0, V0, K0, K1);
+                iteration(T_{}, F_{}, nn + 1, O1, V1, O0, V0);
             } else {
-                iteration(T_{}, F_{}, nn, O0, V0, O1, V1, K1, K0);
+                iteration(T_{}, F_{}, nn, O0, V0, O1, V1);
             }
             lds_barrier();
         }
@@ -994,22 +869,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 #pragma unroll
             for (int i = 0; i < 16; i++) S[rt][i] *= d[32 * rt + 8 * (i / 4) + 4 * hh + (i % 4)];
     }
-    if constexpr (kLocal) {
-        // local state and decay product of this piece
-        if (col_wave) {
-#pragma unroll
-            for (int rt = 0; rt < RT_N; rt++)
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
-                    a.agg_S[((abase + piece) * CK + row) * DV + col] = S[rt][i];
-                }
-        }
-        if (producer && gk_ == 0)
-#pragma unroll
-            for (int e = 0; e < kPC; e++)
-                a.agg_D[(abase + piece) * CK + j0 + e] = __builtin_amdgcn_exp2f(btot[e]);
-    } else if (col_wave && last_piece) {
+    if (col_wave && last_piece) {
 #pragma unroll
         for (int rt = 0; rt < RT_N; rt++)
 #pragma unroll
@@ -1053,9 +913,7 @@ bool launch_ws_shape(const ChunkArgs& a, int c, int d, hipStream_t st) {
 hipError_t launch_chunk_ws(int mode, const ChunkArgs& a, int c, int d, hipStream_t st) {
     if ((int64_t)a.num_seqs * a.H == 0) return hipSuccess;
     bool ok = false;
-    if (mode == kModeLocal)
-        ok = launch_ws_shape<kModeLocal>(a, c, d, st);
-    else if (mode == kModeShared)
+    if (mode == kModeShared)
         ok = launch_ws_shape<kModeShared>(a, c, d, st);
     else if (mode == kModeRouted)
         ok = launch_ws_shape<kModeRouted>(a, c, d, st);

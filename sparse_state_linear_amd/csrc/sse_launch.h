@@ -81,6 +81,9 @@ int chunk_piece_len(int dtype);
 int chunk_max_pieces(int max_seqlen, int dtype);
 
 hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+// bf16 inputs: key-softmax normalisers of every token and the shared
+// partition's piece states (piece_state.hip).
+hipError_t launch_piece_state(const ChunkArgs& a, int c, int d, hipStream_t st);
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 
