@@ -115,6 +115,17 @@ __device__ __forceinline__ void store_run(uint16_t* p, const uint16_t (&v)[R]) {
 __device__ __forceinline__ u16x8 lds8(const uint16_t* p) {
     return *reinterpret_cast<const u16x8*>(p);
 }
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): in each 16-lane group,
+// lane i = 4b + k receives element k of the 8 bytes addressed by lanes
+// 4e + b of the group, e = 0..3 (layout measured on the hardware).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+__device__ __forceinline__ u16x8 cat_tr(const s16x4& a, const s16x4& b) {
+    return __builtin_bit_cast(u16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 __device__ __forceinline__ u16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) {
     const u16x4 a = *reinterpret_cast<const u16x4*>(p0);
     const u16x4 b = *reinterpret_cast<const u16x4*>(p1);

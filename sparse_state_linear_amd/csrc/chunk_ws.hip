@@ -31,11 +31,9 @@
 //     are stored in the order 0,2,1,3, so the 8 columns a lane needs as the
 //     MFMA partner of the state registers (rows 4h..4h+3 and 8+4h..8+4h+3 of
 //     each 16) are contiguous.
-//   Kh^T [j][s] and V^T [col][s], 80-byte rows: the four 8-record blocks of
-//     a row are permuted by XOR with (j >> 2) ^ (j >> 4).  The producers'
-//     transposed 8-byte stores (rows 4 apart) then spread over all banks, and
-//     of the layouts measured on gfx950 this one also costs the consumers'
-//     32-row 16-byte reads the fewest bank conflicts.
+//   Kh and V record-major as well (no transposed copies): the operands of
+//     S += Kh^T V and O += A V, whose contraction runs over records, come from
+//     8-byte LDS transpose reads (row stride and swizzle: rm_stride, rm_swz).
 #include "chunk_common.h"
 
 namespace sse {
@@ -53,14 +51,33 @@ constexpr uint32_t kPadOff = 0x80000000u;  // row offset of padded records: past
 
 static_assert(kProd == kNW, "the preparation layout assumes four producer waves");
 
+// Record-major tiles read by 8-byte transpose reads (Kh, V): row stride in
+// elements, and the column swizzle of record r.  With 64 or more columns the
+// stride is 64 or 192 bytes modulo 256 and columns are XORed with 48 when
+// bit 2 xor bit 3 of r is set: the transpose reads (4 records x 64 bytes per
+// half-wave), the producers' 8-byte stores (2 records 4 apart x 64 bytes per
+// 16 lanes) and Kh's 16-byte A-tile reads (16 records x 32 bytes per
+// half-wave) then all hit distinct banks (found by exhaustive search over
+// strides and XOR-linear swizzles under the measured bank rules).  32-column
+// tiles have no such layout and keep a padded stride.  The swizzled
+// addresses of the two transpose reads of an operand differ per lane, which
+// costs registers: the routed pass uses the swizzle, the shared pass (which
+// would spill with it) keeps plain rows, conflict-free for its transpose
+// reads and 2-way for the A-tile reads and the stores (measured on gfx950:
+// routed 446 -> 429 us with the swizzle; shared 316 us with it, 261 without).
+constexpr int rm_stride(int cols) { return cols >= 64 ? cols + 32 : cols + 8; }
+template <int COLS, bool SWZ>
+__device__ __forceinline__ int rm_swz(int r) {
+    return (SWZ && COLS >= 64) ? 48 * (((r >> 2) ^ (r >> 3)) & 1) : 0;
+}
+
 template <int CK, int DV>
 struct WsStage {
     static constexpr int QS = CK + 8;
-    static constexpr int TS = kWsC + 8;
+    static constexpr int KS = rm_stride(CK), VS = rm_stride(DV);
     uint16_t q[kL][kWsC][QS];     // Qt terms [r][perm(j)]
-    uint16_t kr[kL][kWsC][QS];    // Kh terms [s][perm(j)]
-    uint16_t kt[kL][CK][TS];      // Kh terms [j][swz(j, s)]
-    uint16_t vt[DV][TS];          // V (exact in bf16) [col][swz(col, s)]
+    uint16_t kr[kL][kWsC][KS];    // Kh terms [s][perm(j) ^ rm_swz(s)] (see rm_swz)
+    uint16_t v[kWsC][VS];         // V (exact in bf16) [s][col ^ rm_swz(s)]
 };
 
 template <int CK, int DV>
@@ -84,11 +101,6 @@ __device__ __forceinline__ int perm_col(int j) {
     const int b = (j >> 2) & 3;
     return (j & ~15) | ((((b & 1) << 1) | (b >> 1)) << 2);
 }
-// Storage position of record s in row `row` of Kh^T / V^T.
-__device__ __forceinline__ int swz(int row, int s) {
-    return ((((s >> 3) ^ (row >> 2) ^ (row >> 4)) & 3) << 3) | (s & 7);
-}
-
 struct Meta {
     uint32_t row, orow;  // input row t*H + h; output row (slot row or o row)
     float cr, w;
@@ -102,6 +114,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     using GK = Geo<kWsC, CK>;
     using GV = Geo<kWsC, DV>;
     static_assert(MODE == kModeShared || MODE == kModeRouted, "routed and shared passes only");
+    constexpr bool kSwz = MODE == kModeRouted;  // record-major tile swizzle (rm_swz)
     constexpr int NS = DV / 32;       // consumer waves that own state columns
     constexpr int RT_N = CK / 32;     // 32-row tiles of the state
     constexpr int RPG = GK::RPG, RPGV = GV::RPG;
@@ -379,46 +392,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 #pragma unroll
             for (int l = 0; l < kL; l++) {
                 *reinterpret_cast<uint2*>(&st.q[l][r0 + i][jp]) = pq[l];
-                *reinterpret_cast<uint2*>(&st.kr[l][r0 + i][jp]) = pk[i][l];
+                *reinterpret_cast<uint2*>(&st.kr[l][r0 + i][jp ^ rm_swz<CK, kSwz>(r0 + i)]) = pk[i][l];
             }
         }
         hook(3);
-        // Kh^T and V^T: the lane's records of each of its 4 columns, two
-        // records per 32-bit word (one byte permutation per word)
-        auto pair = [](uint32_t w_lo, uint32_t w_hi, int e) {
-            // 16-bit element e%2 of w_lo and of w_hi -> low / high half
-            return __builtin_amdgcn_perm(w_hi, w_lo, (e & 1) ? 0x07060302u : 0x05040100u);
-        };
+        // V rows as loaded (record-major, 4 columns per store)
 #pragma unroll
-        for (int e = 0; e < kPC; e++)
-#pragma unroll
-            for (int l = 0; l < kL; l++) {
-                if constexpr (RPG == 4) {
-                    const uint32_t w0 = (e < 2) ? pk[0][l].x : pk[0][l].y, w1 = (e < 2) ? pk[1][l].x : pk[1][l].y;
-                    const uint32_t w2 = (e < 2) ? pk[2][l].x : pk[2][l].y, w3 = (e < 2) ? pk[3][l].x : pk[3][l].y;
-                    *reinterpret_cast<uint2*>(&st.kt[l][j0 + e][swz(j0 + e, r0)]) =
-                        make_uint2(pair(w0, w1, e), pair(w2, w3, e));
-                } else {
-                    uint16_t rr[RPG];
-#pragma unroll
-                    for (int i = 0; i < RPG; i++) rr[i] = elem(pk[i][l], e);
-                    store_run<RPG>(&st.kt[l][j0 + e][swz(j0 + e, r0)], rr);
-                }
-            }
-#pragma unroll
-        for (int e = 0; e < kPC; e++) {
-            if constexpr (RPGV == 4) {
-                const uint32_t w0 = (e < 2) ? R.v[0].u.x : R.v[0].u.y, w1 = (e < 2) ? R.v[1].u.x : R.v[1].u.y;
-                const uint32_t w2 = (e < 2) ? R.v[2].u.x : R.v[2].u.y, w3 = (e < 2) ? R.v[3].u.x : R.v[3].u.y;
-                *reinterpret_cast<uint2*>(&st.vt[c0v + e][swz(c0v + e, r0v)]) =
-                    make_uint2(pair(w0, w1, e), pair(w2, w3, e));
-            } else {
-                uint16_t rr[RPGV];
-#pragma unroll
-                for (int i = 0; i < RPGV; i++) rr[i] = R.v[i].bits(e);
-                store_run<RPGV>(&st.vt[c0v + e][swz(c0v + e, r0v)], rr);
-            }
-        }
+        for (int i = 0; i < RPGV; i++)
+            *reinterpret_cast<uint2*>(&st.v[r0v + i][c0v ^ rm_swz<DV, kSwz>(r0v + i)]) = R.v[i].u;
         if (gk_ == 0)
 #pragma unroll
             for (int e = 0; e < kPC; e++) sm.ebc[chunk % 3][j0 + e] = ebc_own[e];
@@ -452,6 +433,25 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     constexpr int sOut = sA + (nA > 1 ? 1 : 0);   // outputs of chunk nn-1 after this step
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
+    // 32x32x16 MFMA operand over records from a record-major tile: lane l
+    // gets records rec0 + 8 (l / 32) + 0..7 of column col0 + l % 32.  Source
+    // lane (g, 4e + b) of each 16-lane group addresses the 4-column block
+    // col0 + 16 (g % 2) + 4 b of record rec0 + 8 (g / 2) + e (+ 4).
+    const int trg = lane / 16, trj = lane % 16;
+    const int tr_rec = 8 * (trg / 2) + trj / 4, tr_col = 16 * (trg % 2) + 4 * (trj % 4);
+    auto tr_kh = [&](const uint16_t* tile, int rec0, int col0) {   // Kh^T (A operand)
+        constexpr int KS = WsStage<CK, DV>::KS;
+        const int r = rec0 + tr_rec, c = perm_col(col0 + tr_col);
+        return cat_tr(lds_tr(tile + r * KS + (c ^ rm_swz<CK, kSwz>(r))),
+                      lds_tr(tile + (r + 4) * KS + (c ^ rm_swz<CK, kSwz>(r + 4))));
+    };
+    auto tr_v = [&](const uint16_t* tile, int rec0, int col0) {    // V (B operand)
+        constexpr int VS = WsStage<CK, DV>::VS;
+        const int r = rec0 + tr_rec, c = col0 + tr_col;
+        return cat_tr(lds_tr(tile + r * VS + (c ^ rm_swz<DV, kSwz>(r))),
+                      lds_tr(tile + (r + 4) * VS + (c ^ rm_swz<DV, kSwz>(r + 4))));
+    };
+
     // operands of step s of iteration nn
     auto fetch = [&](auto sI, int64_t nn, u16x8(&o)[4]) {
         constexpr int s = decltype(sI)::value;
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             constexpr int kk = s - sA;
 #pragma unroll
             for (int l = 0; l < kL; l++) {
-                o[l] = lds8(&st.kr[l][16 * sT + l16][32 * kk + 8 * g16]);
+                o[l] = lds8(&st.kr[l][16 * sT + l16][(32 * kk + 8 * g16) ^ rm_swz<CK, kSwz>(16 * sT + l16)]);
                 o[2 + l] = lds8(&st.q[l][16 * rT + l16][32 * kk + 8 * g16]);
             }
         } else if constexpr (s < sU) {
@@ -480,9 +480,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             o[3] = *reinterpret_cast<const u16x8*>(&d[16 * kk + 8 + 4 * hh]);
         } else {
             constexpr int u = s - sU, rt = u / 2, ks = u % 2;
-            const int j = 32 * rt + l32;
 #pragma unroll
-            for (int l = 0; l < kL; l++) o[l] = lds8(&st.kt[l][j][swz(j, 16 * ks + 8 * hh)]);
+            for (int l = 0; l < kL; l++) o[l] = tr_kh(&st.kr[l][0][0], 16 * ks, 32 * rt);
         }
     };
 
@@ -622,7 +621,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             if constexpr (s == sF && PREV && MODE == kModeShared) out_rows(nn - 1, orow, oval);
             if constexpr (CUR && s == sR) {
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) Vc[ks] = lds8(&st.vt[col][swz(col, 16 * ks + 8 * hh)]);
+                for (int ks = 0; ks < 2; ks++) Vc[ks] = tr_v(&st.v[0][0], 16 * ks, 32 * wv);
             }
         };
         auto compute = [&](auto sI, const u16x8(&o)[4]) {

@@ -44,8 +44,6 @@ constexpr int kDepth = 2;   // steps whose row loads are in flight (2, 4 and 8 m
 static_assert(SSE_SHARED_PIECE % (kPsRec * kDepth) == 0, "pieces must be whole groups of steps");
 static_assert(kDepth % 2 == 0, "stage i % 2 must be static inside the unrolled step loop");
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 // Row stride (elements) of an LDS stage row of `cols` bf16 values.  The
 // transpose reads of a half-wave touch 4 records x 64 bytes; a stride of
 // 64 or 192 bytes modulo 256 puts those four 64-byte pieces on disjoint
@@ -60,13 +58,6 @@ struct PsStage {
     float lnz2[kPsRec];
 };
 
-// Transpose read: 16-lane group g, lane i = 4b + k receives element k of the
-// 8 bytes addressed by lanes 4e + b of its group, e = 0..3.
-__device__ __forceinline__ s16x4 lds_tr(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(p));
-}
-
 // The 8 values (records 8 (lane/32) + 0..7, column col0 + lane % 32) of a
 // 32x32x16 MFMA operand from a record-major LDS tile [16][stride].
 template <int STRIDE>
@@ -74,18 +65,7 @@ __device__ __forceinline__ u16x8 tr_operand(const uint16_t* tile, int col0, int 
     const int g = lane / 16, jj = lane % 16;
     const int rec = 8 * (g / 2) + jj / 4;
     const int col = col0 + 16 * (g % 2) + 4 * (jj % 4);
-    const s16x4 a = lds_tr(tile + rec * STRIDE + col);
-    const s16x4 b = lds_tr(tile + (rec + 4) * STRIDE + col);
-    u16x8 r;
-    r[0] = (uint16_t)a[0];
-    r[1] = (uint16_t)a[1];
-    r[2] = (uint16_t)a[2];
-    r[3] = (uint16_t)a[3];
-    r[4] = (uint16_t)b[0];
-    r[5] = (uint16_t)b[1];
-    r[6] = (uint16_t)b[2];
-    r[7] = (uint16_t)b[3];
-    return r;
+    return cat_tr(lds_tr(tile + rec * STRIDE + col), lds_tr(tile + (rec + 4) * STRIDE + col));
 }
 
 template <int CK, int DV>
