@@ -190,17 +190,25 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                     S[rt][i] = a.init[sbase + (int64_t)row * DV + col];
                 }
         }
-        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the piece-state pass
+        // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the piece-state pass,
+        // whose piece states are stored fragment-major (the 16 values of
+        // this lane's 32x32 tile (rt, wv) contiguous: 16-byte loads)
         for (int p = 0; p < piece; p++) {
             const int64_t ab = abase + p;
 #pragma unroll
-            for (int rt = 0; rt < RT_N; rt++)
+            for (int rt = 0; rt < RT_N; rt++) {
+                const float4* fs = reinterpret_cast<const float4*>(
+                    a.agg_S + (((ab * RT_N + rt) * NS + wv) * kWave + lane) * 16);
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = 32 * rt + 8 * (i / 4) + 4 * hh + (i % 4);
-                    S[rt][i] = a.agg_D[ab * CK + row] * S[rt][i] +
-                               a.agg_S[(ab * CK + row) * DV + col];
+                for (int q4 = 0; q4 < 4; q4++) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(&a.agg_D[ab * CK + 32 * rt + 8 * q4 + 4 * hh]);
+                    const float4 s4 = fs[q4];
+                    S[rt][4 * q4 + 0] = d4.x * S[rt][4 * q4 + 0] + s4.x;
+                    S[rt][4 * q4 + 1] = d4.y * S[rt][4 * q4 + 1] + s4.y;
+                    S[rt][4 * q4 + 2] = d4.z * S[rt][4 * q4 + 2] + s4.z;
+                    S[rt][4 * q4 + 3] = d4.w * S[rt][4 * q4 + 3] + s4.w;
                 }
+            }
         }
     }
 

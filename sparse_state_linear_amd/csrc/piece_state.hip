@@ -244,17 +244,17 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     for (int r = tid; r < n; r += kPsThreads) a.lnz2_out[(lo + r) * H + h] = lnz_all[r];
     if (!state) return;
 
-    // ---- the piece's state and total decay
+    // ---- the piece's state (fragment-major: tile (rt, ct) of the piece,
+    //      lane, its 16 accumulator values) and total decay
     const int64_t ab = ((int64_t)s * H + h) * a.max_pieces + piece;
 #pragma unroll
     for (int u = 0; u < NT; u++) {
         const int ct = ct0 + WPR * u;
         if (ct < CT) {
+            float4* fs = reinterpret_cast<float4*>(a.agg_S + (((ab * RT + rt) * CT + ct) * kWave + lane) * 16);
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int row = 32 * rt + 8 * (e / 4) + 4 * half + (e % 4);
-                a.agg_S[(ab * CK + row) * DV + 32 * ct + lane % 32] = acc[u][e];
-            }
+            for (int q4 = 0; q4 < 4; q4++)
+                fs[q4] = make_float4(acc[u][4 * q4], acc[u][4 * q4 + 1], acc[u][4 * q4 + 2], acc[u][4 * q4 + 3]);
         }
     }
     if (ct0 == 0 && half == 0) a.agg_D[ab * CK + j] = __builtin_amdgcn_exp2f(carry * kLog2e);

@@ -62,7 +62,9 @@ struct ChunkArgs {
     const float* init;           // [S, H, N+1, c, d] or null
     float* o;
     float* final_states;
-    float* agg_S;                // [S*H, max_pieces, c, d] local piece states
+    float* agg_S;                // local piece states, [S*H, max_pieces] of c x d: row-major
+                                 // for fp32 inputs; for bf16 inputs fragment-major
+                                 // [c/32][d/32][64 lanes][16] (32x32 MFMA accumulator tiles)
     float* agg_D;                // [S*H, max_pieces, c] piece decay products
     float* trash;                // one dummy output row for padded records
     float* part;                 // [T, H, topk, d] e-gated routed reads (routed

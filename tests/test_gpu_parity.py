@@ -90,6 +90,18 @@ def test_bf16_other_shapes(c, d):
     _check_full(w, [300, 5, 128], seed=12)
 
 
+@pytest.mark.parametrize("c,d", [(32, 64), (64, 128), (128, 32), (128, 128)])
+def test_multi_piece_with_initial_states(c, d):
+    """Sequences longer than the shared partition's 1024-token pieces (state
+    pieces combined with random initial states), lengths at and just past a
+    piece boundary, a 3-token and an empty sequence; every element checked."""
+    w = si.Workload(f"pieces_{c}x{d}", "bf16", H=2, c=c, d=d, N=8, topk=2)
+    lengths = [2100, 1024, 1025, 3, 0]
+    rng = np.random.default_rng(41)
+    init = (0.5 * rng.standard_normal((len(lengths), w.H, w.N + 1, c, d))).astype(np.float32)
+    _check_full(w, lengths, seed=40, init=init, tag=w.name)
+
+
 def test_initial_states_and_unselected_partition():
     """Random initial states; partition 7 is never chosen (its logit is the
     row minimum), so its final state must equal its initial state byte for
