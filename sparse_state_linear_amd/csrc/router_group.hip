@@ -6,15 +6,18 @@
 // sample and partition, time order kept, new segment offsets).
 //
 // Grouping is a stable counting sort done in three launches:
-//   route_count  one block per (sequence, 64-token block), all heads: routes
-//                the block's rows (one lane per row), then one wave per head
+//   route_count  one block per (sequence, 64-token block, group of 4
+//                heads): routes the block's rows (one lane per row; more
+//                blocks with shorter chains measured faster than one block
+//                for all heads of a token block), then one wave per head
 //                (lane = token) ranks every record among the block's records
 //                of its partition with wave ballots (time order kept), writes
 //                the per-(head, partition) block counts and a head-major
 //                (partition, rank, weight) record per routed token; for fp32
 //                inputs it also stores the log2 normaliser of each row's key
 //                softmax (section 2.3, eq. 11; 16 lanes per row, coalesced
-//                16-byte loads) so that later passes need no row reduction;
+//                16-byte loads; the first head group's block does all heads)
+//                so that later passes need no row reduction;
 //   block_scan   one block per (sequence, head): exclusive scan over its
 //                N x blocks counts.  The records of (s, h) occupy a known
 //                contiguous range (every token contributes exactly k
@@ -153,7 +156,7 @@ __device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
 // sum_j 2^((kl_j - m) log2 e) plus m log2 e, so that kappa_j =
 // 2^(kl_j log2 e - lnz2); the key normaliser spreads each row over CK/8
 // (bf16) or CK/4 (fp32) lanes.
-constexpr int kHG = 16;  // heads per routing group
+constexpr int kHG = 4;  // heads per block (one wave per head in the ranking phase)
 template <int NMAX, int CK, typename TIn>
 __global__ __launch_bounds__(256) void route_count_kernel(
     const TIn* __restrict__ z, const TIn* __restrict__ kl, const int32_t* __restrict__ cu,
@@ -161,13 +164,15 @@ __global__ __launch_bounds__(256) void route_count_kernel(
     int32_t* __restrict__ counts, uint2* __restrict__ rinfo, float* __restrict__ lnz2) {
     extern __shared__ float swt[];  // [kHG][kTokBlock][K] weights, then the choices as bytes
     uint8_t* ssel = reinterpret_cast<uint8_t*>(swt + kHG * kTokBlock * K);
-    const int blk = blockIdx.x, s = blockIdx.y;
+    const int blk = blockIdx.x, s = blockIdx.y, hgb = blockIdx.z * kHG;  // this block's heads
     const int64_t t1 = cu[s + 1];
     const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
     const int ntok = (int)(t1 - tb < 0 ? 0 : (t1 - tb > kTokBlock ? kTokBlock : t1 - tb));
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
-    constexpr int kRB = 4;  // rows per thread and batch, loaded before any is routed
-    for (int hg0 = 0; hg0 < H; hg0 += kHG) {
+    // rows per thread and batch, loaded before any is routed (one with 256
+    // threads for 64 tokens x 4 heads)
+    constexpr int kRB = (kTokBlock * kHG + 255) / 256;
+    for (int hg0 = hgb; hg0 < hgb + kHG && hg0 < H; hg0 += kHG) {
         const int hgc = H - hg0 < kHG ? H - hg0 : kHG;
         const int rows = ntok * hgc;
         for (int rb = threadIdx.x; rb < rows; rb += kRB * (int)blockDim.x) {
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(256) void route_count_kernel(
         }
         __syncthreads();
     }
-    if (lnz2) {
+    if (lnz2 && blockIdx.z == 0) {  // fp32 inputs: the normalisers of all heads' rows
         const int64_t r0 = tb * H, r1 = ntok > 0 ? (tb + ntok) * H : r0;  // rows [r0, r1)
         constexpr int VPL = 16 / (int)sizeof(TIn);  // values per lane
         constexpr int LPR = CK / VPL;                // lanes per row
@@ -485,7 +490,7 @@ static hipError_t launch_route_count_t(const void* z, const void* kl, const int3
     const int nblk = group_nblk(max_seqlen);
     if ((int64_t)num_seqs * H == 0) return hipSuccess;
     if (H > kMaxH || N > kMaxN || K > kMaxTopK) return hipErrorInvalidValue;
-    dim3 grid((unsigned)nblk, (unsigned)num_seqs);
+    dim3 grid((unsigned)nblk, (unsigned)num_seqs, (unsigned)((H + kHG - 1) / kHG));
     const TIn* zz = static_cast<const TIn*>(z);
     const TIn* kk = static_cast<const TIn*>(kl);
     if (N <= 8)
