@@ -172,8 +172,8 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  * Stage tracing (profiling aid, not part of the method).  While enabled,
  * every sse_forward records HIP events on its stream around its five
  * stages: 0 = routing + per-block counts (+ key-softmax normalisers for fp32
- * inputs), 1 = local states of the pieces of long shared chains (+ the
- * key-softmax normalisers for bf16 inputs), 2 = grouping scan and scatter,
+ * inputs), 1 = states of the pieces of long shared chains (+ the key-softmax
+ * normalisers for bf16 inputs), 2 = grouping scan and scatter,
  * 3 = routed partitions (store their e-gated reads into the workspace
  * slots), 4 = shared partition (writes o = shared read + slots).
  * Events of the last 256 calls are kept.  Tracing assumes

@@ -213,7 +213,7 @@ def sse_group_by_partition(topk_idx, topk_w, cu_seqlens, N, max_seqlen=None):
     return off, tok, slot, sw
 
 
-TRACE_STAGES = ("route_count", "shared_local", "group", "routed", "shared")
+TRACE_STAGES = ("route_count", "piece_state", "group", "routed", "shared")
 
 
 def sse_trace_enable(enable: bool = True):
