@@ -39,7 +39,20 @@ def _run_forward(inp, w, init=None, max_seqlen=None):
     return o.cpu().numpy(), fs.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()
 
 
-def _check_full(w, lengths, seed=0, init=None, tag=""):
+def _check_states_per_partition(fs, ref_fs, tol):
+    """Final states checked one partition state at a time: every
+    (sequence, head, partition) c x d state within tol of its own rms, and
+    states the oracle leaves at zero exactly zero."""
+    err = np.abs(fs - ref_fs).max(axis=(3, 4))
+    rms = np.sqrt(np.mean(ref_fs * ref_fs, axis=(3, 4)))
+    zero = rms == 0
+    assert (err[zero] == 0).all(), "a state the oracle leaves at zero is not zero"
+    worst = float((err[~zero] / rms[~zero]).max()) if (~zero).any() else 0.0
+    print(f"  worst per-partition state rel err {worst:.3e}  (tol {tol})", flush=True)
+    assert worst <= tol
+
+
+def _check_full(w, lengths, seed=0, init=None, tag="", states_per_partition=False):
     inp = si.forward_inputs(w, lengths=lengths, seed=seed)
     announce(tag or w.name, "seed", seed, "lengths", lengths, "H", w.H, "c", w.c, "d", w.d,
              "N", w.N, "k", w.topk, "sse_forward")
@@ -51,7 +64,11 @@ def _check_full(w, lengths, seed=0, init=None, tag=""):
     assert rel_err(wt, ref["topk_e"]) < 1e-5
     eo, es = rel_err(o, ref["o"]), rel_err(fs, ref["final_states"])
     print(f"  o rel err {eo:.3e}  states rel err {es:.3e}  (tol {tol})", flush=True)
-    assert eo <= tol and es <= tol
+    assert eo <= tol
+    if states_per_partition:
+        _check_states_per_partition(fs, ref["final_states"], tol)
+    else:
+        assert es <= tol
     return inp, o, fs, ref
 
 
@@ -100,6 +117,22 @@ def test_multi_piece_with_initial_states(c, d):
     rng = np.random.default_rng(41)
     init = (0.5 * rng.standard_normal((len(lengths), w.H, w.N + 1, c, d))).astype(np.float32)
     _check_full(w, lengths, seed=40, init=init, tag=w.name)
+
+
+@pytest.mark.parametrize("dtype,N,k,H,cd", [("bf16", 64, 8, 5, 64), ("f32", 64, 8, 3, 32),
+                                           ("bf16", 1, 1, 2, 128), ("f32", 1, 1, 2, 32),
+                                           ("bf16", 6, 6, 5, 64)])
+def test_forward_partition_extremes(dtype, N, k, H, cd):
+    """Largest router (N = 64, k = 8), the degenerate single partition
+    (N = k = 1: routed and shared states both equal the GLA state), every
+    partition selected (k = N), and head counts that leave a partial group of
+    the router's 4-head blocks; ragged lengths, every element checked.
+    With fp32 inputs and N = 64 the shared state is an order of magnitude
+    larger than the 64 routed ones (it takes every token with weight 1), so
+    its fp32 rounding alone reaches 1e-5 of the rms of the whole states
+    tensor: there the states are checked one partition state at a time."""
+    w = si.Workload(f"extreme_{dtype}_n{N}k{k}", dtype, H=H, c=cd, d=cd, N=N, topk=k)
+    _check_full(w, [300, 1, 70], seed=50 + N + k, states_per_partition=(dtype == "f32" and N > 8))
 
 
 def test_initial_states_and_unselected_partition():
@@ -245,6 +278,12 @@ def _decode_check(w, B, steps, units, seed=0):
         eo, es = rel_err(o_all[:, b, h], ro), rel_err(fs[b, h], rS)
         print(f"  decode unit b={b} h={h}: o {eo:.3e} states {es:.3e}", flush=True)
         assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("dtype,N,k,cd", [("bf16", 64, 8, 64), ("bf16", 1, 1, 128), ("f32", 64, 8, 32)])
+def test_decode_partition_extremes(dtype, N, k, cd):
+    w = si.Workload(f"decode_{dtype}_n{N}k{k}", dtype, H=3, c=cd, d=cd, N=N, topk=k, B=4, seed=0)
+    _decode_check(w, 4, 5, [(b, h) for b in range(4) for h in range(3)])
 
 
 def test_decode_small():
