@@ -72,17 +72,19 @@ def chunk_flops(records, c, d, C=64):
 
 def run_forward(args, w, si, sse, torch):
     inp = si.forward_inputs(w)
-    T = int(inp["cu_seqlens"][-1])
-    S = w.B
+    cu = inp["cu_seqlens"]
+    T = int(cu[-1])
+    S = len(cu) - 1
+    max_len = int((cu[1:] - cu[:-1]).max())
     d_in = {n: to_dev(inp[n]) for n in NAMES + ("cu_seqlens",)}
     del inp
     o = torch.empty((T, w.H, w.d), dtype=torch.float32, device="cuda")
     fs = torch.empty((S, w.H, w.N + 1, w.c, w.d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(sse.sse_forward_workspace_bytes(T, S, w.T, w.H, w.c, w.d, w.N, w.topk),
+    ws = torch.empty(sse.sse_forward_workspace_bytes(T, S, max_len, w.H, w.c, w.d, w.N, w.topk),
                      dtype=torch.uint8, device="cuda")
 
     def step():
-        sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], w.T,
+        sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], max_len,
                         o=o, final_states=fs, workspace=ws)
 
     for _ in range(args.warmup):
@@ -229,6 +231,7 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the varlen forward timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -263,6 +266,29 @@ def main():
     ff = chunk_flops(T * w.H * (w.topk + 1), w.c, w.d)
     roof_ms = max(fb / (HBM_PEAK_GBS * 1e9), ff / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     log(f"forward {ms:.3f} ms/step; stages {stages}")
+
+    varlen = None
+    if not args.no_varlen:
+        wv = si.WORKLOADS["varlen_bf16"]
+        log("forward", wv.notes)
+        Tv, Sv, v_total_ms, v_stages, _ = run_forward(args, wv, si, sse, torch)
+        v_ms = v_total_ms / args.steps
+        vb = forward_bytes(Tv, Sv, wv.H, wv.c, wv.d, wv.N)
+        vf = chunk_flops(Tv * wv.H * (wv.topk + 1), wv.c, wv.d)
+        v_roof = max(vb / (HBM_PEAK_GBS * 1e9), vf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+        varlen = {
+            "workload": "varlen_bf16: 8 packed sequences, lengths U[1024,16384] (seed 0), "
+                        "H=16, c=d=128, N=32, k=4 + shared partition, bf16 inputs",
+            "tokens": Tv,
+            "ms_per_step": v_ms,
+            "tokens_per_s": Tv / (v_ms * 1e-3),
+            "algorithmic_bytes": vb,
+            "algorithmic_flops": vf,
+            "roofline_ms": v_roof,
+            "frac": v_roof / v_ms,
+            "stage_ms": v_stages,
+        }
+        log(f"varlen forward {v_ms:.3f} ms/step ({Tv} tokens); stages {v_stages}")
 
     decode = None
     if not args.no_decode:
@@ -315,6 +341,7 @@ def main():
             "stage_ms": stages,
             "traced_calls": calls,
         },
+        "varlen_forward": varlen,
         "decode": decode,
         "cpu_baseline": cpu,
     }

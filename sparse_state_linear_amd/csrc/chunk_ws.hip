@@ -684,8 +684,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             }
         };
         // work that waits for an earlier step's MFMA results
-        // shared pass: o = shared read + the record's routed slots
-        auto shared_store = [&]() {
+        // shared pass: o = shared read + the record's routed slots.  In an
+        // iteration that also runs a chunk, slots 0 .. kPre-1 (loaded at step
+        // sF) are added at step sU and slots kPre .. 2 kPre - 1 are loaded
+        // there into the same registers, so up to 2 kPre slots arrive without
+        // a wait; further slots are loaded where they are added.
+        auto shared_store = [&](auto midI) {
+            constexpr bool MID = decltype(midI)::value;  // slots 0 .. kPre-1 already in tv
+            constexpr int j0 = MID ? kPre : 0;
 #pragma unroll
             for (int p = 0; p < 2; p++)
 #pragma unroll
@@ -693,8 +699,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                     float4 v = tv[p][h2];
 #pragma unroll
                     for (int j = 0; j < kPre; j++)
-                        if (j < a.topk) slot_add(v, pre[p][h2][j]);
-                    for (int j = kPre; j < a.topk; j++) slot_add(v, slot_ld(orow[p][h2], j));
+                        if (j0 + j < a.topk) slot_add(v, pre[p][h2][j]);
+                    for (int j = j0 + kPre; j < a.topk; j++) slot_add(v, slot_ld(orow[p][h2], j));
                     store_out(a.o, orow[p][h2], oval[p][h2], v);
                 }
         };
@@ -729,12 +735,28 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
                         }
                     } else {
                         transpose(Op, mw4, tv);
-                        if constexpr (!CUR) shared_store();
+                        if constexpr (!CUR) shared_store(std::false_type{});
                     }
                 }
             }
+            if constexpr (PREV && CUR && MODE == kModeShared && s == sU) {
+                if (col_wave) {
+#pragma unroll
+                    for (int p = 0; p < 2; p++)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; h2++) {
+#pragma unroll
+                            for (int j = 0; j < kPre; j++)
+                                if (j < a.topk) slot_add(tv[p][h2], pre[p][h2][j]);
+                            if (a.topk > kPre)
+#pragma unroll
+                                for (int j = 0; j < kPre; j++)
+                                    pre[p][h2][j] = slot_ld(orow[p][h2], kPre + j < a.topk ? kPre + j : 0);
+                        }
+                }
+            }
             if constexpr (PREV && CUR && MODE == kModeShared && s == sEnd - 1)
-                if (col_wave) shared_store();
+                if (col_wave) shared_store(std::true_type{});
             if constexpr (CUR && s == sR) {
                 // causal mask, bf16 terms, store of this wave's A tile
                 const int r = 16 * rT + l16, s0 = 16 * sT + 4 * g16;
