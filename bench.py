@@ -210,6 +210,37 @@ def measured_traffic(stage):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
+def measured_peaks(torch):
+    """Achievable rates on this GPU for scale: a 1 GiB device copy, an
+    in-place read-modify-write of 1 GiB (the decode's access type) and a
+    bf16 GEMM of 8192^3 (library MFMA code), each the best of 5."""
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+
+    def best_ms(f, reps=5):
+        f()
+        torch.cuda.synchronize()
+        out = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            out = ms if out is None else min(out, ms)
+        return out
+
+    copy = 2 * n * 4 / (best_ms(lambda: y.copy_(x)) * 1e-3) / 1e9
+    rmw = 2 * n * 4 / (best_ms(lambda: x.mul_(1.0)) * 1e-3) / 1e9
+    gemm = 2 * 8192 ** 3 / (best_ms(lambda: torch.matmul(a, b)) * 1e-3) / 1e12
+    del x, y, a, b
+    return {"copy_GBs": copy, "inplace_rmw_GBs": rmw, "bf16_gemm_TFLOPs": gemm}
+
+
 def calib_copy(torch, mib=1024, reps=3):
     """A plain device copy of known size, run under the same counters as the
     benchmark to calibrate FETCH_SIZE / WRITE_SIZE."""
@@ -232,6 +263,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the varlen forward timing")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -296,6 +328,18 @@ def main():
         decode = run_decode(args, si, sse, torch)
         log(f"decode {decode['ms_per_step'] * 1e3:.1f} us/step, {decode['achieved_GBs']:.0f} GB/s")
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks(torch)
+        # the forward's roofline time against the measured rates instead of
+        # the spec peaks
+        roof_meas_ms = max(fb / (peaks["copy_GBs"] * 1e9),
+                           ff / (peaks["bf16_gemm_TFLOPs"] * 1e12)) * 1e3
+        peaks["forward_frac"] = roof_meas_ms / ms
+        if decode is not None:
+            peaks["decode_frac"] = decode["achieved_GBs"] / peaks["inplace_rmw_GBs"]
+        log(f"measured peaks {peaks}")
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -342,6 +386,7 @@ def main():
             "traced_calls": calls,
         },
         "varlen_forward": varlen,
+        "measured_peaks": peaks,
         "decode": decode,
         "cpu_baseline": cpu,
     }
