@@ -9,8 +9,9 @@
 
 namespace sse {
 
-// Warp-specialised kernel for bf16 inputs (chunk_ws.hip); mode is one of
-// the chunk modes below.  Returns hipErrorInvalidValue for a shape it has no
+// Warp-specialised kernel for bf16 inputs (chunk_ws.hip); mode is
+// kModeShared or kModeRouted (bf16 piece states come from piece_state.hip).
+// Returns hipErrorInvalidValue for another mode or a shape it has no
 // instance for.
 hipError_t launch_chunk_ws(int mode, const ChunkArgs& a, int c, int d, hipStream_t st);
 

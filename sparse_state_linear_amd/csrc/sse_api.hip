@@ -164,13 +164,15 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.max_pieces = sse::chunk_max_pieces(max_seqlen, dtype);
 
     // 1. router + per-block counts (+ the key-softmax normaliser for fp32
-    //    inputs; for bf16 inputs the local-state pass computes it)
+    //    inputs; for bf16 inputs the piece-state pass computes it)
     trace_mark(0, s);
     hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
                                            max_seqlen, total_tokens, H, c, N, topk, idx, w,
                                            counts, rinfo, dtype == SSE_F32 ? lnz2 : nullptr, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
-    // 2. local states of the shared pieces
+    // 2. piece states of the shared partition (bf16 inputs: the piece-state
+    //    pass, which also computes the key normalisers; fp32 inputs: the
+    //    chunk kernel's local-state mode)
     trace_mark(1, s);
     e = sse::launch_chunk_local(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;

@@ -58,7 +58,7 @@ struct ChunkArgs {
     const int32_t* seg_offsets;  // routed segments
     const SegRec* seg_rec;       // routed records, segment by segment
     const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
-    float* lnz2_out;             // where the bf16 local-state pass stores lnz2
+    float* lnz2_out;             // where the bf16 piece-state pass stores lnz2
     const float* init;           // [S, H, N+1, c, d] or null
     float* o;
     float* final_states;
