@@ -169,6 +169,14 @@ __global__ __launch_bounds__(256) void route_count_kernel(
     const int64_t tb = cu[s] + (int64_t)blk * kTokBlock;
     const int ntok = (int)(t1 - tb < 0 ? 0 : (t1 - tb > kTokBlock ? kTokBlock : t1 - tb));
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    if (ntok == 0) {
+        // a block past the end of a shorter sequence: zero counts for its
+        // heads (no rows to route or rank, no normalisers)
+        const int hgc = H - hgb < kHG ? H - hgb : kHG;
+        for (int x = threadIdx.x; x < hgc * N; x += blockDim.x)
+            counts[(((int64_t)s * H + hgb + x / N) * N + x % N) * nblk + blk] = 0;
+        return;  // uniform
+    }
     // rows per thread and batch, loaded before any is routed (one with 256
     // threads for 64 tokens x 4 heads)
     constexpr int kRB = (kTokBlock * kHG + 255) / 256;
