@@ -332,15 +332,22 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
     const int s = sh / H, h = sh % H;
     const int64_t len = cu[s + 1] - cu[s];
     int carry = (int)((int64_t)K * ((int64_t)H * cu[s] + h * len));
-    const int M = N * nblk;
-    int32_t* c = counts + (int64_t)sh * M;
+    // only the sequence's own token blocks hold records (blocks past its end
+    // have zero counts and are never read): scan element e is partition
+    // e / nb, block e % nb
+    const int nb = (int)((len + kTokBlock - 1) / kTokBlock);
+    const int M = N * nb;
+    int32_t* c = counts + (int64_t)sh * N * nblk;
+    if (nb == 0)
+        for (int i = threadIdx.x; i < N; i += blockDim.x) seg_offsets[(int64_t)sh * N + i] = carry;
     for (int base = 0; base < M; base += (int)blockDim.x * kScanE) {
         const int e0 = base + (int)threadIdx.x * kScanE;
         int x[kScanE];
         int tsum = 0;
 #pragma unroll
         for (int u = 0; u < kScanE; u++) {
-            x[u] = e0 + u < M ? c[e0 + u] : 0;
+            const int e = e0 + u;
+            x[u] = e < M ? c[(e / nb) * nblk + e % nb] : 0;
             tsum += x[u];
         }
         int total;
@@ -349,8 +356,8 @@ __global__ __launch_bounds__(256) void block_scan_kernel(const int32_t* __restri
         for (int u = 0; u < kScanE; u++) {
             const int e = e0 + u;
             if (e < M) {
-                c[e] = run;
-                if (e % nblk == 0) seg_offsets[(int64_t)sh * N + e / nblk] = run;
+                c[(e / nb) * nblk + e % nb] = run;
+                if (e % nb == 0) seg_offsets[(int64_t)sh * N + e / nb] = run;
             }
             run += x[u];
         }
