@@ -40,9 +40,8 @@ namespace {
 constexpr int kPsWaves = 4;
 constexpr int kPsThreads = kPsWaves * kWave;
 constexpr int kPsRec = 16;  // records per step
-constexpr int kDepth = 2;   // steps whose row loads are in flight (2, 4 and 8 measure alike)
-static_assert(SSE_SHARED_PIECE % (kPsRec * kDepth) == 0, "pieces must be whole groups of steps");
-static_assert(kDepth % 2 == 0, "stage i % 2 must be static inside the unrolled step loop");
+constexpr int kDepth = 2;   // steps whose row loads are in flight
+static_assert(SSE_SHARED_PIECE % kPsRec == 0, "pieces must be whole steps");
 
 // Row stride (elements) of an LDS stage row of `cols` bf16 values.  The
 // transpose reads of a half-wave touch 4 records x 64 bytes; a stride of
@@ -103,7 +102,11 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     // ---- row layout: this thread's record and 8-column piece
     const int rr = tid / LPR, kc = 8 * (tid % LPR);
     const int rv = tid / LPRV, vc = 8 * (tid % LPRV);
-    const bool krow = rr < kPsRec, vrow = rv < kPsRec;
+    // Guards that hold for every thread of a shape are compile-time true:
+    // a runtime condition around code in the step loop makes the compiler
+    // wait for every load in flight at the loop head, defeating the prefetch.
+    const bool krow = (kPsRec * LPR >= kPsThreads) || rr < kPsRec;
+    const bool vrow = (kPsRec * LPRV >= kPsThreads) || rv < kPsRec;
     // record index (within the piece) of row r of step i: backwards over a
     // state piece, forwards over the last piece
     auto rec_of = [&](int i, int r) { return state ? n - kPsRec * (i + 1) + r : kPsRec * i + r; };
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     };
 
     // ---- MFMA layout: row tile rt, this wave's column tiles
-    const int rt = wv % RT, ct0 = wv / RT;
+    const int rt = wv % RT, ct0 = RT == kPsWaves ? 0 : wv / RT;
+    constexpr bool kAllTiles = CT % WPR == 0;  // every (ct0, u) names a tile
     const int j = 32 * rt + lane % 32;      // state row of this lane's A operand
     const int half = lane / 32;             // records 8 half .. 8 half + 7 of a step
     f32x16 acc[NT];
@@ -138,11 +142,14 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
         for (int e = 0; e < 16; e++) acc[u][e] = 0.f;
     float carry = 0.f;  // sum of log_alpha over the records after the current step (row j)
 
-    // Step i's rows are loaded kDepth steps ahead into ring[i % kDepth] (the
-    // step loop is unrolled by kDepth so the ring is indexed statically and
-    // the compiler waits only for the loads it consumes).
-    Raw ring[kDepth];
-    auto step = [&](auto stI, int i, Raw& R) {
+    // Step i's rows are loaded kDepth steps ahead into ring[i % (kDepth + 1)]:
+    // each step loads into the register set the previous step consumed, not
+    // its own (with the set just consumed as the load target the compiler
+    // waited for every load in flight at the loop head).  The step loop is
+    // unrolled by kDepth + 1 so the ring is indexed statically.
+    constexpr int kRing = kDepth + 1;
+    Raw ring[kRing];
+    auto step = [&](auto stI, int i, Raw& R, Raw& Rnext) {
         constexpr bool STATE = decltype(stI)::value;
         PsStage<CK, DV>& S = st[i & 1];
         // 1. normaliser of this thread's record (max-shifted log-sum-exp over
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
         if constexpr (STATE) {
             if (vrow) *reinterpret_cast<uint4*>(&S.v[rv][vc]) = R.v;
         }
-        load(stI, i + kDepth, R);
+        load(stI, i + kDepth, Rnext);
         if constexpr (!STATE) return;
         lds_barrier();
 
@@ -218,22 +225,24 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
 #pragma unroll
         for (int u = 0; u < NT; u++) {
             const int ct = ct0 + WPR * u;
-            if (ct < CT) {
+            if (kAllTiles || ct < CT) {
                 const u16x8 vb = tr_operand<VS>(&S.v[0][0], 32 * ct, lane);
                 acc[u] = mfma32(ah, vb, acc[u]);
                 acc[u] = mfma32(al, vb, acc[u]);
             }
         }
     };
-    // whole groups of kDepth steps (state pieces are whole groups; the last
-    // piece's extra steps only re-read valid rows and store nothing)
     auto run = [&](auto stI) {
 #pragma unroll
         for (int p = 0; p < kDepth; p++) load(stI, p, ring[p]);
-        for (int i0 = 0; i0 < nsteps; i0 += kDepth) {
+        int i0 = 0;
+        for (; i0 + kRing <= nsteps; i0 += kRing) {
 #pragma unroll
-            for (int p = 0; p < kDepth; p++) step(stI, i0 + p, ring[p]);
+            for (int p = 0; p < kRing; p++) step(stI, i0 + p, ring[p], ring[(p + kDepth) % kRing]);
         }
+#pragma unroll
+        for (int p = 0; p < kRing - 1; p++)
+            if (i0 + p < nsteps) step(stI, i0 + p, ring[p], ring[(p + kDepth) % kRing]);
     };
     if (state)
         run(std::true_type{});
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
 #pragma unroll
     for (int u = 0; u < NT; u++) {
         const int ct = ct0 + WPR * u;
-        if (ct < CT) {
+        if (kAllTiles || ct < CT) {
             float4* fs = reinterpret_cast<float4*>(a.agg_S + (((ab * RT + rt) * CT + ct) * kWave + lane) * 16);
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++)
