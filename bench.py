@@ -70,8 +70,9 @@ def chunk_flops(records, c, d, C=64):
     return records * 2 * (C * c / 2 + C * d / 2 + 2 * c * d)
 
 
-def run_forward(args, w, si, sse, torch):
-    inp = si.forward_inputs(w)
+def run_forward(args, w, si, sse, torch, inp=None):
+    if inp is None:
+        inp = si.forward_inputs(w)
     cu = inp["cu_seqlens"]
     T = int(cu[-1])
     S = len(cu) - 1
@@ -103,6 +104,41 @@ def run_forward(args, w, si, sse, torch):
     stages, calls = sse.sse_trace_read()
     sse.sse_trace_enable(False)
     return T, S, total_ms, {k: v / max(calls, 1) for k, v in stages.items()}, calls
+
+
+def fig6_sweep(args, si, sse, torch):
+    """Forward time of the varlen path in the operator-timing setting of
+    "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记"
+    (§2.6, Fig. 6): 8 heads, head dim 128, one routed partition per token,
+    two sequences of L/2 tokens, N = 4, 8, 16; bf16 inputs here.  That figure
+    times forward plus backward on another GPU and gives no values in the
+    text; this measures the forward only, to see how the time moves with N
+    at fixed k."""
+    from types import SimpleNamespace
+    ns = SimpleNamespace(warmup=2, steps=10)
+    rows = []
+    for L in (2048, 4096, 8192, 16384, 32768, 65536):
+        # one draw per L; the router logits of N partitions are the first N
+        # columns of the N = 16 draw (still N(0, 1) and free of ties)
+        base = si.forward_inputs(si.Workload(f"fig6_L{L}", "bf16", H=8, c=128, d=128, N=16,
+                                             topk=1, B=2, T=L // 2))
+        for N in (4, 8, 16):
+            w = si.Workload(f"fig6_N{N}_L{L}", "bf16", H=8, c=128, d=128, N=N, topk=1, B=2,
+                            T=L // 2)
+            inp = dict(base)
+            inp["router_logits"] = np.ascontiguousarray(base["router_logits"][..., :N])
+            T, S, total_ms, stages, _ = run_forward(ns, w, si, sse, torch, inp=inp)
+            ms = total_ms / ns.steps
+            rows.append({"L": L, "N": N, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                         "stage_ms": stages})
+            log(f"fig6 L={L} N={N}: {ms:.3f} ms")
+    spread = {}
+    for L in sorted({r["L"] for r in rows}):
+        t = [r["ms"] for r in rows if r["L"] == L]
+        spread[str(L)] = max(t) / min(t)
+    return {"setting": "H=8, c=d=128, k=1, cu_seqlens=[0, L/2, L], N in {4, 8, 16}, bf16 "
+                       "inputs, router logits N(0,1), forward only",
+            "rows": rows, "max_over_min_across_N": spread}
 
 
 def run_decode(args, si, sse, torch):
@@ -264,6 +300,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the varlen forward timing")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration")
+    ap.add_argument("--fig6", action="store_true",
+                    help="also time the forward over L and N in the operator-timing setting (Fig. 6)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -340,6 +378,8 @@ def main():
             peaks["decode_frac"] = decode["achieved_GBs"] / peaks["inplace_rmw_GBs"]
         log(f"measured peaks {peaks}")
 
+    fig6 = fig6_sweep(args, si, sse, torch) if args.fig6 else None
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -388,6 +428,7 @@ def main():
         "varlen_forward": varlen,
         "measured_peaks": peaks,
         "decode": decode,
+        "fig6_sweep": fig6,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -27,6 +27,25 @@ struct FwdLayout {
     size_t idx, w, counts, seg_off, rinfo, seg_rec, lnz2, agg_S, agg_D, trash, part, total;
 };
 
+// Piece length of the shared partition's chain.  bf16 inputs: 1024 tokens,
+// halved (down to 256) while the shared pass would run fewer than 512
+// (sequence, head, piece) blocks and a sequence would still have at most 16
+// pieces, so that a few short sequences spread over the chip; the shared
+// pass and the piece-state pass launch one block per piece.  The cap bounds
+// the shared pass's prologue, which reads the aggregates of every earlier
+// piece (quadratic in the piece count).  fp32 inputs keep the fixed length.
+int shared_piece_len(int dtype, int64_t S, int H, int max_seqlen) {
+    int p = sse::chunk_piece_len(dtype);
+    if (dtype == SSE_F32) return p;
+    auto pieces = [&](int pl) { return max_seqlen <= 0 ? 1 : (max_seqlen + pl - 1) / pl; };
+    while (p > 256 && S * H * pieces(p) < 512 && pieces(p / 2) <= 16) p /= 2;
+    return p;
+}
+
+int max_pieces(int max_seqlen, int piece_len) {
+    return max_seqlen <= 0 ? 1 : (max_seqlen + piece_len - 1) / piece_len;
+}
+
 // Workspace carving.  c, d = 0 sizes the grouping part only.  Returns false
 // when the sizes overflow the 32-bit indexing of the kernels.
 bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N, int K,
@@ -39,8 +58,9 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     if (recs >= INT_MAX || cnt >= INT_MAX || units >= INT_MAX || T >= INT_MAX) return false;
     if ((int64_t)S * H >= INT_MAX || (int64_t)S * H * N + 1 >= INT_MAX) return false;
     if ((int64_t)S * nblk * H >= INT_MAX) return false;
-    // pieces are sized for the shorter (fp32) piece length: an upper bound
-    const int64_t maxp = sse::chunk_max_pieces(max_seqlen, sse::kF32);
+    // pieces counted at the bf16 piece length, never longer than the fp32
+    // one: an upper bound for both
+    const int64_t maxp = max_pieces(max_seqlen, shared_piece_len(SSE_BF16, S, H, max_seqlen));
     if (maxp >= 65536) return false;
     size_t off = 0;
     L.idx = off;     off += align_up(sizeof(int32_t) * (size_t)recs);
@@ -160,8 +180,8 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.H = H;
     a.N = N;
     a.topk = topk;
-    a.piece_len = sse::chunk_piece_len(dtype);
-    a.max_pieces = sse::chunk_max_pieces(max_seqlen, dtype);
+    a.piece_len = shared_piece_len(dtype, num_seqs, H, max_seqlen);
+    a.max_pieces = max_pieces(max_seqlen, a.piece_len);
 
     // 1. router + per-block counts (+ the key-softmax normaliser for fp32
     //    inputs; for bf16 inputs the piece-state pass computes it)
