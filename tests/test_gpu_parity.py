@@ -109,14 +109,28 @@ def test_bf16_other_shapes(c, d):
 
 @pytest.mark.parametrize("c,d", [(32, 64), (64, 128), (128, 32), (128, 128)])
 def test_multi_piece_with_initial_states(c, d):
-    """Sequences longer than the shared partition's 1024-token pieces (state
-    pieces combined with random initial states), lengths at and just past a
-    piece boundary, a 3-token and an empty sequence; every element checked."""
+    """Sequences spanning several pieces of the shared partition (piece
+    states combined with random initial states; with this few (sequence,
+    head) units the pieces are 256 tokens), lengths at and just past a piece
+    boundary, a 3-token and an empty sequence; every element checked."""
     w = si.Workload(f"pieces_{c}x{d}", "bf16", H=2, c=c, d=d, N=8, topk=2)
     lengths = [2100, 1024, 1025, 3, 0]
     rng = np.random.default_rng(41)
     init = (0.5 * rng.standard_normal((len(lengths), w.H, w.N + 1, c, d))).astype(np.float32)
     _check_full(w, lengths, seed=40, init=init, tag=w.name)
+
+
+def test_sixteen_shared_pieces():
+    """The deepest chain of shared pieces the piece-length rule allows: two
+    (sequence, head) units per sequence and 4,096 tokens give 16 pieces of
+    256 tokens (the second sequence ends in a 161-token piece), so the last
+    piece's input state combines 15 piece aggregates with the initial
+    state; every element checked."""
+    w = si.Workload("pieces16", "bf16", H=2, c=128, d=128, N=4, topk=1)
+    lengths = [4096, 4001]
+    rng = np.random.default_rng(43)
+    init = (0.5 * rng.standard_normal((len(lengths), w.H, w.N + 1, w.c, w.d))).astype(np.float32)
+    _check_full(w, lengths, seed=42, init=init, tag=w.name)
 
 
 @pytest.mark.parametrize("dtype,N,k,H,cd", [("bf16", 64, 8, 5, 64), ("f32", 64, 8, 3, 32),
