@@ -11,13 +11,18 @@ reported under "decode".
 roofline: the dominant kernel is the chunked GLA pass with the longest
 time (the routed pass); its duration comes from HIP events recorded around it
 on the library's stream during the timed steps (sse_trace_*).  Its
-algorithmic bytes per launch are the token inputs read once, o written once
-and the pass's final states written once; "traffic" is the HBM bytes the
+algorithmic bytes per launch are what the pass itself must move: the routed
+pass reads every token's q, key logits, log decay and v rows once and writes
+the routed partitions' final states (its e-gated reads go to workspace
+slots, an implementation cost, not counted); the shared pass reads the same
+rows, writes o and the shared final states.  "traffic" is the HBM bytes the
 committed FETCH_SIZE/WRITE_SIZE counter runs measured for it (null if the
-kernel source changed since).
+kernel source changed since).  forward_roofline gives the whole forward's
+fraction (all launches, algorithmic bytes of the layer).
 
-cpu_baseline: the fp64 oracle (untuned) on a bounded sample of the same
-workload: a number of (sequence, head) units, over the host cores.
+cpu_baseline: the fp64 oracle (untuned) on the whole main workload (all 64
+(sequence, head) units), threads over units on the host cores; plus the
+single-thread rate on the small bf16 workload (per-core figure).
 """
 from __future__ import annotations
 
@@ -58,11 +63,13 @@ def forward_bytes(T, S, H, c, d, N, in_bytes=2):
     return inputs + T * H * 4 * d + S * H * (N + 1) * c * d * 4
 
 
-def pass_bytes(T, S, H, c, d, parts, in_bytes=2):
+def pass_bytes(T, S, H, c, d, parts, writes_o, in_bytes=2):
     """Algorithmic bytes of one chunked-GLA pass over `parts` partitions of
     every (sequence, head): each token's q, key logits, log_alpha and v read
-    once, its o row written once, the pass's final states written once."""
-    return T * H * in_bytes * (3 * c + d) + T * H * 4 * d + S * H * parts * c * d * 4
+    once, the pass's final states written once, and o written once if the
+    pass writes it (the shared pass does; the routed pass does not)."""
+    return (T * H * in_bytes * (3 * c + d) + (T * H * 4 * d if writes_o else 0)
+            + S * H * parts * c * d * 4)
 
 
 def chunk_flops(records, c, d, C=64):
@@ -187,32 +194,38 @@ def run_decode(args, si, sse, torch):
 
 
 def cpu_baseline(args, w, si):
+    """The untuned fp64 oracle on the whole main workload (every one of its
+    64 distinct (sequence, head) units), threads over units, plus its
+    single-thread rate on the small workload."""
     import oracle
-    threads = min(len(os.sched_getaffinity(0)), 16)
-    n_units = args.cpu_units or 4 * threads
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(affinity, 16)
     inp = si.forward_inputs(w)
-    units = [(u % w.B, (u * 5) % w.H) for u in range(n_units)]
     cu = inp["cu_seqlens"]
-    # gather the sampled (sequence, head) units as independent 1-head sequences
-    sel = {n: np.stack([inp[n][cu[s]:cu[s + 1], h] for (s, h) in units])[:, :, None]
-           for n in NAMES}
-    sub = {n: np.ascontiguousarray(sel[n].reshape(-1, 1, sel[n].shape[-1])) for n in NAMES}
-    lens = [int(cu[s + 1] - cu[s]) for (s, h) in units]
-    cus = np.zeros(len(units) + 1, np.int32)
-    cus[1:] = np.cumsum(lens)
+    T = int(cu[-1])
     lib = oracle.load()
     t0 = time.perf_counter()
-    oracle.forward(*(sub[n] for n in NAMES), cus, w.N, w.topk, threads=threads, lib=lib)
+    oracle.forward(*(inp[n] for n in NAMES), cu, w.N, w.topk, threads=threads, lib=lib)
     el = time.perf_counter() - t0
-    head_tokens = int(sum(lens))
+    ws = si.WORKLOADS["small_bf16"]
+    inp_s = si.forward_inputs(ws)
+    t1 = time.perf_counter()
+    oracle.forward(*(inp_s[n] for n in NAMES), inp_s["cu_seqlens"], ws.N, ws.topk, threads=1,
+                   lib=lib)
+    el1 = time.perf_counter() - t1
+    T1 = int(inp_s["cu_seqlens"][-1])
     return {
-        "value": head_tokens / w.H / el,
+        "value": T / el,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(units)} (sequence, head) units of the main workload "
-                  f"({head_tokens} head-tokens = {head_tokens / w.H:.0f} full tokens), "
-                  f"{el:.1f} s wall on {threads} threads",
+        "sample": f"the whole main workload: {T} tokens x {w.H} heads, all "
+                  f"{(len(cu) - 1) * w.H} (sequence, head) units, {el:.1f} s wall on {threads} "
+                  f"threads ({threads * el:.0f} thread-seconds)",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": affinity,
+        "single_thread_small_bf16": {"tokens_per_s": T1 / el1, "seconds": el1,
+                                     "workload": ws.notes},
     }
 
 
@@ -295,7 +308,6 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-reps", type=int, default=3)
-    ap.add_argument("--cpu-units", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the varlen forward timing")
@@ -324,11 +336,11 @@ def main():
     ms = total_ms / args.steps
     tokens_per_s = T / (ms * 1e-3)
     # dominant kernel: the routed pass (k of the k+1 partition reads)
-    kern = {"routed": ("chunk_ws_kernel<128,128,routed>", w.N, T * w.H * w.topk),
-            "shared": ("chunk_ws_kernel<128,128,shared>", 1, T * w.H)}
+    kern = {"routed": ("chunk_ws_kernel<128,128,routed>", w.N, T * w.H * w.topk, False),
+            "shared": ("chunk_ws_kernel<128,128,shared>", 1, T * w.H, True)}
     dom = max(kern, key=lambda k: stages[k])
-    kname, parts, records = kern[dom]
-    kb = pass_bytes(T, S, w.H, w.c, w.d, parts)
+    kname, parts, records, writes_o = kern[dom]
+    kb = pass_bytes(T, S, w.H, w.c, w.d, parts, writes_o)
     kf = chunk_flops(records, w.c, w.d)
     k_ms = stages[dom]
     achieved = kb / (k_ms * 1e-3) / 1e9

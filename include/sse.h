@@ -39,9 +39,11 @@
  *   - Preconditions the library does not check (documented, not detected):
  *     cu_seqlens is non-decreasing with cu_seqlens[0] == 0 and
  *     cu_seqlens[num_seqs] == total_tokens; every length <= max_seqlen;
- *     inputs are finite; log_alpha <= 0 and the sum of log_alpha over any 64
- *     consecutive records of one partition stays above -80 (the chunked
- *     factorisation multiplies by exp of minus that sum in fp32).
+ *     inputs are finite; log_alpha <= 0 and, for bf16 inputs, the sum of
+ *     log_alpha over any 64 consecutive records of one partition stays above
+ *     -80 (the chunked factorisation multiplies by exp of minus the in-chunk
+ *     sum in fp32; fp32 inputs are computed in fp64, where the sum over any 16
+ *     consecutive records only has to stay above -700).
  */
 #ifndef SSE_H
 #define SSE_H
@@ -102,6 +104,15 @@ size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_s
  *   topk_idx, topk_w          [total_tokens, H, topk] int32 / fp32, or NULL:
  *                             the chosen partitions (descending logits) and
  *                             their router probabilities
+ *   seg_offsets               [num_seqs*H*N + 1] int32 or NULL: the grouping
+ *                             this call ran (§2.6 varlen regrouping; the
+ *                             layout of sse_group_by_partition): segment
+ *                             g = (s*H + h)*N + i holds records
+ *                             [seg_offsets[g], seg_offsets[g+1])
+ *   seg_tok, seg_slot         [total_tokens*H*topk] int32 or NULL: token and
+ *                             top-k rank of every record, in the order the
+ *                             chunk kernels walk them (copied from the
+ *                             forward's own segment records)
  *   workspace                 device buffer of workspace_bytes >=
  *                             sse_forward_workspace_bytes(...)
  * o may not alias any input.  Each routed read (e-gated) is stored into a
@@ -113,7 +124,8 @@ int sse_forward(const void *q, const void *key_logits, const void *v, const void
                 const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
                 int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
                 const float *initial_states, float *o, float *final_states, int32_t *topk_idx,
-                float *topk_w, void *workspace, size_t workspace_bytes, void *stream);
+                float *topk_w, int32_t *seg_offsets, int32_t *seg_tok, int32_t *seg_slot,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step (§2.6: decoding recurs only on the selected states).
@@ -137,7 +149,8 @@ int sse_decode_step(const void *q, const void *key_logits, const void *v, const 
  * N logits (rows = tokens x heads).
  *   router_logits [rows, N] (dtype) -> topk_idx [rows, topk] int32,
  *   topk_w [rows, topk] fp32 (router probability of each chosen partition).
- * Deterministic.  The forward pass runs the same device code.
+ * Deterministic.  The forward pass selects with the same per-row routine
+ * (same top-k order and weights) inside its fused routing kernel.
  */
 int sse_router_topk(const void *router_logits, int dtype, int64_t rows, int N, int topk,
                     int32_t *topk_idx, float *topk_w, void *stream);
@@ -160,7 +173,10 @@ size_t sse_group_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seq
  *               its token's top-k list
  *   seg_w       [total_tokens*H*topk] fp32 or NULL (requires topk_w): the
  *               record's router probability
- * Deterministic.  The forward pass runs the same device code.
+ * Deterministic.  The forward pass groups with its own kernels (ballot
+ * ranks fused into its routing kernel, then the same scan); its result is
+ * observable through the seg_offsets / seg_tok / seg_slot outputs of
+ * sse_forward and has this same layout and order.
  */
 int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
                            const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
@@ -177,7 +193,9 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  * 3 = routed partitions (store their e-gated reads into the workspace
  * slots), 4 = shared partition (writes o = shared read + slots).
  * Events of the last 256 calls are kept.  Tracing assumes
- * one device per process.
+ * one device per process.  The first sse_trace_enable(1) creates the HIP
+ * events it records into (256 x 6 events, kept until the process ends):
+ * the one place where the library itself acquires a runtime resource.
  *   sse_trace_enable(1) creates the events (first time) and starts a fresh
  *   record; sse_trace_enable(0) stops recording.
  *   sse_trace_read waits for the recorded calls to finish, writes the summed

@@ -54,7 +54,7 @@ def lib():
     L.sse_forward_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I]
     L.sse_forward_workspace_bytes.restype = SZ
     L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
-                              SZ, P]
+                              P, P, P, SZ, P]
     L.sse_forward.restype = I
     L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
     L.sse_decode_step.restype = I
@@ -110,12 +110,14 @@ def sse_forward_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N, 
 
 def sse_forward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens, max_seqlen=None,
                 initial_states=None, *, o=None, final_states=None, topk_idx=None, topk_w=None,
-                workspace=None):
+                seg_offsets=None, seg_tok=None, seg_slot=None, workspace=None):
     """Varlen SSE forward.  q/key_logits/log_alpha [T,H,c], v [T,H,d],
     router_logits [T,H,N] (bf16 or fp32, one dtype), cu_seqlens int32
     [S+1] on the device.  Returns (o [T,H,d] fp32, final_states
     [S,H,N+1,c,d] fp32).  Optional preallocated outputs/workspace avoid
-    allocation; ``max_seqlen`` (host int) avoids a device->host read."""
+    allocation; ``max_seqlen`` (host int) avoids a device->host read.
+    ``seg_offsets`` [S*H*N+1], ``seg_tok`` / ``seg_slot`` [T*H*topk] (int32,
+    optional) receive the grouping this call ran."""
     dev = q.device
     T, H, c = q.shape
     d = v.shape[2]
@@ -134,14 +136,22 @@ def sse_forward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens,
         o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
     if final_states is None:
         final_states = torch.empty((S, H, N + 1, c, d), dtype=torch.float32, device=dev)
+    for t, n_, nm in ((seg_offsets, S * H * N + 1, "seg_offsets"),
+                      (seg_tok, T * H * topk, "seg_tok"), (seg_slot, T * H * topk, "seg_slot")):
+        if t is not None:
+            _need(t, (n_,), torch.int32, nm, dev)
+    for t, nm in ((topk_idx, "topk_idx"), (topk_w, "topk_w")):
+        if t is not None:
+            _need(t, (T, H, topk), torch.int32 if nm == "topk_idx" else torch.float32, nm, dev)
     ws_bytes = sse_forward_workspace_bytes(T, S, max_seqlen, H, c, d, N, topk)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = lib().sse_forward(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
                            _ptr(router_logits), _dtype_code(q), _ptr(cu_seqlens), S,
                            int(max_seqlen), T, H, c, d, N, topk, _ptr(initial_states), _ptr(o),
-                           _ptr(final_states), _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
-                           workspace.numel(), _stream(dev))
+                           _ptr(final_states), _ptr(topk_idx), _ptr(topk_w), _ptr(seg_offsets),
+                           _ptr(seg_tok), _ptr(seg_slot), _ptr(workspace), workspace.numel(),
+                           _stream(dev))
     _check(st, "sse_forward")
     return o, final_states
 

@@ -20,11 +20,6 @@ namespace {
 constexpr int kNW = 4;        // waves per block
 constexpr int kThreads = kNW * kWave;
 constexpr int kPC = 4;        // columns per lane in the preparation layout
-#ifndef SSE_SHARED_PIECE
-#define SSE_SHARED_PIECE 1024
-#endif
-
-enum { kModeLocal = 0, kModeShared = 1, kModeRouted = 2 };
 
 // Four consecutive input values of one row.
 template <typename TIn>

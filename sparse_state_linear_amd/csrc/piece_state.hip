@@ -41,7 +41,7 @@ constexpr int kPsWaves = 4;
 constexpr int kPsThreads = kPsWaves * kWave;
 constexpr int kPsRec = 16;  // records per step
 constexpr int kDepth = 2;   // steps whose row loads are in flight
-static_assert(SSE_SHARED_PIECE % kPsRec == 0, "pieces must be whole steps");
+static_assert(kSharedPiece % kPsRec == 0, "pieces must be whole steps");
 
 // Row stride (elements) of an LDS stage row of `cols` bf16 values.  The
 // transpose reads of a half-wave touch 4 records x 64 bytes; a stride of
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     // the piece's normalisers, written to global memory once at the end: a
     // store inside the step loop would be counted with the loads in flight
     // (one vector-memory counter), so every step would wait for it
-    __shared__ __attribute__((aligned(16))) float lnz_all[SSE_SHARED_PIECE];
+    __shared__ __attribute__((aligned(16))) float lnz_all[kSharedPiece];
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -279,7 +279,7 @@ void launch_ps(const ChunkArgs& a, hipStream_t st) {
 
 hipError_t launch_piece_state(const ChunkArgs& a, int c, int d, hipStream_t st) {
     if ((int64_t)a.num_seqs * a.H == 0) return hipSuccess;
-    if (a.piece_len > SSE_SHARED_PIECE || a.piece_len % kPsRec != 0) return hipErrorInvalidValue;
+    if (a.piece_len > kSharedPiece || a.piece_len % kPsRec != 0) return hipErrorInvalidValue;
 #define SSE_PS_CASE(CC, DD)          \
     if (c == CC && d == DD) {        \
         launch_ps<CC, DD>(a, st);    \

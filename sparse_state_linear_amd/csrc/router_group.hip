@@ -31,7 +31,6 @@
 
 namespace sse {
 
-constexpr int kTokBlock = 64;   // tokens per grouping block (one wave)
 
 // Router for one row of N logits: top-k by logit (descending, equal logits ->
 // lower index) and the softmax probability of each chosen partition.
@@ -482,7 +481,6 @@ hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int
                          : launch_router_rows_t<bf16_t>(z, rows, N, K, idx, w, st);
 }
 
-int group_nblk(int max_seqlen) { return max_seqlen <= 0 ? 1 : (max_seqlen + kTokBlock - 1) / kTokBlock; }
 
 template <int NMAX, typename TIn>
 static void launch_rc_n(dim3 grid, const TIn* z, const TIn* kl, const int32_t* cu, int64_t T,
@@ -568,6 +566,34 @@ hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, i
     if (e != hipSuccess) return e;
     scatter_kernel<<<dim3(SH, (nblk + kScatterWaves - 1) / kScatterWaves), kScatterWaves * kWave,
                      0, st>>>(idx, w, cu, H, N, K, nblk, counts, seg_tok, seg_slot, seg_w);
+    return hipGetLastError();
+}
+
+// Debug copies of the forward's own grouping: the segment offsets as
+// scanned, and the token and top-k rank of every record the chunk kernels
+// read (decoded from its input row t*H + h and slot row (t*H + h)*K + rank).
+__global__ __launch_bounds__(256) void seg_debug_kernel(const SegRec* __restrict__ seg,
+                                                        const int32_t* __restrict__ seg_off,
+                                                        int64_t nrec, int64_t noff, int H, int K,
+                                                        int32_t* __restrict__ out_off,
+                                                        int32_t* __restrict__ out_tok,
+                                                        int32_t* __restrict__ out_slot) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (out_off && i < noff) out_off[i] = seg_off[i];
+    if (i < nrec) {
+        const uint2 r = *reinterpret_cast<const uint2*>(seg + i);
+        if (out_tok) out_tok[i] = (int32_t)(r.x / (uint32_t)H);
+        if (out_slot) out_slot[i] = (int32_t)(r.y % (uint32_t)K);
+    }
+}
+
+hipError_t launch_seg_debug(const SegRec* seg, const int32_t* seg_off, int64_t nrec, int64_t nseg,
+                            int H, int K, int32_t* out_off, int32_t* out_tok, int32_t* out_slot,
+                            hipStream_t st) {
+    const int64_t n = nrec > nseg + 1 ? nrec : nseg + 1;
+    if (!out_off && !out_tok && !out_slot) return hipSuccess;
+    seg_debug_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(seg, seg_off, nrec, nseg + 1, H,
+                                                                  K, out_off, out_tok, out_slot);
     return hipGetLastError();
 }
 

@@ -27,16 +27,16 @@ struct FwdLayout {
     size_t idx, w, counts, seg_off, rinfo, seg_rec, lnz2, agg_S, agg_D, trash, part, total;
 };
 
-// Piece length of the shared partition's chain.  bf16 inputs: 1024 tokens,
-// halved (down to 256) while the shared pass would run fewer than 512
-// (sequence, head, piece) blocks and a sequence would still have at most 16
-// pieces, so that a few short sequences spread over the chip; the shared
-// pass and the piece-state pass launch one block per piece.  The cap bounds
-// the shared pass's prologue, which reads the aggregates of every earlier
-// piece (quadratic in the piece count).  fp32 inputs keep the fixed length.
-int shared_piece_len(int dtype, int64_t S, int H, int max_seqlen) {
-    int p = sse::chunk_piece_len(dtype);
-    if (dtype == SSE_F32) return p;
+// Piece length of the shared partition's chain (bf16 inputs; the fp32-input
+// kernel walks each chain in one block): 1024 tokens, halved (down to 256)
+// while the shared pass would run fewer than 512 (sequence, head, piece)
+// blocks and a sequence would still have at most 16 pieces, so that a few
+// short sequences spread over the chip; the shared pass and the piece-state
+// pass launch one block per piece.  The cap bounds the shared pass's
+// prologue, which reads the aggregates of every earlier piece (quadratic in
+// the piece count).
+int shared_piece_len(int64_t S, int H, int max_seqlen) {
+    int p = sse::chunk_piece_len();
     auto pieces = [&](int pl) { return max_seqlen <= 0 ? 1 : (max_seqlen + pl - 1) / pl; };
     while (p > 256 && S * H * pieces(p) < 512 && pieces(p / 2) <= 16) p /= 2;
     return p;
@@ -58,9 +58,7 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     if (recs >= INT_MAX || cnt >= INT_MAX || units >= INT_MAX || T >= INT_MAX) return false;
     if ((int64_t)S * H >= INT_MAX || (int64_t)S * H * N + 1 >= INT_MAX) return false;
     if ((int64_t)S * nblk * H >= INT_MAX) return false;
-    // pieces counted at the bf16 piece length, never longer than the fp32
-    // one: an upper bound for both
-    const int64_t maxp = max_pieces(max_seqlen, shared_piece_len(SSE_BF16, S, H, max_seqlen));
+    const int64_t maxp = max_pieces(max_seqlen, shared_piece_len(S, H, max_seqlen));
     if (maxp >= 65536) return false;
     size_t off = 0;
     L.idx = off;     off += align_up(sizeof(int32_t) * (size_t)recs);
@@ -125,7 +123,8 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
                 const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
                 int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
                 const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
-                float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+                float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
+                void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_common(dtype, H, c, d, N, topk);
     if (st != SSE_OK) return st;
     if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
@@ -180,7 +179,7 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     a.H = H;
     a.N = N;
     a.topk = topk;
-    a.piece_len = shared_piece_len(dtype, num_seqs, H, max_seqlen);
+    a.piece_len = shared_piece_len(num_seqs, H, max_seqlen);
     a.max_pieces = max_pieces(max_seqlen, a.piece_len);
 
     // 1. router + per-block counts (+ the key-softmax normaliser for fp32
@@ -200,6 +199,9 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     trace_mark(2, s);
     e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N, topk,
                               counts, seg_off, lnz2, seg_rec, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    e = sse::launch_seg_debug(seg_rec, seg_off, total_tokens * H * topk, (int64_t)num_seqs * H * N,
+                              H, topk, seg_offsets, seg_tok, seg_slot, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(3, s);
     // 4. routed partitions: e-gated reads into the workspace slots

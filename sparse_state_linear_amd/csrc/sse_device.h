@@ -122,7 +122,4 @@ __device__ __forceinline__ float row_reduce(float x, Op op) {
     }
 }
 
-// fp32 atomic add that maps to the hardware instruction (no CAS loop).
-__device__ __forceinline__ void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
-
 }  // namespace sse

@@ -15,7 +15,11 @@ constexpr int kMaxN = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxH = 256;
 
-int group_nblk(int max_seqlen);
+// Tokens per grouping block (one wave ranks a block's records).
+constexpr int kTokBlock = 64;
+inline int group_nblk(int max_seqlen) {
+    return max_seqlen <= 0 ? 1 : (max_seqlen + kTokBlock - 1) / kTokBlock;
+}
 
 hipError_t launch_router_rows(const void* z, int dtype, int64_t rows, int N, int K, int32_t* idx,
                               float* w, hipStream_t st);
@@ -48,6 +52,13 @@ hipError_t launch_group_fwd(const uint2* rinfo, const int32_t* cu, int num_seqs,
                             int64_t T, int H, int N, int K, int32_t* counts, int32_t* seg_offsets,
                             const float* lnz2, SegRec* seg, hipStream_t st);
 
+// Debug outputs of the forward's grouping: copies of the segment offsets
+// [nseg + 1] and, per record, its token t and top-k rank (any pointer may be
+// null).
+hipError_t launch_seg_debug(const SegRec* seg, const int32_t* seg_off, int64_t nrec, int64_t nseg,
+                            int H, int K, int32_t* out_off, int32_t* out_tok, int32_t* out_slot,
+                            hipStream_t st);
+
 // Arguments of the chunked GLA passes (see chunk_gla.hip).
 struct ChunkArgs {
     const void* q;
@@ -67,9 +78,10 @@ struct ChunkArgs {
                                  // [c/32][d/32][64 lanes][16] (32x32 MFMA accumulator tiles)
     float* agg_D;                // [S*H, max_pieces, c] piece decay products
     float* trash;                // one dummy output row for padded records
-    float* part;                 // [T, H, topk, d] e-gated routed reads (routed
-                                 // pass writes, shared pass adds into o): fp32
-                                 // for fp32 inputs, int16 steps for bf16 inputs
+    float* part;                 // [T, H, topk, d] e-gated routed reads (the
+                                 // routed pass writes them, the shared pass adds
+                                 // them into o): fp32 for fp32 inputs, int16
+                                 // values for bf16 inputs
     float* part_scale;           // bf16 inputs: [T, H, topk, d/32] fp32 steps
     uint32_t slot_rows;          // T H topk; bf16 slots have one spare row past it
     uint32_t rows;               // T H: rows of every token input
@@ -78,16 +90,25 @@ struct ChunkArgs {
     int max_pieces;
 };
 
-// Records per shared piece and the pieces needed for max_seqlen tokens.
-int chunk_piece_len(int dtype);
-int chunk_max_pieces(int max_seqlen, int dtype);
+// Passes of the chunked kernels: the routed partitions' segments, or the
+// shared partition's chain.
+enum { kModeShared = 1, kModeRouted = 2 };
 
-hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+// Records per shared piece of the bf16 kernels (the longest piece length).
+constexpr int kSharedPiece = 1024;
+inline int chunk_piece_len() { return kSharedPiece; }
+
 // bf16 inputs: key-softmax normalisers of every token and the shared
-// partition's piece states (piece_state.hip).
+// partition's piece states (piece_state.hip); fp32 inputs: nothing (the fp64
+// kernel walks each shared chain in one block and computes its own
+// normalisers).
+hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 hipError_t launch_piece_state(const ChunkArgs& a, int c, int d, hipStream_t st);
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+// fp32 inputs: the fp64 chunk kernel (chunk_f64.hip), mode kModeRouted or
+// kModeShared.
+hipError_t launch_chunk_f64(int mode, const ChunkArgs& a, int c, int d, hipStream_t st);
 
 hipError_t launch_decode(const void* q, const void* kl, const void* v, const void* la,
                          const void* z, int dtype, int B, int H, int c, int d, int N, int K,

@@ -1,0 +1,116 @@
+"""Host-side calls of the C ABI that its argument checks must reject (or that
+have nothing to do), with the status each must return.  No call here reaches
+a device: every one returns before its first HIP call.  Used by the plain
+host ABI test and by the sanitizer build of the ABI layer; it needs only
+ctypes (no torch)."""
+from __future__ import annotations
+
+import ctypes
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+F32, BF16 = 0, 1
+P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+FAKE = P(0x1000)   # never dereferenced: the checks reject the call first
+
+
+def declare(L):
+    L.sse_status_string.argtypes = [I]
+    L.sse_status_string.restype = ctypes.c_char_p
+    L.sse_forward_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I]
+    L.sse_forward_workspace_bytes.restype = SZ
+    L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
+                              P, P, P, SZ, P]
+    L.sse_forward.restype = I
+    L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
+    L.sse_decode_step.restype = I
+    L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
+    L.sse_router_topk.restype = I
+    L.sse_group_workspace_bytes.argtypes = [I64, I, I, I, I, I]
+    L.sse_group_workspace_bytes.restype = SZ
+    L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
+    L.sse_group_by_partition.restype = I
+    L.sse_trace_read.argtypes = [P, I, P]
+    L.sse_trace_read.restype = I
+
+
+def forward(L, **kw):
+    a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, z=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16,
+             T=16, H=2, c=32, d=32, N=4, k=2, init=None, o=FAKE, fs=FAKE, idx=None, w=None,
+             soff=None, stok=None, sslot=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.sse_forward(a["q"], a["kl"], a["v"], a["la"], a["z"], a["dtype"], a["cu"], a["S"],
+                         a["maxlen"], a["T"], a["H"], a["c"], a["d"], a["N"], a["k"], a["init"],
+                         a["o"], a["fs"], a["idx"], a["w"], a["soff"], a["stok"], a["sslot"],
+                         a["ws"], a["wsb"], a["stream"])
+
+
+FORWARD_REJECTS = [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(fs=None), INVALID),
+    (dict(cu=None), INVALID), (dict(dtype=7), INVALID), (dict(k=5), INVALID),
+    (dict(k=0), INVALID), (dict(H=0), INVALID), (dict(T=-1), INVALID), (dict(S=0), INVALID),
+    (dict(S=-1), INVALID), (dict(maxlen=-1), INVALID),
+    (dict(c=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(N=65, k=1), UNSUPPORTED),
+    (dict(N=16, k=9), UNSUPPORTED), (dict(H=257), UNSUPPORTED),
+    # 32-bit offsets of token rows and slots
+    (dict(T=1 << 26, S=1, maxlen=1 << 26, H=16, c=128, d=128), UNSUPPORTED),
+    (dict(T=1 << 40, S=1, maxlen=1 << 30), UNSUPPORTED),
+    (dict(wsb=16), WORKSPACE), (dict(ws=None), WORKSPACE),
+]
+
+DECODE_REJECTS = [
+    (dict(states=None), INVALID), (dict(B=-1), INVALID), (dict(c=16), UNSUPPORTED),
+    (dict(k=3, N=2), INVALID), (dict(B=1 << 30, H=256), UNSUPPORTED),
+]
+
+
+def decode(L, **kw):
+    a = dict(B=4, H=2, c=32, d=32, N=4, k=2, states=FAKE, dtype=F32)
+    a.update(kw)
+    return L.sse_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, a["dtype"], a["B"], a["H"], a["c"],
+                             a["d"], a["N"], a["k"], a["states"], FAKE, None, None)
+
+
+def exercise(L) -> int:
+    """Run every rejection case; raise AssertionError on a wrong status.
+    Returns the number of calls made."""
+    declare(L)
+    n = 0
+    for code in range(6):
+        assert L.sse_status_string(code).startswith(b"SSE_")
+        n += 1
+    for kw, code in FORWARD_REJECTS:
+        got = forward(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    for kw, code in DECODE_REJECTS:
+        got = decode(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    # workspace queries, including sizes that overflow the kernels' indexing
+    assert L.sse_forward_workspace_bytes(32768, 4, 8192, 16, 128, 128, 16, 2) > 0
+    assert L.sse_forward_workspace_bytes(1 << 40, 4, 1 << 30, 16, 128, 128, 16, 2) == 0
+    assert L.sse_forward_workspace_bytes(100, 1, 100, 1, 48, 32, 4, 1) == 0
+    assert L.sse_forward_workspace_bytes(-1, 1, 100, 1, 32, 32, 4, 1) == 0
+    assert L.sse_forward_workspace_bytes(100, -3, 100, 1, 32, 32, 4, 1) == 0
+    assert L.sse_forward_workspace_bytes(0, 0, 0, 1, 32, 32, 4, 1) > 0
+    assert L.sse_group_workspace_bytes(100, 1, 100, 2, 4, 1) > 0
+    assert L.sse_group_workspace_bytes(100, 1, 100, 2, 65, 1) == 0
+    assert L.sse_group_workspace_bytes(1 << 40, 1, 1 << 30, 2, 4, 1) == 0
+    n += 9
+    assert L.sse_router_topk(FAKE, 0, 10, 4, 5, FAKE, FAKE, None) == INVALID
+    assert L.sse_router_topk(None, 0, 10, 4, 2, FAKE, FAKE, None) == INVALID
+    assert L.sse_router_topk(FAKE, 0, 10, 80, 2, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.sse_router_topk(FAKE, 0, -1, 4, 2, FAKE, FAKE, None) == INVALID
+    assert L.sse_group_by_partition(FAKE, None, FAKE, 1, 16, 16, 2, 4, 2, FAKE, FAKE, None, None,
+                                    FAKE, 0, None) == WORKSPACE
+    assert L.sse_group_by_partition(FAKE, None, FAKE, 1, 16, 16, 2, 4, 2, FAKE, FAKE, None, FAKE,
+                                    FAKE, 1 << 20, None) == INVALID
+    assert L.sse_group_by_partition(FAKE, None, None, 1, 16, 16, 2, 4, 2, FAKE, FAKE, None, None,
+                                    FAKE, 1 << 20, None) == INVALID
+    n += 7
+    ms = (ctypes.c_float * 5)()
+    calls = ctypes.c_int64(0)
+    assert L.sse_trace_read(None, 5, ctypes.byref(calls)) == INVALID
+    assert L.sse_trace_read(ms, 9, ctypes.byref(calls)) == INVALID
+    n += 2
+    return n
