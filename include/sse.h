@@ -128,6 +128,30 @@ int sse_forward(const void *q, const void *key_logits, const void *v, const void
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sse_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the workspace taken from a static
+ * device array of the library (sse_forward_noalloc_max_bytes() bytes, 64 MiB,
+ * one copy per device, held until the process ends) instead of a caller
+ * buffer.  The caller still owns every input and output.  Sizes whose
+ * workspace (sse_forward_workspace_bytes) exceeds that limit return
+ * SSE_ERR_WORKSPACE before any HIP call.  No memory is allocated or freed;
+ * the first call on a device looks up that device's array address
+ * (SSE_ERR_HIP if the lookup fails).  Every call on one device shares that
+ * array: calls that overlap in time on one device (concurrent streams or
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero (every pass writes what it later reads).
+ * No grouping debug outputs.
+ */
+size_t sse_forward_noalloc_max_bytes(void);
+int sse_forward_noalloc(const void *q, const void *key_logits, const void *v,
+                        const void *log_alpha, const void *router_logits, int dtype,
+                        const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+                        int64_t total_tokens, int H, int c, int d, int N, int topk,
+                        const float *initial_states, float *o, float *final_states,
+                        int32_t *topk_idx, float *topk_w, void *stream);
+
+/*
  * One decode step (§2.6: decoding recurs only on the selected states).
  * B independent sequences, one new token each, for every head.
  *   q, key_logits, log_alpha  [B, H, c]   (dtype)

@@ -24,6 +24,7 @@ SSE_OK, SSE_ERR_INVALID_ARG, SSE_ERR_UNSUPPORTED, SSE_ERR_WORKSPACE, SSE_ERR_HIP
 SSE_F32, SSE_BF16 = 0, 1
 
 EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
+            "sse_forward_noalloc_max_bytes", "sse_forward_noalloc",
             "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
             "sse_group_by_partition", "sse_trace_enable", "sse_trace_read")
 
@@ -56,6 +57,11 @@ def lib():
     L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
                               P, P, P, SZ, P]
     L.sse_forward.restype = I
+    L.sse_forward_noalloc_max_bytes.argtypes = []
+    L.sse_forward_noalloc_max_bytes.restype = SZ
+    L.sse_forward_noalloc.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
+                                      P, P]
+    L.sse_forward_noalloc.restype = I
     L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
     L.sse_decode_step.restype = I
     L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
@@ -153,6 +159,41 @@ def sse_forward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens,
                            _ptr(seg_tok), _ptr(seg_slot), _ptr(workspace), workspace.numel(),
                            _stream(dev))
     _check(st, "sse_forward")
+    return o, final_states
+
+
+def sse_forward_noalloc_max_bytes() -> int:
+    return int(lib().sse_forward_noalloc_max_bytes())
+
+
+def sse_forward_noalloc(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens,
+                        max_seqlen, o, final_states, initial_states=None, *, topk_idx=None,
+                        topk_w=None):
+    """sse_forward with the library's static workspace: the caller passes
+    every output (o [T,H,d], final_states [S,H,N+1,c,d] fp32) and the host
+    max_seqlen, and nothing is allocated.  Raises SSEError
+    (SSE_ERR_WORKSPACE) when the sizes need more than
+    sse_forward_noalloc_max_bytes() of workspace."""
+    dev = q.device
+    T, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (T, H, c), "q"), (key_logits, (T, H, c), "key_logits"),
+                       (log_alpha, (T, H, c), "log_alpha"), (v, (T, H, d), "v"),
+                       (router_logits, (T, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    _need(o, (T, H, d), torch.float32, "o", dev)
+    _need(final_states, (S, H, N + 1, c, d), torch.float32, "final_states", dev)
+    if initial_states is not None:
+        _need(initial_states, (S, H, N + 1, c, d), torch.float32, "initial_states", dev)
+    st = lib().sse_forward_noalloc(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                                   _ptr(router_logits), _dtype_code(q), _ptr(cu_seqlens), S,
+                                   int(max_seqlen), T, H, c, d, N, topk, _ptr(initial_states),
+                                   _ptr(o), _ptr(final_states), _ptr(topk_idx), _ptr(topk_w),
+                                   _stream(dev))
+    _check(st, "sse_forward_noalloc")
     return o, final_states
 
 

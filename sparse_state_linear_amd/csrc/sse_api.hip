@@ -4,8 +4,14 @@
 // reported without touching a device.
 #include <limits.h>
 
+#include <mutex>
+
 #include "sse.h"
 #include "sse_launch.h"
+
+// Workspace of sse_forward_noalloc (see scratch_ptr below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -94,37 +100,38 @@ inline void trace_mark(int mark, hipStream_t s) {
     if (g_trace.on) (void)hipEventRecord(g_trace.ev[g_trace.calls % kTraceCalls][mark], s);
 }
 
-}  // namespace
+// ---- no-allocation forward: the workspace in a static device array ----------
+// Callers that cannot allocate device memory (code under graph capture,
+// serving loops, harnesses that forbid hipMalloc) use sse_forward_noalloc,
+// whose workspace is this array.  Each device that loads the library holds
+// its own copy until the process ends; host code reaches a device's copy
+// only through the address hipGetSymbolAddress returns for it (the array's
+// name is a host-side stand-in, not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
 
-extern "C" {
-
-const char* sse_status_string(int status) {
-    switch (status) {
-        case SSE_OK: return "SSE_OK";
-        case SSE_ERR_INVALID_ARG: return "SSE_ERR_INVALID_ARG: null pointer or inconsistent size";
-        case SSE_ERR_UNSUPPORTED: return "SSE_ERR_UNSUPPORTED: size outside the supported set";
-        case SSE_ERR_WORKSPACE: return "SSE_ERR_WORKSPACE: workspace too small";
-        case SSE_ERR_HIP: return "SSE_ERR_HIP: a HIP launch failed";
-        default: return "SSE_ERR_UNKNOWN";
+// Device address of the current device's scratch array (looked up once per
+// device), or null on a HIP error.
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
     }
+    return g_scratch_ptr[dev];
 }
 
-int sse_version(void) { return 100; }
-
-size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
-                                   int c, int d, int N, int topk) {
-    if (check_common(SSE_BF16, H, c, d, N, topk) != SSE_OK) return 0;
-    FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L)) return 0;
-    return L.total;
-}
-
-int sse_forward(const void* q, const void* key_logits, const void* v, const void* log_alpha,
-                const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
-                int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
-                const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
-                float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
-                void* workspace, size_t workspace_bytes, void* stream) {
+int forward_impl(const void* q, const void* key_logits, const void* v, const void* log_alpha,
+                 const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
+                 int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                 const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
+                 float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
+                 void* workspace, size_t workspace_bytes, void* stream,
+                 bool use_scratch = false) {
     int st = check_common(dtype, H, c, d, N, topk);
     if (st != SSE_OK) return st;
     if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
@@ -140,6 +147,13 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     // [T, H, topk, d] fp32 must fit in 32 bits
     if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
     if (total_tokens * H * topk * d >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
+    if (use_scratch) {
+        // every argument is checked; now the static array (no allocation)
+        if (L.total > kScratchBytes) return SSE_ERR_WORKSPACE;
+        workspace = scratch_ptr();
+        if (!workspace) return SSE_ERR_HIP;
+        workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -214,6 +228,57 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     trace_mark(5, s);
     if (g_trace.on) g_trace.calls++;
     return SSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sse_status_string(int status) {
+    switch (status) {
+        case SSE_OK: return "SSE_OK";
+        case SSE_ERR_INVALID_ARG: return "SSE_ERR_INVALID_ARG: null pointer or inconsistent size";
+        case SSE_ERR_UNSUPPORTED: return "SSE_ERR_UNSUPPORTED: size outside the supported set";
+        case SSE_ERR_WORKSPACE: return "SSE_ERR_WORKSPACE: workspace too small";
+        case SSE_ERR_HIP: return "SSE_ERR_HIP: a HIP launch failed";
+        default: return "SSE_ERR_UNKNOWN";
+    }
+}
+
+int sse_version(void) { return 100; }
+
+size_t sse_forward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                   int c, int d, int N, int topk) {
+    if (check_common(SSE_BF16, H, c, d, N, topk) != SSE_OK) return 0;
+    FwdLayout L;
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L)) return 0;
+    return L.total;
+}
+
+int sse_forward(const void* q, const void* key_logits, const void* v, const void* log_alpha,
+                const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
+                int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
+                float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
+                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
+                        final_states, topk_idx, topk_w, seg_offsets, seg_tok, seg_slot, workspace,
+                        workspace_bytes, stream);
+}
+
+size_t sse_forward_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int sse_forward_noalloc(const void* q, const void* key_logits, const void* v,
+                        const void* log_alpha, const void* router_logits, int dtype,
+                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                        int64_t total_tokens, int H, int c, int d, int N, int topk,
+                        const float* initial_states, float* o, float* final_states,
+                        int32_t* topk_idx, float* topk_w, void* stream) {
+    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
+                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
+                        final_states, topk_idx, topk_w, nullptr, nullptr, nullptr, nullptr, 0,
+                        stream, true);
 }
 
 int sse_trace_enable(int enable) {

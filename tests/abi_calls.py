@@ -21,6 +21,11 @@ def declare(L):
     L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
                               P, P, P, SZ, P]
     L.sse_forward.restype = I
+    L.sse_forward_noalloc_max_bytes.argtypes = []
+    L.sse_forward_noalloc_max_bytes.restype = SZ
+    L.sse_forward_noalloc.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
+                                      P, P]
+    L.sse_forward_noalloc.restype = I
     L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
     L.sse_decode_step.restype = I
     L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
@@ -57,6 +62,25 @@ FORWARD_REJECTS = [
     (dict(wsb=16), WORKSPACE), (dict(ws=None), WORKSPACE),
 ]
 
+
+def forward_noalloc(L, **kw):
+    a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, z=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16,
+             T=16, H=2, c=32, d=32, N=4, k=2, init=None, o=FAKE, fs=FAKE, idx=None, w=None,
+             stream=None)
+    a.update(kw)
+    return L.sse_forward_noalloc(a["q"], a["kl"], a["v"], a["la"], a["z"], a["dtype"], a["cu"],
+                                 a["S"], a["maxlen"], a["T"], a["H"], a["c"], a["d"], a["N"],
+                                 a["k"], a["init"], a["o"], a["fs"], a["idx"], a["w"],
+                                 a["stream"])
+
+
+NOALLOC_REJECTS = [
+    (dict(q=None), INVALID), (dict(fs=None), INVALID), (dict(k=5), INVALID),
+    (dict(c=48), UNSUPPORTED),
+    # workspace beyond the static array: 8 sequences x 16 heads x 8192 tokens
+    (dict(T=65536, S=8, maxlen=8192, H=16, c=128, d=128, N=16), WORKSPACE),
+]
+
 DECODE_REJECTS = [
     (dict(states=None), INVALID), (dict(B=-1), INVALID), (dict(c=16), UNSUPPORTED),
     (dict(k=3, N=2), INVALID), (dict(B=1 << 30, H=256), UNSUPPORTED),
@@ -80,6 +104,11 @@ def exercise(L) -> int:
         n += 1
     for kw, code in FORWARD_REJECTS:
         got = forward(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    assert L.sse_forward_noalloc_max_bytes() == 64 << 20
+    for kw, code in NOALLOC_REJECTS:
+        got = forward_noalloc(L, **kw)
         assert got == code, (kw, got, code)
         n += 1
     for kw, code in DECODE_REJECTS:
