@@ -60,6 +60,8 @@ def load(path: str | None = None):
     lib.sse_oracle_decode_step.restype = I
     lib.sse_oracle_group.argtypes = [P, P, I, I, I, I, P, P, P]
     lib.sse_oracle_group.restype = I
+    lib.sse_oracle_rowsparse_forward.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
+    lib.sse_oracle_rowsparse_forward.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -168,3 +170,33 @@ def group(topk_idx, cu_seqlens, N, lib=None):
     slot = np.zeros(T * H * k, np.int32)
     lib.sse_oracle_group(_ptr(idx), _ptr(cu), S, H, N, k, _ptr(off), _ptr(tok), _ptr(slot))
     return off, tok, slot
+
+
+def rowsparse_forward(q, key_logits, v, log_alpha, cu_seqlens, row_topk, identity_unselected=True,
+                      initial_states=None, lib=None):
+    """Row-sparse top-k key variant (single state per head).  Inputs
+    [T_tot, H, .] (fp32 or bf16 bits).  Returns a dict of fp64 o [T_tot,H,d]
+    and final_states [S,H,c,d]."""
+    lib = lib or load()
+    dt, q = _raw(q)
+    arrs = [_raw(a) for a in (key_logits, v, log_alpha)]
+    if any(a[0] != dt for a in arrs):
+        raise TypeError("all inputs must share one dtype")
+    kl, v, la = (a[1] for a in arrs)
+    T, H, c = q.shape
+    d = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    S = cu.shape[0] - 1
+    assert kl.shape == (T, H, c) and la.shape == (T, H, c) and int(cu[-1]) == T
+    init = None
+    if initial_states is not None:
+        init = np.ascontiguousarray(initial_states, dtype=np.float64)
+        assert init.shape == (S, H, c, d)
+    o = np.empty((T, H, d), np.float64)
+    fs = np.empty((S, H, c, d), np.float64)
+    rc = lib.sse_oracle_rowsparse_forward(dt, _ptr(q), _ptr(kl), _ptr(v), _ptr(la), _ptr(cu), S,
+                                          H, c, d, int(row_topk), int(bool(identity_unselected)),
+                                          _ptr(init), _ptr(o), _ptr(fs))
+    if rc != 0:
+        raise ValueError("sse_oracle_rowsparse_forward rejected its arguments")
+    return {"o": o, "final_states": fs}

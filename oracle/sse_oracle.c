@@ -355,3 +355,98 @@ int sse_oracle_group(const int32_t *topk_idx, const int32_t *cu_seqlens, int num
     seg_offsets[(int64_t)num_seqs * H * N] = (int32_t)pos;
     return 0;
 }
+
+/*
+ * Row-sparse key variant (§2.2, eqs. (7)-(8)): one state per head.  The key
+ * keeps the k largest of the c key logits (descending, equal logits -> lower
+ * row first) and is the softmax over those rows, zero on the others:
+ *     kappa_j = exp(kl_j) / sum_{i in top} exp(kl_i)   (j in top), 0 otherwise.
+ * The update is S = Lambda~ S + kappa^T v with Lambda~ = diag(alpha) on the
+ * selected rows and, when identity_unselected is set, the identity on the
+ * other rows (the "no forgetting of unselected rows" form the page says
+ * needs an identity transition; otherwise every row decays, the plain
+ * zeroed-key form).  o = q S, read after the write.
+ *   S: [c, d] fp64, in = initial state, out = final state; o: [(t1-t0), d]
+ */
+int sse_oracle_rowsparse_unit(int dtype, const void *q, const void *key_logits, const void *v,
+                              const void *log_alpha, int64_t t0, int64_t t1, int h, int H, int c,
+                              int d, int k, int identity_unselected, double *S, double *o)
+{
+    if (k < 1 || k > c || c < 1 || d < 1 || h < 0 || h >= H || t1 < t0 || c > ORACLE_MAX_N)
+        return -1;
+    double qq[ORACLE_MAX_N], kk[ORACLE_MAX_N], ll[ORACLE_MAX_N], kappa[ORACLE_MAX_N];
+    int top[ORACLE_MAX_N];
+    unsigned char sel[ORACLE_MAX_N];
+    double *vv = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!vv)
+        return -1;
+    for (int64_t t = t0; t < t1; t++) {
+        int64_t rc = (t * H + h) * (int64_t)c, rd = (t * H + h) * (int64_t)d;
+        for (int j = 0; j < c; j++) {
+            qq[j] = load_value(q, dtype, rc + j);
+            kk[j] = load_value(key_logits, dtype, rc + j);
+            ll[j] = load_value(log_alpha, dtype, rc + j);
+        }
+        for (int m = 0; m < d; m++)
+            vv[m] = load_value(v, dtype, rd + m);
+        /* eq. (7): top-k of the key logits, then the softmax over them */
+        top_k(kk, c, k, top);
+        memset(sel, 0, sizeof sel);
+        for (int r = 0; r < k; r++)
+            sel[top[r]] = 1;
+        double mx = kk[top[0]], z = 0.0;
+        for (int r = 0; r < k; r++)
+            z += exp(kk[top[r]] - mx);
+        for (int j = 0; j < c; j++)
+            kappa[j] = sel[j] ? exp(kk[j] - mx) / z : 0.0;
+        /* eq. (8) with the transition of the selected rows only */
+        for (int j = 0; j < c; j++) {
+            double a = (sel[j] || !identity_unselected) ? exp(ll[j]) : 1.0;
+            for (int m = 0; m < d; m++)
+                S[(int64_t)j * d + m] = a * S[(int64_t)j * d + m] + kappa[j] * vv[m];
+        }
+        for (int m = 0; m < d; m++) {
+            double acc = 0.0;
+            for (int j = 0; j < c; j++)
+                acc += qq[j] * S[(int64_t)j * d + m];
+            o[(t - t0) * d + m] = acc;
+        }
+    }
+    free(vv);
+    return 0;
+}
+
+/* Varlen row-sparse forward over sequences [cu[s], cu[s+1]), every head.
+ *   init: [S, H, c, d] or NULL (zeros); o: [T_tot, H, d]; fs: [S, H, c, d] */
+int sse_oracle_rowsparse_forward(int dtype, const void *q, const void *key_logits, const void *v,
+                                 const void *log_alpha, const int32_t *cu_seqlens, int num_seqs,
+                                 int H, int c, int d, int k, int identity_unselected,
+                                 const double *init, double *o, double *final_states)
+{
+    const int64_t cd = (int64_t)c * d;
+    for (int s = 0; s < num_seqs; s++) {
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+        int64_t t0 = cu_seqlens[s], t1 = cu_seqlens[s + 1], L = t1 - t0;
+        double *ou = (double *)malloc(sizeof(double) * (size_t)(L * d + 1));
+        if (!ou)
+            return -1;
+        for (int h = 0; h < H; h++) {
+            double *S = final_states + ((int64_t)s * H + h) * cd;
+            if (init)
+                memcpy(S, init + ((int64_t)s * H + h) * cd, sizeof(double) * (size_t)cd);
+            else
+                memset(S, 0, sizeof(double) * (size_t)cd);
+            int rc = sse_oracle_rowsparse_unit(dtype, q, key_logits, v, log_alpha, t0, t1, h, H,
+                                               c, d, k, identity_unselected, S, ou);
+            if (rc) {
+                free(ou);
+                return rc;
+            }
+            for (int64_t t = 0; t < L; t++)
+                memcpy(o + ((t0 + t) * H + h) * d, ou + t * d, sizeof(double) * (size_t)d);
+        }
+        free(ou);
+    }
+    return 0;
+}

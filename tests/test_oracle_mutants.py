@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from pins import PINS
+from pins_rowsparse import ROWSPARSE_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sse_oracle.c")
 
@@ -42,6 +43,17 @@ MUTANTS = {
     "state_reset_missing": ("memset(S, 0, sizeof(double) * (size_t)st);", "(void)0;"),
     "init_ignored": ("memcpy(S, J->init + (int64_t)u * st, sizeof(double) * (size_t)st);",
                      "memset(S, 0, sizeof(double) * (size_t)st);"),
+    # row-sparse key variant
+    "rowsparse_unselected_decay": ("double a = (sel[j] || !identity_unselected) ? exp(ll[j]) : 1.0;",
+                                   "double a = exp(ll[j]);"),
+    "rowsparse_softmax_over_all_rows": ("kappa[j] = sel[j] ? exp(kk[j] - mx) / z : 0.0;",
+                                        "kappa[j] = sel[j] ? exp(kk[j] - mx) / (z + 1.0) : 0.0;"),
+    "rowsparse_dense_key": ("kappa[j] = sel[j] ? exp(kk[j] - mx) / z : 0.0;",
+                            "kappa[j] = exp(kk[j] - mx) / z;"),
+    "rowsparse_selected_rows_no_decay": ("double a = (sel[j] || !identity_unselected) ? exp(ll[j]) : 1.0;",
+                                         "double a = (!sel[j] && !identity_unselected) ? exp(ll[j]) : 1.0;"),
+    "rowsparse_read_before_write": ("            o[(t - t0) * d + m] = acc;",
+                                    "            o[(t - t0) * d + m] = acc - qq[0] * kappa[0] * vv[m];"),
 }
 
 
@@ -56,7 +68,7 @@ def test_mutant_is_caught(name, tmp_path):
                       extra_flags=("-Wno-error", "-w"))
     lib = oracle.load(so)
     failed = []
-    for pin in PINS:
+    for pin in PINS + ROWSPARSE_PINS:
         try:
             pin(lib)
         except (AssertionError, ValueError, IndexError, FloatingPointError):

@@ -2,8 +2,11 @@
 import pytest
 
 from pins import PINS
+from pins_rowsparse import ROWSPARSE_PINS
+
+ALL = PINS + ROWSPARSE_PINS
 
 
-@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+@pytest.mark.parametrize("pin", ALL, ids=[p.__name__ for p in ALL])
 def test_pin(pin, oracle_lib):
     pin(oracle_lib)
