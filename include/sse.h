@@ -209,6 +209,33 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Row-sparse top-k key variant (§2.2, eqs. (7)-(8)): one state per head,
+ * no partitions.  Per token t and head h:
+ *   kappa_t = softmax over the row_topk largest key logits (descending,
+ *             equal logits -> lower row first); zero on the other rows
+ *   S       = Lambda~_t S + kappa_t^T v_t,  o_t = q_t S (read after write)
+ * where Lambda~_t = diag(alpha_t) on the selected rows and, with
+ * identity_unselected != 0, the identity on the other rows (their memory is
+ * neither written nor decayed: the no-forgetting form, which needs the
+ * identity transition); with identity_unselected = 0 every row decays.
+ *   q, key_logits, log_alpha  [total_tokens, H, c]; v [total_tokens, H, d]
+ *   initial_states            [num_seqs, H, c, d] fp32 or NULL (zeros)
+ *   o                         [total_tokens, H, d] fp32 (written)
+ *   final_states              [num_seqs, H, c, d] fp32 (written)
+ *   1 <= row_topk <= c; workspace >= sse_rowsparse_workspace_bytes(...).
+ * Same conventions, checks and preconditions as sse_forward (the decay
+ * bound applies to the masked log decay).  Deterministic.
+ */
+size_t sse_rowsparse_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                     int c, int d);
+int sse_rowsparse_forward(const void *q, const void *key_logits, const void *v,
+                          const void *log_alpha, int dtype, const int32_t *cu_seqlens,
+                          int num_seqs, int max_seqlen, int64_t total_tokens, int H, int c, int d,
+                          int row_topk, int identity_unselected, const float *initial_states,
+                          float *o, float *final_states, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * Stage tracing (profiling aid, not part of the method).  While enabled,
  * every sse_forward records HIP events on its stream around its five
  * stages: 0 = routing + per-block counts (+ key-softmax normalisers for fp32

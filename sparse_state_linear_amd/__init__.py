@@ -26,7 +26,8 @@ SSE_F32, SSE_BF16 = 0, 1
 EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
             "sse_forward_noalloc_max_bytes", "sse_forward_noalloc",
             "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
-            "sse_group_by_partition", "sse_trace_enable", "sse_trace_read")
+            "sse_group_by_partition", "sse_rowsparse_workspace_bytes", "sse_rowsparse_forward",
+            "sse_trace_enable", "sse_trace_read")
 
 _lib = None
 
@@ -70,6 +71,11 @@ def lib():
     L.sse_group_workspace_bytes.restype = SZ
     L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
     L.sse_group_by_partition.restype = I
+    L.sse_rowsparse_workspace_bytes.argtypes = [I64, I, I, I, I, I]
+    L.sse_rowsparse_workspace_bytes.restype = SZ
+    L.sse_rowsparse_forward.argtypes = [P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
+                                        SZ, P]
+    L.sse_rowsparse_forward.restype = I
     L.sse_trace_enable.argtypes = [I]
     L.sse_trace_enable.restype = I
     L.sse_trace_read.argtypes = [P, I, P]
@@ -262,6 +268,47 @@ def sse_group_by_partition(topk_idx, topk_w, cu_seqlens, N, max_seqlen=None):
                                       _ptr(slot), _ptr(sw), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "sse_group_by_partition")
     return off, tok, slot, sw
+
+
+def sse_rowsparse_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d) -> int:
+    return int(lib().sse_rowsparse_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d))
+
+
+def sse_rowsparse_forward(q, key_logits, v, log_alpha, row_topk, cu_seqlens, max_seqlen=None,
+                          initial_states=None, identity_unselected=True, *, o=None,
+                          final_states=None, workspace=None):
+    """Row-sparse top-k key variant: one state per head, key = softmax over
+    the row_topk largest key logits, unselected rows keep their state
+    (identity_unselected) or decay.  q/key_logits/log_alpha [T,H,c], v [T,H,d]
+    (bf16 or fp32), cu_seqlens int32 [S+1].  Returns (o [T,H,d], final_states
+    [S,H,c,d]) in fp32."""
+    dev = q.device
+    T, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (T, H, c), "q"), (key_logits, (T, H, c), "key_logits"),
+                       (log_alpha, (T, H, c), "log_alpha"), (v, (T, H, d), "v")):
+        _need(t, shp, dt, nm, dev)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S > 0 else 0
+    if initial_states is not None:
+        _need(initial_states, (S, H, c, d), torch.float32, "initial_states", dev)
+    if o is None:
+        o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, c, d), dtype=torch.float32, device=dev)
+    nbytes = sse_rowsparse_workspace_bytes(T, S, max_seqlen, H, c, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sse_rowsparse_forward(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                                     _dtype_code(q), _ptr(cu_seqlens), S, int(max_seqlen), T, H,
+                                     c, d, int(row_topk), int(bool(identity_unselected)),
+                                     _ptr(initial_states), _ptr(o), _ptr(final_states),
+                                     _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "sse_rowsparse_forward")
+    return o, final_states
 
 
 TRACE_STAGES = ("route_count", "piece_state", "group", "routed", "shared")

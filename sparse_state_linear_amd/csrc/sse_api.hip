@@ -86,6 +86,38 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSE_OK : SSE_ERR_HIP; }
 
+// Workspace of the row-sparse forward: the masked key logits and log decay
+// (fp32-sized rows, either input type), the key normalisers, the shared
+// pieces' aggregates, a dummy output row and one slot row (no routed reads).
+struct RsLayout {
+    size_t kl, la, lnz2, agg_S, agg_D, trash, part, total;
+};
+
+bool rowsparse_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, RsLayout& L) {
+    if (T < 0 || S < 0 || max_seqlen < 0 || H < 1) return false;
+    if (T >= INT_MAX || (int64_t)S * H >= INT_MAX) return false;
+    const int64_t maxp = max_pieces(max_seqlen, shared_piece_len(S, H, max_seqlen));
+    if (maxp >= 65536) return false;
+    size_t off = 0;
+    L.kl = off;    off += align_up(sizeof(float) * (size_t)(T * H * c));
+    L.la = off;    off += align_up(sizeof(float) * (size_t)(T * H * c));
+    L.lnz2 = off;  off += align_up(sizeof(float) * (size_t)(T * H));
+    L.agg_S = off; off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
+    L.agg_D = off; off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
+    L.trash = off; off += align_up(sizeof(float) * (size_t)(2 * d));
+    L.part = off;  off += align_up(sizeof(float) * (size_t)d);
+    L.total = off;
+    return true;
+}
+
+int check_rowsparse(int dtype, int H, int c, int d, int row_topk) {
+    if (dtype != SSE_F32 && dtype != SSE_BF16) return SSE_ERR_INVALID_ARG;
+    if (H < 1 || c < 1 || d < 1 || row_topk < 1 || row_topk > c) return SSE_ERR_INVALID_ARG;
+    if (!supported_dim(c) || !supported_dim(d)) return SSE_ERR_UNSUPPORTED;
+    if (H > sse::kMaxH) return SSE_ERR_UNSUPPORTED;
+    return SSE_OK;
+}
+
 // ---- stage tracing: a ring of per-call HIP events (profiling aid) ----------
 constexpr int kTraceCalls = 256;
 constexpr int kTraceMarks = SSE_TRACE_STAGES + 1;
@@ -279,6 +311,67 @@ int sse_forward_noalloc(const void* q, const void* key_logits, const void* v,
                         max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
                         final_states, topk_idx, topk_w, nullptr, nullptr, nullptr, nullptr, 0,
                         stream, true);
+}
+
+size_t sse_rowsparse_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                     int c, int d) {
+    if (check_rowsparse(SSE_BF16, H, c, d, 1) != SSE_OK) return 0;
+    RsLayout L;
+    if (!rowsparse_layout(total_tokens, num_seqs, max_seqlen, H, c, d, L)) return 0;
+    return L.total;
+}
+
+int sse_rowsparse_forward(const void* q, const void* key_logits, const void* v,
+                          const void* log_alpha, int dtype, const int32_t* cu_seqlens, int num_seqs,
+                          int max_seqlen, int64_t total_tokens, int H, int c, int d, int row_topk,
+                          int identity_unselected, const float* initial_states, float* o,
+                          float* final_states, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    int st = check_rowsparse(dtype, H, c, d, row_topk);
+    if (st != SSE_OK) return st;
+    if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
+    if (total_tokens > 0 && num_seqs == 0) return SSE_ERR_INVALID_ARG;
+    if (!cu_seqlens) return SSE_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !key_logits || !v || !log_alpha || !o)) return SSE_ERR_INVALID_ARG;
+    if (num_seqs > 0 && !final_states) return SSE_ERR_INVALID_ARG;
+    RsLayout L;
+    if (!rowsparse_layout(total_tokens, num_seqs, max_seqlen, H, c, d, L)) return SSE_ERR_UNSUPPORTED;
+    if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    sse::ChunkArgs a = {};
+    a.q = q;
+    a.kl = ws + L.kl;
+    a.v = v;
+    a.la = ws + L.la;
+    a.cu = cu_seqlens;
+    a.lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
+    a.lnz2_out = reinterpret_cast<float*>(ws + L.lnz2);
+    a.init = initial_states;
+    a.o = o;
+    a.final_states = final_states;
+    a.agg_S = reinterpret_cast<float*>(ws + L.agg_S);
+    a.agg_D = reinterpret_cast<float*>(ws + L.agg_D);
+    a.trash = reinterpret_cast<float*>(ws + L.trash);
+    a.part = reinterpret_cast<float*>(ws + L.part);
+    a.part_scale = reinterpret_cast<float*>(ws + L.part + sizeof(int16_t) * (size_t)d);
+    a.slot_rows = 0;
+    a.rows = (uint32_t)(total_tokens * H);
+    a.num_seqs = num_seqs;
+    a.H = H;
+    a.N = 0;       // the single state is the shared partition's slot
+    a.topk = 0;    // no routed reads to add
+    a.piece_len = shared_piece_len(num_seqs, H, max_seqlen);
+    a.max_pieces = max_pieces(max_seqlen, a.piece_len);
+    hipError_t e = sse::launch_rowsparse_mask(key_logits, log_alpha, dtype, total_tokens * H, c,
+                                              row_topk, identity_unselected, ws + L.kl,
+                                              ws + L.la, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    if (num_seqs == 0) return SSE_OK;
+    e = sse::launch_chunk_local(a, dtype, c, d, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    return hip_status(sse::launch_chunk_shared(a, dtype, c, d, s));
 }
 
 int sse_trace_enable(int enable) {

@@ -110,6 +110,13 @@ hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipS
 // kModeShared.
 hipError_t launch_chunk_f64(int mode, const ChunkArgs& a, int c, int d, hipStream_t st);
 
+// Row-sparse key variant: per (token, head) row of c key logits, kl_out =
+// kl on the k largest entries (equal values: lower rows first) and -inf
+// elsewhere; la_out = la on those rows and 0 elsewhere (identity != 0) or la
+// everywhere.  Inputs and outputs in the storage type of dtype.
+hipError_t launch_rowsparse_mask(const void* kl, const void* la, int dtype, int64_t rows, int c,
+                                 int k, int identity, void* kl_out, void* la_out, hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* kl, const void* v, const void* la,
                          const void* z, int dtype, int B, int H, int c, int d, int N, int K,
                          float* states, float* o, int32_t* topk_idx, hipStream_t st);

@@ -34,6 +34,11 @@ def declare(L):
     L.sse_group_workspace_bytes.restype = SZ
     L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
     L.sse_group_by_partition.restype = I
+    L.sse_rowsparse_workspace_bytes.argtypes = [I64, I, I, I, I, I]
+    L.sse_rowsparse_workspace_bytes.restype = SZ
+    L.sse_rowsparse_forward.argtypes = [P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
+                                        SZ, P]
+    L.sse_rowsparse_forward.restype = I
     L.sse_trace_read.argtypes = [P, I, P]
     L.sse_trace_read.restype = I
 
@@ -81,6 +86,24 @@ NOALLOC_REJECTS = [
     (dict(T=65536, S=8, maxlen=8192, H=16, c=128, d=128, N=16), WORKSPACE),
 ]
 
+def rowsparse(L, **kw):
+    a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16, T=16, H=2,
+             c=32, d=32, k=8, ident=1, init=None, o=FAKE, fs=FAKE, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return L.sse_rowsparse_forward(a["q"], a["kl"], a["v"], a["la"], a["dtype"], a["cu"], a["S"],
+                                   a["maxlen"], a["T"], a["H"], a["c"], a["d"], a["k"],
+                                   a["ident"], a["init"], a["o"], a["fs"], a["ws"], a["wsb"],
+                                   a["stream"])
+
+
+ROWSPARSE_REJECTS = [
+    (dict(q=None), INVALID), (dict(la=None), INVALID), (dict(fs=None), INVALID),
+    (dict(k=0), INVALID), (dict(k=33), INVALID), (dict(dtype=3), INVALID), (dict(S=0), INVALID),
+    (dict(c=48), UNSUPPORTED), (dict(H=300), UNSUPPORTED), (dict(wsb=8), WORKSPACE),
+    (dict(T=1 << 26, S=1, maxlen=1 << 26, H=16, c=128, d=128), UNSUPPORTED),
+]
+
 DECODE_REJECTS = [
     (dict(states=None), INVALID), (dict(B=-1), INVALID), (dict(c=16), UNSUPPORTED),
     (dict(k=3, N=2), INVALID), (dict(B=1 << 30, H=256), UNSUPPORTED),
@@ -113,6 +136,10 @@ def exercise(L) -> int:
         n += 1
     for kw, code in DECODE_REJECTS:
         got = decode(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    for kw, code in ROWSPARSE_REJECTS:
+        got = rowsparse(L, **kw)
         assert got == code, (kw, got, code)
         n += 1
     # workspace queries, including sizes that overflow the kernels' indexing
