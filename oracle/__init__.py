@@ -62,6 +62,9 @@ def load(path: str | None = None):
     lib.sse_oracle_group.restype = I
     lib.sse_oracle_rowsparse_forward.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
     lib.sse_oracle_rowsparse_forward.restype = I
+    lib.sse_oracle_forward_ex.argtypes = [I, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P,
+                                          P, P, P, P]
+    lib.sse_oracle_forward_ex.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -200,3 +203,43 @@ def rowsparse_forward(q, key_logits, v, log_alpha, cu_seqlens, row_topk, identit
     if rc != 0:
         raise ValueError("sse_oracle_rowsparse_forward rejected its arguments")
     return {"o": o, "final_states": fs}
+
+
+def forward_ex(q, key_logits, v, log_alpha, router_logits, cu_seqlens, N, topk, q_shared=None,
+               key_logits_shared=None, read_router_logits=None, read_topk=None,
+               initial_states=None, lib=None):
+    """General forward: optional own q / key logits of the shared partition
+    and optional read-set router logits (read_topk partitions read).  Returns
+    a dict of fp64 o [T,H,d], final_states [S,H,N+1,c,d], int32 write_idx
+    [T,H,topk] and read_idx [T,H,read_topk or topk]."""
+    lib = lib or load()
+    dt, q = _raw(q)
+    req = [_raw(a) for a in (key_logits, v, log_alpha, router_logits)]
+    opt = [None if a is None else _raw(a) for a in (q_shared, key_logits_shared,
+                                                     read_router_logits)]
+    if any(a[0] != dt for a in req) or any(a is not None and a[0] != dt for a in opt):
+        raise TypeError("all inputs must share one dtype")
+    kl, v, la, z = (a[1] for a in req)
+    qs, ks, zr = (None if a is None else a[1] for a in opt)
+    T, H, c = q.shape
+    d = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    S = cu.shape[0] - 1
+    assert z.shape == (T, H, N) and int(cu[-1]) == T
+    for a, shp in ((qs, (T, H, c)), (ks, (T, H, c)), (zr, (T, H, N))):
+        assert a is None or a.shape == shp
+    kr = int(read_topk) if zr is not None else int(topk)
+    init = None
+    if initial_states is not None:
+        init = np.ascontiguousarray(initial_states, dtype=np.float64)
+        assert init.shape == (S, H, N + 1, c, d)
+    o = np.empty((T, H, d), np.float64)
+    fs = np.empty((S, H, N + 1, c, d), np.float64)
+    widx = np.empty((T, H, topk), np.int32)
+    ridx = np.empty((T, H, kr), np.int32)
+    rc = lib.sse_oracle_forward_ex(dt, _ptr(q), _ptr(kl), _ptr(v), _ptr(la), _ptr(z), _ptr(qs),
+                                   _ptr(ks), _ptr(zr), kr, _ptr(cu), S, H, c, d, N, topk,
+                                   _ptr(init), _ptr(o), _ptr(fs), _ptr(widx), _ptr(ridx))
+    if rc != 0:
+        raise ValueError("sse_oracle_forward_ex rejected its arguments")
+    return {"o": o, "final_states": fs, "write_idx": widx, "read_idx": ridx}

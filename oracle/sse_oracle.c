@@ -450,3 +450,153 @@ int sse_oracle_rowsparse_forward(int dtype, const void *q, const void *key_logit
     }
     return 0;
 }
+
+/*
+ * General form (§2.5 and §2.3): the shared partition may have its own query
+ * and key (the page gives it rank-64 LoRA projections of its own Q and K;
+ * the projected rows are inputs here), and the partitions read may differ
+ * from those written ("读写集合可以不同,默认相同": the read and write sets may
+ * differ, the same by default).  Per token:
+ *   write set W = top-k of the router logits z, weights e = softmax(z);
+ *   read set  R = top-kr of the read logits zr, weights er = softmax(zr)
+ *             (R = W and er = e when no read logits are given);
+ *   for i in W: S^i = diag(alpha) S^i + e^i kappa^T v;  others unchanged;
+ *   S^sh = diag(alpha) S^sh + kappa_sh^T v, kappa_sh = softmax(kl_sh);
+ *   o = sum_{i in R} er^i q S^i + q_sh S^sh  (every read after the writes).
+ * Reads of a partition not written at this token see its unchanged state.
+ * Inputs of the optional pieces may be NULL: q_sh -> q, kl_sh -> kl,
+ * zr -> none (kr ignored).  Outputs: o [(t1-t0), d]; wsel, rsel [(t1-t0), k]
+ * and [(t1-t0), kr].
+ */
+int sse_oracle_unit_ex(int dtype, const void *q, const void *key_logits, const void *v,
+                       const void *log_alpha, const void *router_logits, const void *q_sh,
+                       const void *key_logits_sh, const void *read_logits, int kr, int64_t t0,
+                       int64_t t1, int h, int H, int c, int d, int N, int k, double *S, double *o,
+                       int32_t *wsel, int32_t *rsel)
+{
+    if (N < 1 || N > ORACLE_MAX_N || k < 1 || k > N || c < 1 || d < 1 || c > ORACLE_MAX_N ||
+        h < 0 || h >= H || t1 < t0)
+        return -1;
+    if (read_logits && (kr < 1 || kr > N))
+        return -1;
+    const int krr = read_logits ? kr : k;
+    const int64_t cd = (int64_t)c * d;
+    double z[ORACLE_MAX_N], zr[ORACLE_MAX_N], e[ORACLE_MAX_N], er[ORACLE_MAX_N];
+    double qq[ORACLE_MAX_N], qs[ORACLE_MAX_N], kk[ORACLE_MAX_N], ks[ORACLE_MAX_N];
+    double ll[ORACLE_MAX_N], kap[ORACLE_MAX_N], kaps[ORACLE_MAX_N], alpha[ORACLE_MAX_N];
+    int W[ORACLE_MAX_N], R[ORACLE_MAX_N];
+    double *vv = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!vv)
+        return -1;
+    for (int64_t t = t0; t < t1; t++) {
+        int64_t rc = (t * H + h) * (int64_t)c, rd = (t * H + h) * (int64_t)d,
+                rn = (t * H + h) * (int64_t)N;
+        for (int i = 0; i < N; i++) {
+            z[i] = load_value(router_logits, dtype, rn + i);
+            zr[i] = read_logits ? load_value(read_logits, dtype, rn + i) : z[i];
+        }
+        for (int j = 0; j < c; j++) {
+            qq[j] = load_value(q, dtype, rc + j);
+            qs[j] = q_sh ? load_value(q_sh, dtype, rc + j) : qq[j];
+            kk[j] = load_value(key_logits, dtype, rc + j);
+            ks[j] = key_logits_sh ? load_value(key_logits_sh, dtype, rc + j) : kk[j];
+            ll[j] = load_value(log_alpha, dtype, rc + j);
+        }
+        for (int m = 0; m < d; m++)
+            vv[m] = load_value(v, dtype, rd + m);
+        softmax(z, N, e);                 /* eq. (9), write weights */
+        top_k(z, N, k, W);                /* eq. (10), write set */
+        softmax(zr, N, er);               /* read weights */
+        top_k(zr, N, krr, R);             /* read set */
+        softmax(kk, c, kap);              /* eq. (11) */
+        softmax(ks, c, kaps);             /* the shared partition's own key */
+        for (int j = 0; j < c; j++)
+            alpha[j] = exp(ll[j]);
+        /* writes: eq. (12) on the write set, the shared partition always */
+        for (int r = 0; r < k + 1; r++) {
+            const int part = (r < k) ? W[r] : N;
+            const double ww = (r < k) ? e[part] : 1.0;
+            const double *key = (r < k) ? kap : kaps;
+            double *Sw = S + (int64_t)part * cd;
+            for (int j = 0; j < c; j++)
+                for (int m = 0; m < d; m++)
+                    Sw[(int64_t)j * d + m] = alpha[j] * Sw[(int64_t)j * d + m] + ww * key[j] * vv[m];
+        }
+        /* reads: eq. (14) on the read set, plus the shared partition */
+        int64_t lt = t - t0;
+        for (int m = 0; m < d; m++)
+            o[lt * d + m] = 0.0;
+        for (int r = 0; r <= krr; r++) {
+            int part = (r < krr) ? R[r] : N;
+            double w = (r < krr) ? er[part] : 1.0;
+            const double *qv = (r < krr) ? qq : qs;
+            const double *Sp = S + (int64_t)part * cd;
+            for (int m = 0; m < d; m++) {
+                double acc = 0.0;
+                for (int j = 0; j < c; j++)
+                    acc += qv[j] * Sp[(int64_t)j * d + m];
+                o[lt * d + m] += w * acc;
+            }
+        }
+        for (int r = 0; r < k; r++)
+            wsel[lt * k + r] = W[r];
+        for (int r = 0; r < krr; r++)
+            rsel[lt * krr + r] = R[r];
+    }
+    free(vv);
+    return 0;
+}
+
+/* Varlen forward of the general form, sequence by sequence and head by
+ * head.  init [S,H,N+1,c,d] or NULL; o [T,H,d]; fs [S,H,N+1,c,d];
+ * wsel [T,H,k]; rsel [T,H,kr'] with kr' = kr (read logits given) or k. */
+int sse_oracle_forward_ex(int dtype, const void *q, const void *key_logits, const void *v,
+                          const void *log_alpha, const void *router_logits, const void *q_sh,
+                          const void *key_logits_sh, const void *read_logits, int kr,
+                          const int32_t *cu_seqlens, int num_seqs, int H, int c, int d, int N,
+                          int k, const double *init, double *o, double *final_states,
+                          int32_t *wsel, int32_t *rsel)
+{
+    const int64_t st = (int64_t)(N + 1) * c * d;
+    const int krr = read_logits ? kr : k;
+    for (int s = 0; s < num_seqs; s++) {
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+        int64_t t0 = cu_seqlens[s], t1 = cu_seqlens[s + 1], L = t1 - t0;
+        double *ou = (double *)malloc(sizeof(double) * (size_t)(L * d + 1));
+        int32_t *wu = (int32_t *)malloc(sizeof(int32_t) * (size_t)(L * k + 1));
+        int32_t *ru = (int32_t *)malloc(sizeof(int32_t) * (size_t)(L * krr + 1));
+        if (!ou || !wu || !ru) {
+            free(ou);
+            free(wu);
+            free(ru);
+            return -1;
+        }
+        for (int h = 0; h < H; h++) {
+            double *Su = final_states + ((int64_t)s * H + h) * st;
+            if (init)
+                memcpy(Su, init + ((int64_t)s * H + h) * st, sizeof(double) * (size_t)st);
+            else
+                memset(Su, 0, sizeof(double) * (size_t)st);
+            int rc = sse_oracle_unit_ex(dtype, q, key_logits, v, log_alpha, router_logits, q_sh,
+                                        key_logits_sh, read_logits, kr, t0, t1, h, H, c, d, N, k,
+                                        Su, ou, wu, ru);
+            if (rc) {
+                free(ou);
+                free(wu);
+                free(ru);
+                return rc;
+            }
+            for (int64_t t = 0; t < L; t++) {
+                int64_t g = (t0 + t) * H + h;
+                memcpy(o + g * d, ou + t * d, sizeof(double) * (size_t)d);
+                memcpy(wsel + g * k, wu + t * k, sizeof(int32_t) * (size_t)k);
+                memcpy(rsel + g * krr, ru + t * krr, sizeof(int32_t) * (size_t)krr);
+            }
+        }
+        free(ou);
+        free(wu);
+        free(ru);
+    }
+    return 0;
+}

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from pins import PINS
+from pins_ex import EX_PINS
 from pins_rowsparse import ROWSPARSE_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sse_oracle.c")
@@ -52,6 +53,16 @@ MUTANTS = {
                             "kappa[j] = exp(kk[j] - mx) / z;"),
     "rowsparse_selected_rows_no_decay": ("double a = (sel[j] || !identity_unselected) ? exp(ll[j]) : 1.0;",
                                          "double a = (!sel[j] && !identity_unselected) ? exp(ll[j]) : 1.0;"),
+    # general form (own shared q/k, read sets)
+    "ex_shared_uses_routed_key": ("const double *key = (r < k) ? kap : kaps;",
+                                  "const double *key = kap;"),
+    "ex_shared_uses_routed_query": ("const double *qv = (r < krr) ? qq : qs;",
+                                    "const double *qv = qq;"),
+    "ex_read_with_write_weight": ("double w = (r < krr) ? er[part] : 1.0;",
+                                  "double w = (r < krr) ? e[part] : 1.0;"),
+    "ex_read_set_is_write_set": ("top_k(zr, N, krr, R);             /* read set */",
+                                 "top_k(z, N, krr, R);"),
+    "ex_no_shared_read": ("for (int r = 0; r <= krr; r++) {", "for (int r = 0; r < krr; r++) {"),
     "rowsparse_read_before_write": ("            o[(t - t0) * d + m] = acc;",
                                     "            o[(t - t0) * d + m] = acc - qq[0] * kappa[0] * vv[m];"),
 }
@@ -68,7 +79,7 @@ def test_mutant_is_caught(name, tmp_path):
                       extra_flags=("-Wno-error", "-w"))
     lib = oracle.load(so)
     failed = []
-    for pin in PINS + ROWSPARSE_PINS:
+    for pin in PINS + ROWSPARSE_PINS + EX_PINS:
         try:
             pin(lib)
         except (AssertionError, ValueError, IndexError, FloatingPointError):

@@ -2,9 +2,10 @@
 import pytest
 
 from pins import PINS
+from pins_ex import EX_PINS
 from pins_rowsparse import ROWSPARSE_PINS
 
-ALL = PINS + ROWSPARSE_PINS
+ALL = PINS + ROWSPARSE_PINS + EX_PINS
 
 
 @pytest.mark.parametrize("pin", ALL, ids=[p.__name__ for p in ALL])
