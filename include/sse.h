@@ -65,6 +65,12 @@ typedef enum {
 
 typedef enum { SSE_F32 = 0, SSE_BF16 = 1 } sse_dtype;
 
+/* Parallel schedules of the forward (§2.6): varlen gathers each partition's
+ * records into its own segment (one chunked pass over about k L records);
+ * masked runs every partition over every token of the sequence with the
+ * tokens outside its sets masked (no decay, no write, no read). */
+typedef enum { SSE_SCHEDULE_VARLEN = 0, SSE_SCHEDULE_MASKED = 1 } sse_schedule;
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *sse_status_string(int status);
 
@@ -126,6 +132,40 @@ int sse_forward(const void *q, const void *key_logits, const void *v, const void
                 const float *initial_states, float *o, float *final_states, int32_t *topk_idx,
                 float *topk_w, int32_t *seg_offsets, int32_t *seg_tok, int32_t *seg_slot,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * General forward: sse_forward plus the options the page describes beside
+ * the default layer.  Each optional pointer may be NULL (the default):
+ *   q_shared, key_logits_shared  [total_tokens, H, c] (dtype): the shared
+ *             partition's own query and key logits (§2.5: it has rank-64
+ *             LoRA projections of its own Q and K; the projected rows are
+ *             passed here).  NULL -> q / key_logits.
+ *   read_router_logits [total_tokens, H, N] (dtype): logits of the read set
+ *             (§2.3: the read and write sets may differ, the same by
+ *             default).  The read set is the read_topk largest read logits
+ *             (same order and tie rule), read weights their softmax over N;
+ *             the write set and its weights come from router_logits.  A
+ *             partition read but not written at a token is read from its
+ *             unchanged state.  Supported on the masked schedule only
+ *             (SSE_ERR_UNSUPPORTED with varlen).  1 <= read_topk <= N, <= 8.
+ *   schedule  SSE_SCHEDULE_VARLEN or SSE_SCHEDULE_MASKED (same results up
+ *             to rounding order).  seg_* outputs must be NULL with masked.
+ *   read_topk_idx [total_tokens, H, read_topk] int32 or NULL: the read set
+ *             (only with read_router_logits).
+ * o = sum over the read set of e_r q S + q_shared S_shared.  The workspace
+ * is sse_forward_ex_workspace_bytes(..., read_topk or 0).
+ */
+size_t sse_forward_ex_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                      int c, int d, int N, int topk, int read_topk);
+int sse_forward_ex(const void *q, const void *key_logits, const void *v, const void *log_alpha,
+                   const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
+                   int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                   const void *q_shared, const void *key_logits_shared,
+                   const void *read_router_logits, int read_topk, int schedule,
+                   const float *initial_states, float *o, float *final_states,
+                   int32_t *topk_idx, float *topk_w, int32_t *read_topk_idx,
+                   int32_t *seg_offsets, int32_t *seg_tok, int32_t *seg_slot, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * sse_forward for callers that cannot allocate device memory (code under

@@ -22,9 +22,12 @@ LIB_PATH = os.environ.get("SSE_LIB_PATH") or os.path.join(_PKG, "libsse_amd.so")
 
 SSE_OK, SSE_ERR_INVALID_ARG, SSE_ERR_UNSUPPORTED, SSE_ERR_WORKSPACE, SSE_ERR_HIP = range(5)
 SSE_F32, SSE_BF16 = 0, 1
+SSE_SCHEDULE_VARLEN, SSE_SCHEDULE_MASKED = 0, 1
+SCHEDULES = {"varlen": SSE_SCHEDULE_VARLEN, "masked": SSE_SCHEDULE_MASKED}
 
 EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
             "sse_forward_noalloc_max_bytes", "sse_forward_noalloc",
+            "sse_forward_ex_workspace_bytes", "sse_forward_ex",
             "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
             "sse_group_by_partition", "sse_rowsparse_workspace_bytes", "sse_rowsparse_forward",
             "sse_trace_enable", "sse_trace_read")
@@ -58,6 +61,11 @@ def lib():
     L.sse_forward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
                               P, P, P, SZ, P]
     L.sse_forward.restype = I
+    L.sse_forward_ex_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I, I]
+    L.sse_forward_ex_workspace_bytes.restype = SZ
+    L.sse_forward_ex.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, I, I, P,
+                                 P, P, P, P, P, P, P, P, P, SZ, P]
+    L.sse_forward_ex.restype = I
     L.sse_forward_noalloc_max_bytes.argtypes = []
     L.sse_forward_noalloc_max_bytes.restype = SZ
     L.sse_forward_noalloc.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
@@ -165,6 +173,59 @@ def sse_forward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens,
                            _ptr(seg_tok), _ptr(seg_slot), _ptr(workspace), workspace.numel(),
                            _stream(dev))
     _check(st, "sse_forward")
+    return o, final_states
+
+
+def sse_forward_ex_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk,
+                                   read_topk=0) -> int:
+    return int(lib().sse_forward_ex_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d,
+                                                    N, topk, read_topk))
+
+
+def sse_forward_ex(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens,
+                   max_seqlen=None, initial_states=None, *, q_shared=None, key_logits_shared=None,
+                   read_router_logits=None, read_topk=None, schedule="varlen", o=None,
+                   final_states=None, topk_idx=None, topk_w=None, read_topk_idx=None,
+                   seg_offsets=None, seg_tok=None, seg_slot=None, workspace=None):
+    """General forward: the shared partition's own q / key logits, read sets
+    from their own router logits (masked schedule), and the choice of the
+    varlen or masked schedule.  Returns (o, final_states) as sse_forward."""
+    dev = q.device
+    T, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (T, H, c), "q"), (key_logits, (T, H, c), "key_logits"),
+                       (log_alpha, (T, H, c), "log_alpha"), (v, (T, H, d), "v"),
+                       (router_logits, (T, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    for t, shp, nm in ((q_shared, (T, H, c), "q_shared"),
+                       (key_logits_shared, (T, H, c), "key_logits_shared"),
+                       (read_router_logits, (T, H, N), "read_router_logits")):
+        if t is not None:
+            _need(t, shp, dt, nm, dev)
+    kr = 0 if read_router_logits is None else int(read_topk)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S > 0 else 0
+    if initial_states is not None:
+        _need(initial_states, (S, H, N + 1, c, d), torch.float32, "initial_states", dev)
+    if o is None:
+        o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, N + 1, c, d), dtype=torch.float32, device=dev)
+    nbytes = sse_forward_ex_workspace_bytes(T, S, max_seqlen, H, c, d, N, topk, kr)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sse_forward_ex(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                              _ptr(router_logits), _dtype_code(q), _ptr(cu_seqlens), S,
+                              int(max_seqlen), T, H, c, d, N, topk, _ptr(q_shared),
+                              _ptr(key_logits_shared), _ptr(read_router_logits), kr,
+                              SCHEDULES[schedule], _ptr(initial_states), _ptr(o),
+                              _ptr(final_states), _ptr(topk_idx), _ptr(topk_w),
+                              _ptr(read_topk_idx), _ptr(seg_offsets), _ptr(seg_tok),
+                              _ptr(seg_slot), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "sse_forward_ex")
     return o, final_states
 
 

@@ -62,10 +62,12 @@ struct F64Smem {
     double a[kFW][kFC][kFC + 1];  // partial A tiles (one per wave's row quarter)
     double ebc[CK];          // e^{b_C} per state row
     double lnz[kFC];         // key-softmax normaliser per record
-    double w[kFC];           // gate (write and read)
+    double ww[kFC];          // write gate (0: the record writes nothing)
+    double wr[kFC];          // read gate
     uint32_t row[kFC];       // input row t*H + h
     uint32_t orow[kFC];      // output row (slot row or o row)
-    int valid[kFC];
+    int dec[kFC];            // the record decays the state (it is a write)
+    int rd[kFC];             // the record is read (its gated read is stored)
 };
 
 }  // namespace
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(kFThreads, 1) void chunk_f64_kernel(const ChunkArgs
     constexpr int RT = CK / 16;             // 16-row tiles of the state
     constexpr int NCT = DV / 16;            // 16-column tiles of the state
     constexpr int CTW = NCT >= kFW ? NCT / kFW : 1;   // column tiles per owning wave
-    static_assert(MODE == kModeRouted || MODE == kModeShared, "routed and shared passes");
+    static_assert(MODE == kModeRouted || MODE == kModeShared || MODE == kModeMasked,
+                  "routed, shared and masked passes");
     __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -88,13 +91,18 @@ __global__ __launch_bounds__(kFThreads, 1) void chunk_f64_kernel(const ChunkArgs
 
     int s, h, part;
     int64_t lo, n;
-    if constexpr (MODE == kModeRouted) {
+    if constexpr (MODE != kModeShared) {
         const int g = blockIdx.x;
         part = g % N;
         s = g / N / H;
         h = g / N % H;
-        lo = a.seg_offsets[g];
-        n = a.seg_offsets[g + 1] - lo;
+        if constexpr (MODE == kModeRouted) {
+            lo = a.seg_offsets[g];
+            n = a.seg_offsets[g + 1] - lo;
+        } else {
+            lo = a.cu[s];
+            n = a.cu[s + 1] - lo;
+        }
     } else {
         const int sh = blockIdx.x;
         s = sh / H;
@@ -132,31 +140,52 @@ __global__ __launch_bounds__(kFThreads, 1) void chunk_f64_kernel(const ChunkArgs
             const bool valid = idx < n;
             const int64_t ci = valid ? idx : n - 1;   // a real row for padded records
             uint32_t row, orow;
-            float w;
+            double ww = 0.0, wr = 0.0;
+            bool wrt = valid, rdd = valid;
             if constexpr (MODE == kModeRouted) {
                 const SegRec r = a.seg_rec[lo + ci];
                 row = r.row;
                 orow = r.orow;
-                w = r.w;
+                ww = wr = r.w;
+            } else if constexpr (MODE == kModeMasked) {
+                // token lo + ci: written if the partition is in its write
+                // set, read if it is in its read set (slot = read rank)
+                row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
+                wrt = rdd = false;
+                int jr = 0;
+                for (int j = 0; j < a.sel_k; j++)
+                    if (a.sel_idx[row * (uint32_t)a.sel_k + j] == part) {
+                        wrt = valid;
+                        ww = a.sel_w[row * (uint32_t)a.sel_k + j];
+                    }
+                for (int j = 0; j < a.rd_k; j++)
+                    if (a.rd_idx[row * (uint32_t)a.rd_k + j] == part) {
+                        rdd = valid;
+                        wr = a.rd_w[row * (uint32_t)a.rd_k + j];
+                        jr = j;
+                    }
+                orow = row * (uint32_t)a.rd_k + (uint32_t)jr;
             } else {
                 row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
                 orow = row;
-                w = 1.f;
+                ww = wr = 1.0;
             }
             sm.row[tid] = row;
             sm.orow[tid] = orow;
-            sm.w[tid] = valid ? (double)w : 0.0;
-            sm.valid[tid] = valid;
+            sm.ww[tid] = wrt ? ww : 0.0;
+            sm.wr[tid] = wr;
+            sm.dec[tid] = wrt;
+            sm.rd[tid] = rdd;
         }
         __syncthreads();
-        // ---- raw rows as fp64 (padded records: no decay, no key) ----
+        // ---- raw rows as fp64 (records that do not write: no decay; their
+        //      key is zeroed below) ----
         for (int e = tid; e < kFC * CK; e += kFThreads) {
             const int r = e / CK, j = e % CK;
             const int64_t off = (int64_t)sm.row[r] * CK + j;
-            const bool valid = sm.valid[r] != 0;
             sm.q[r][j] = (double)gq[off];
             sm.k[r][j] = (double)gk[off];
-            sm.l[r][j] = valid ? (double)gl[off] : 0.0;
+            sm.l[r][j] = sm.dec[r] ? (double)gl[off] : 0.0;
         }
         for (int e = tid; e < kFC * DV; e += kFThreads) {
             const int r = e / DV, m = e % DV;
@@ -193,7 +222,7 @@ __global__ __launch_bounds__(kFThreads, 1) void chunk_f64_kernel(const ChunkArgs
             const int r = e / CK, j = e % CK;
             const double b = sm.l[r][j];
             sm.q[r][j] = sm.q[r][j] * exp(b);
-            sm.k[r][j] = sm.w[r] > 0.0 ? sm.w[r] * exp(sm.k[r][j] - sm.lnz[r] - b) : 0.0;
+            sm.k[r][j] = sm.dec[r] ? sm.ww[r] * exp(sm.k[r][j] - sm.lnz[r] - b) : 0.0;
         }
         __syncthreads();
         // ---- partial A over state rows [wv CK/4, (wv+1) CK/4): lane gets
@@ -261,10 +290,10 @@ __global__ __launch_bounds__(kFThreads, 1) void chunk_f64_kernel(const ChunkArgs
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int r = g4 + 4 * i, col = 16 * ct + l16;
-                    if (!sm.valid[r]) continue;
-                    const double val = sm.w[r] * O[u][i];
+                    if (!sm.rd[r]) continue;
+                    const double val = sm.wr[r] * O[u][i];
                     const uint32_t orow = sm.orow[r];
-                    if constexpr (MODE == kModeRouted) {
+                    if constexpr (MODE != kModeShared) {
                         a.part[(int64_t)orow * DV + col] = (float)val;
                     } else {
                         double sum = val;
@@ -298,7 +327,7 @@ namespace {
 
 template <int CK, int DV, int MODE>
 void launch_f64_cfg(const ChunkArgs& a, hipStream_t st) {
-    const unsigned grid = (unsigned)(a.num_seqs * a.H * (MODE == kModeRouted ? a.N : 1));
+    const unsigned grid = (unsigned)(a.num_seqs * a.H * (MODE != kModeShared ? a.N : 1));
     if (grid == 0) return;
     chunk_f64_kernel<CK, DV, MODE><<<grid, kFThreads, 0, st>>>(a);
 }
@@ -326,6 +355,8 @@ hipError_t launch_chunk_f64(int mode, const ChunkArgs& a, int c, int d, hipStrea
         ok = launch_f64_shape<kModeRouted>(a, c, d, st);
     else if (mode == kModeShared)
         ok = launch_f64_shape<kModeShared>(a, c, d, st);
+    else if (mode == kModeMasked)
+        ok = launch_f64_shape<kModeMasked>(a, c, d, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -343,6 +374,10 @@ hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipS
 hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
     return dtype == kF32 ? launch_chunk_f64(kModeRouted, a, c, d, st)
                          : launch_chunk_ws(kModeRouted, a, c, d, st);
+}
+hipError_t launch_chunk_masked(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st) {
+    return dtype == kF32 ? launch_chunk_f64(kModeMasked, a, c, d, st)
+                         : launch_chunk_ws(kModeMasked, a, c, d, st);
 }
 
 }  // namespace sse

@@ -48,6 +48,8 @@ constexpr int kRing = 8;          // metadata ring slots (7 are live at a time)
 constexpr int kL = 2;             // bf16 terms of Qt, Kh, A and S
 constexpr uint32_t kPadOff = 0x80000000u;  // row offset of padded records: past every
                                            // input (inputs are < 2^31 bytes)
+constexpr uint32_t kNoRow = 0xffffffffu;   // masked schedule: token outside the
+                                           // partition's write and read sets
 
 static_assert(kProd == kNW, "the preparation layout assumes four producer waves");
 
@@ -113,8 +115,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     using SM = WsSmem<CK, DV>;
     using GK = Geo<kWsC, CK>;
     using GV = Geo<kWsC, DV>;
-    static_assert(MODE == kModeShared || MODE == kModeRouted, "routed and shared passes only");
-    constexpr bool kSwz = MODE == kModeRouted;  // record-major tile swizzle (rm_swz)
+    static_assert(MODE == kModeShared || MODE == kModeRouted || MODE == kModeMasked,
+                  "shared, routed and masked passes only");
+    constexpr bool kPart = MODE != kModeShared;  // one block per (sequence, head, partition)
+    constexpr bool kSwz = kPart;                 // record-major tile swizzle (rm_swz)
     constexpr int NS = DV / 32;       // consumer waves that own state columns
     constexpr int RT_N = CK / 32;     // 32-row tiles of the state
     constexpr int RPG = GK::RPG, RPGV = GV::RPG;
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     // on gfx950 against equal priority: routed 426-429 us against 434-437 on
     // one box, no difference on another; shared 263 against 265 us, and
     // 286 us with the producers first.
-    if (MODE == kModeRouted ? producer : !producer) __builtin_amdgcn_s_setprio(2);
+    if (kPart ? producer : !producer) __builtin_amdgcn_s_setprio(2);
     const int pw = wv - kCons;                                   // producer index
     const int hh = lane / 32, l32 = lane % 32;
     const int H = a.H, N = a.N;
@@ -138,12 +142,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     // ---------------- which records this block runs ----------------
     int s, h, part, piece = 0, npieces = 1;
     int64_t lo, n;
-    if constexpr (MODE == kModeRouted) {
+    if constexpr (kPart) {
         // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD
         // b % 8).  Map the N partitions of one (sequence, head) to the same
         // XCD, dispatched together: they walk the same tokens at about the
         // same pace, so the k reads of a token's rows and the k additions to
-        // its output row meet in that XCD's L2.
+        // its output row meet in that XCD's L2.  The masked schedule walks
+        // every token of the sequence for every partition.
         int g = blockIdx.x;
         const int U = a.num_seqs * H;
         if ((U & 7) == 0) {
@@ -153,8 +158,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         part = g % N;
         s = g / N / H;
         h = g / N % H;
-        lo = a.seg_offsets[g];
-        n = a.seg_offsets[g + 1] - lo;
+        if constexpr (MODE == kModeRouted) {
+            lo = a.seg_offsets[g];
+            n = a.seg_offsets[g + 1] - lo;
+        } else {
+            lo = a.cu[s];
+            n = a.cu[s + 1] - lo;
+        }
     } else {
         const int sh = blockIdx.x;
         s = sh / H;
@@ -233,6 +243,46 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
             m.orow = r.y;
             m.cr = __uint_as_float(r.z);
             m.w = __uint_as_float(r.w);
+        } else if constexpr (MODE == kModeMasked) {
+            // token lo + ci is written when the partition is in its write
+            // set (weight e: the key is e kappa) and read when it is in its
+            // read set (read weight, slot row = the read rank); a token in
+            // neither is padding.  All loads are issued before any select.
+            const uint32_t row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
+            int32_t wi[kMaxTopK], ri[kMaxTopK];
+            float ww[kMaxTopK], rw[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; j++) {
+                if (j < a.sel_k) {
+                    wi[j] = a.sel_idx[row * (uint32_t)a.sel_k + j];
+                    ww[j] = a.sel_w[row * (uint32_t)a.sel_k + j];
+                }
+                if (j < a.rd_k) {
+                    ri[j] = a.rd_idx[row * (uint32_t)a.rd_k + j];
+                    rw[j] = a.rd_w[row * (uint32_t)a.rd_k + j];
+                }
+            }
+            const float l2 = a.lnz2_r[row];
+            bool wrt = false;
+            float we = 1.f, wr = -0.f;
+            int jr = -1;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; j++) {
+                if (j < a.sel_k && wi[j] == part) {
+                    wrt = true;
+                    we = ww[j];
+                }
+                if (j < a.rd_k && ri[j] == part) {
+                    jr = j;
+                    wr = rw[j];
+                }
+            }
+            m.row = (wrt || jr >= 0) ? row : kNoRow;
+            m.orow = row * (uint32_t)a.rd_k + (uint32_t)(jr >= 0 ? jr : 0);
+            // a weight that underflowed to zero keeps a finite offset, so
+            // the record still decays the state
+            m.cr = wrt ? l2 - log2f(fmaxf(we, 1.17549435e-38f)) : INFINITY;
+            m.w = wr;
         } else {
             m.row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
             m.orow = m.row;
@@ -243,7 +293,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
     auto meta_store = [&](int64_t chunk, const Meta& m) {
         if (lane < kWsC) {
             const int slot = (int)(chunk % kRing);
-            const bool valid = chunk * kWsC + lane < n;
+            const bool valid = chunk * kWsC + lane < n && (MODE != kModeMasked || m.row != kNoRow);
             // padded records read zeros (buffer loads past the end): no log
             // decay, no key, no value
             sm.mrow[slot][lane] = valid ? m.row * (uint32_t)(CK * 2) : kPadOff;
@@ -374,12 +424,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         float run[kPC] = {0.f, 0.f, 0.f, 0.f};
         float bb[RPG][kPC];
 #pragma unroll
-        for (int i = 0; i < RPG; i++)
+        for (int i = 0; i < RPG; i++) {
+            // masked schedule: a record that is only read does not decay the
+            // state (its exponent offset is +inf: it writes nothing either)
+            const bool dec = MODE != kModeMasked || gcr[i] != INFINITY;
 #pragma unroll
             for (int e = 0; e < kPC; e++) {
-                run[e] = fmaf(R.l[i].get(e), kLog2e, run[e]);  // zero for a padded record
+                const float x = dec ? R.l[i].get(e) : 0.f;
+                run[e] = fmaf(x, kLog2e, run[e]);  // zero for a padded record
                 bb[i][e] = run[e];
             }
+        }
         hook(1);
         float excl[kPC], ebc_own[kPC], incl[kPC], tot[kPC];
         group_scan4(run, incl, tot);
@@ -724,7 +779,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 #pragma unroll
                     for (int q4 = 0; q4 < 4; q4++)
                         mw4[q4] = *reinterpret_cast<const float4*>(&sm.mw[slot][8 * q4 + 4 * hh]);
-                    if constexpr (MODE == kModeRouted) {
+                    if constexpr (kPart) {
                         out_rows(nn - 1, orow, oval);
 #pragma unroll
                         for (int p = 0; p < 2; p++) {
@@ -922,7 +977,7 @@ namespace {
 template <int CK, int DV, int MODE>
 void launch_ws_cfg(const ChunkArgs& a, hipStream_t st) {
     dim3 grid;
-    if (MODE == kModeRouted)
+    if (MODE != kModeShared)
         grid = dim3((unsigned)(a.num_seqs * a.H * a.N));
     else
         grid = dim3((unsigned)(a.num_seqs * a.H), (unsigned)a.max_pieces);
@@ -953,6 +1008,8 @@ hipError_t launch_chunk_ws(int mode, const ChunkArgs& a, int c, int d, hipStream
         ok = launch_ws_shape<kModeShared>(a, c, d, st);
     else if (mode == kModeRouted)
         ok = launch_ws_shape<kModeRouted>(a, c, d, st);
+    else if (mode == kModeMasked)
+        ok = launch_ws_shape<kModeMasked>(a, c, d, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -569,6 +569,68 @@ hipError_t launch_group(const int32_t* idx, const float* w, const int32_t* cu, i
     return hipGetLastError();
 }
 
+// Key normalisers alone (used when the routed and shared partitions have
+// different keys, or when no routing kernel runs): one (token, head) row per
+// CK/8 (bf16) or CK/4 (fp32) lanes, 16-byte loads, max-shifted sum of exp2
+// with row reductions in registers.
+template <int CK, typename TIn>
+__global__ __launch_bounds__(256) void key_norm_kernel(const TIn* __restrict__ kl, int64_t rows,
+                                                       float* __restrict__ lnz2) {
+    constexpr int VPL = 16 / (int)sizeof(TIn);   // values per lane
+    constexpr int LPR = CK / VPL;                // lanes per row
+    constexpr int RPB = 256 / LPR;               // rows per block
+    const int sub = threadIdx.x % LPR;
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const bool ok = r < rows;
+    const uint4 v = reinterpret_cast<const uint4*>(kl + (ok ? r : 0) * CK)[sub];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    float x[VPL];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        if constexpr (sizeof(TIn) == 2) {
+            x[2 * e] = __uint_as_float(w4[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        } else {
+            x[e] = __uint_as_float(w4[e]);
+        }
+    }
+    float m = x[0];
+#pragma unroll
+    for (int j = 1; j < VPL; j++) m = fmaxf(m, x[j]);
+    m = row_reduce<LPR>(m, [](float u, float w) { return fmaxf(u, w); });
+    const float m2 = m * kLog2e;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
+    sum = row_reduce<LPR>(sum, [](float u, float w) { return u + w; });
+    if (ok && sub == 0) lnz2[r] = m2 + log2f(sum);
+}
+
+template <typename TIn>
+static hipError_t launch_key_norm_t(const void* kl, int64_t rows, int c, float* lnz2,
+                                    hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const TIn* k = static_cast<const TIn*>(kl);
+    constexpr int VPL = 16 / (int)sizeof(TIn);
+    const int64_t rpb = 256 / (c / VPL);
+    const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+    if (c == 32)
+        key_norm_kernel<32, TIn><<<grid, 256, 0, st>>>(k, rows, lnz2);
+    else if (c == 64)
+        key_norm_kernel<64, TIn><<<grid, 256, 0, st>>>(k, rows, lnz2);
+    else if (c == 128)
+        key_norm_kernel<128, TIn><<<grid, 256, 0, st>>>(k, rows, lnz2);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_key_norm(const void* kl, int dtype, int64_t rows, int c, float* lnz2,
+                           hipStream_t st) {
+    return dtype == kF32 ? launch_key_norm_t<float>(kl, rows, c, lnz2, st)
+                         : launch_key_norm_t<bf16_t>(kl, rows, c, lnz2, st);
+}
+
 // Debug copies of the forward's own grouping: the segment offsets as
 // scanned, and the token and top-k rank of every record the chunk kernels
 // read (decoded from its input row t*H + h and slot row (t*H + h)*K + rank).

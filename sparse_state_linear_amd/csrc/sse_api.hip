@@ -30,7 +30,8 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
 }
 
 struct FwdLayout {
-    size_t idx, w, counts, seg_off, rinfo, seg_rec, lnz2, agg_S, agg_D, trash, part, total;
+    size_t idx, w, ridx, rw, counts, seg_off, rinfo, seg_rec, lnz2, lnz2_sh, agg_S, agg_D, trash,
+        part, total;
 };
 
 // Piece length of the shared partition's chain (bf16 inputs; the fp32-input
@@ -52,16 +53,22 @@ int max_pieces(int max_seqlen, int piece_len) {
     return max_seqlen <= 0 ? 1 : (max_seqlen + piece_len - 1) / piece_len;
 }
 
-// Workspace carving.  c, d = 0 sizes the grouping part only.  Returns false
-// when the sizes overflow the 32-bit indexing of the kernels.
+// Workspace carving.  c, d = 0 sizes the grouping part only; Kr > 0
+// reserves the read-set choices (Kr per token) and sizes the routed-read
+// slots by Kr instead of K.  Returns false when the sizes overflow the
+// 32-bit indexing of the kernels.
 bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N, int K,
-                    FwdLayout& L) {
-    if (T < 0 || S < 0 || max_seqlen < 0 || H < 1 || N < 1 || K < 1) return false;
+                    FwdLayout& L, int Kr = 0) {
+    if (T < 0 || S < 0 || max_seqlen < 0 || H < 1 || N < 1 || K < 1 || Kr < 0) return false;
     const int64_t recs = T * H * K;
+    const int64_t rrecs = T * H * Kr;
+    const int64_t slots = Kr > 0 ? rrecs : recs;
     const int64_t nblk = sse::group_nblk(max_seqlen);
     const int64_t cnt = (int64_t)S * H * N * nblk;
     const int64_t units = (int64_t)S * H * (N + 1);
-    if (recs >= INT_MAX || cnt >= INT_MAX || units >= INT_MAX || T >= INT_MAX) return false;
+    if (recs >= INT_MAX || rrecs >= INT_MAX || cnt >= INT_MAX || units >= INT_MAX ||
+        T >= INT_MAX)
+        return false;
     if ((int64_t)S * H >= INT_MAX || (int64_t)S * H * N + 1 >= INT_MAX) return false;
     if ((int64_t)S * nblk * H >= INT_MAX) return false;
     const int64_t maxp = max_pieces(max_seqlen, shared_piece_len(S, H, max_seqlen));
@@ -69,17 +76,20 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     size_t off = 0;
     L.idx = off;     off += align_up(sizeof(int32_t) * (size_t)recs);
     L.w = off;       off += align_up(sizeof(float) * (size_t)recs);
+    L.ridx = off;    off += align_up(sizeof(int32_t) * (size_t)rrecs);
+    L.rw = off;      off += align_up(sizeof(float) * (size_t)rrecs);
     L.counts = off;  off += align_up(sizeof(int32_t) * (size_t)cnt);
     L.seg_off = off; off += align_up(sizeof(int32_t) * (size_t)((int64_t)S * H * N + 1));
     L.rinfo = off;   off += align_up(sizeof(uint2) * (size_t)recs);
     L.seg_rec = off; off += align_up(sizeof(sse::SegRec) * (size_t)recs);
     L.lnz2 = off;    off += align_up(sizeof(float) * (size_t)(T * H));
+    L.lnz2_sh = off; off += align_up(sizeof(float) * (size_t)(T * H));
     L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
     L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
     L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? 2 * d : 1));
-    // fp32 slots: recs rows of d floats; bf16 slots: recs + 1 rows of d int16
-    // values, then recs + 1 rows of d/32 fp32 steps
-    L.part = off;    off += align_up(sizeof(float) * (size_t)(recs + 1) * (size_t)d);
+    // fp32 slots: `slots` rows of d floats; bf16 slots: slots + 1 rows of d
+    // int16 values, then slots + 1 rows of d/32 fp32 steps
+    L.part = off;    off += align_up(sizeof(float) * (size_t)(slots + 1) * (size_t)d);
     L.total = off;
     return true;
 }
@@ -157,48 +167,85 @@ void* scratch_ptr() {
     return g_scratch_ptr[dev];
 }
 
+// Options of the general forward (the defaults give sse_forward).
+struct FwdOpts {
+    const void* q_sh = nullptr;   // shared partition's own query rows (or q)
+    const void* kl_sh = nullptr;  // shared partition's own key logits (or key_logits)
+    const void* zr = nullptr;     // read-set router logits (or the write set's)
+    int kr = 0;                   // read-set size when zr is given
+    int schedule = SSE_SCHEDULE_VARLEN;
+    int32_t* ridx_out = nullptr;  // read-set choices [T, H, kr] (optional)
+    bool use_scratch = false;     // workspace = the static array
+};
+
+FwdOpts scratch_opts() {
+    FwdOpts opt;
+    opt.use_scratch = true;
+    return opt;
+}
+
 int forward_impl(const void* q, const void* key_logits, const void* v, const void* log_alpha,
                  const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
                  int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
                  const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
                  float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
-                 void* workspace, size_t workspace_bytes, void* stream,
-                 bool use_scratch = false) {
+                 void* workspace, size_t workspace_bytes, void* stream, const FwdOpts& opt) {
     int st = check_common(dtype, H, c, d, N, topk);
     if (st != SSE_OK) return st;
+    const bool masked = opt.schedule == SSE_SCHEDULE_MASKED;
+    if (opt.schedule != SSE_SCHEDULE_VARLEN && !masked) return SSE_ERR_INVALID_ARG;
+    const bool rsets = opt.zr != nullptr;
+    if (rsets && (opt.kr < 1 || opt.kr > N)) return SSE_ERR_INVALID_ARG;
+    if (rsets && opt.kr > sse::kMaxTopK) return SSE_ERR_UNSUPPORTED;
+    if (!rsets && opt.ridx_out) return SSE_ERR_INVALID_ARG;
+    // the varlen grouping carries one set per token: read sets that differ
+    // run on the masked schedule
+    if (rsets && !masked) return SSE_ERR_UNSUPPORTED;
+    if (masked && (seg_offsets || seg_tok || seg_slot)) return SSE_ERR_INVALID_ARG;
     if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
     if (total_tokens > 0 && num_seqs == 0) return SSE_ERR_INVALID_ARG;
     if (!cu_seqlens) return SSE_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !o))
         return SSE_ERR_INVALID_ARG;
     if (num_seqs > 0 && !final_states) return SSE_ERR_INVALID_ARG;
+    const int kslot = rsets ? opt.kr : topk;   // routed reads per token
     FwdLayout L;
-    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L))
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L,
+                        rsets ? opt.kr : 0))
         return SSE_ERR_UNSUPPORTED;
     // byte offsets of token rows (fp32 worst case) and of the routed slots
-    // [T, H, topk, d] fp32 must fit in 32 bits
+    // [T, H, kslot, d] fp32 must fit in 32 bits
     if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
-    if (total_tokens * H * topk * d >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
-    if (use_scratch) {
+    if (total_tokens * H * kslot * d >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
+    void* ws_ptr = workspace;
+    size_t ws_bytes = workspace_bytes;
+    if (opt.use_scratch) {
         // every argument is checked; now the static array (no allocation)
         if (L.total > kScratchBytes) return SSE_ERR_WORKSPACE;
-        workspace = scratch_ptr();
-        if (!workspace) return SSE_ERR_HIP;
-        workspace_bytes = kScratchBytes;
+        ws_ptr = scratch_ptr();
+        if (!ws_ptr) return SSE_ERR_HIP;
+        ws_bytes = kScratchBytes;
     }
-    if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
+    if (!ws_ptr || ws_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(ws_ptr);
     int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
+    int32_t* ridx = opt.ridx_out ? opt.ridx_out : reinterpret_cast<int32_t*>(ws + L.ridx);
+    float* rw = reinterpret_cast<float*>(ws + L.rw);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
     int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
     uint2* rinfo = reinterpret_cast<uint2*>(ws + L.rinfo);
     sse::SegRec* seg_rec = reinterpret_cast<sse::SegRec*>(ws + L.seg_rec);
     float* lnz2 = reinterpret_cast<float*>(ws + L.lnz2);
+    // the shared partition's normalisers: the routed ones unless it has its
+    // own keys
+    const bool own_keys = opt.kl_sh != nullptr;
+    float* lnz2_sh = own_keys ? reinterpret_cast<float*>(ws + L.lnz2_sh) : lnz2;
 
-    sse::ChunkArgs a;
+    // routed passes (routed / masked)
+    sse::ChunkArgs a = {};
     a.q = q;
     a.kl = key_logits;
     a.v = v;
@@ -208,6 +255,13 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     a.seg_rec = seg_rec;
     a.lnz2 = lnz2;
     a.lnz2_out = lnz2;
+    a.lnz2_r = lnz2;
+    a.sel_idx = idx;
+    a.sel_w = w;
+    a.sel_k = topk;
+    a.rd_idx = rsets ? ridx : idx;
+    a.rd_w = rsets ? rw : w;
+    a.rd_k = kslot;
     a.init = initial_states;
     a.o = o;
     a.final_states = final_states;
@@ -217,45 +271,66 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     a.part = reinterpret_cast<float*>(ws + L.part);
     // bf16 inputs: int16 slot values, then their steps, inside the fp32-sized
     // slot area (2 d + d/8 <= 4 d bytes per slot row)
-    a.slot_rows = (uint32_t)(total_tokens * H * topk);
+    a.slot_rows = (uint32_t)(total_tokens * H * kslot);
     a.rows = (uint32_t)(total_tokens * H);
     a.part_scale = reinterpret_cast<float*>(ws + L.part + sizeof(int16_t) * ((size_t)a.slot_rows + 1) *
                                                              (size_t)d);
     a.num_seqs = num_seqs;
     a.H = H;
     a.N = N;
-    a.topk = topk;
+    a.topk = kslot;
     a.piece_len = shared_piece_len(num_seqs, H, max_seqlen);
     a.max_pieces = max_pieces(max_seqlen, a.piece_len);
+    // the shared partition's passes: its own query and keys when given
+    sse::ChunkArgs ash = a;
+    if (opt.q_sh) ash.q = opt.q_sh;
+    if (own_keys) ash.kl = opt.kl_sh;
+    ash.lnz2 = lnz2_sh;
+    ash.lnz2_out = lnz2_sh;
 
-    // 1. router + per-block counts (+ the key-softmax normaliser for fp32
-    //    inputs; for bf16 inputs the piece-state pass computes it)
+    hipError_t e;
     trace_mark(0, s);
-    hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
-                                           max_seqlen, total_tokens, H, c, N, topk, idx, w,
-                                           counts, rinfo, dtype == SSE_F32 ? lnz2 : nullptr, s);
+    if (!masked) {
+        // 1. router + per-block counts (+ the routed keys' normalisers when
+        //    the piece-state pass will not compute them: fp32 inputs, or a
+        //    shared partition with its own keys)
+        e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
+                                    max_seqlen, total_tokens, H, c, N, topk, idx, w, counts, rinfo,
+                                    (dtype == SSE_F32 || own_keys) ? lnz2 : nullptr, s);
+    } else {
+        // 1. routers of the write set and the read set (no grouping), the
+        //    routed keys' normalisers when the shared pass has its own keys
+        e = sse::launch_router_rows(router_logits, dtype, total_tokens * H, N, topk, idx, w, s);
+        if (e == hipSuccess && rsets)
+            e = sse::launch_router_rows(opt.zr, dtype, total_tokens * H, N, opt.kr, ridx, rw, s);
+        if (e == hipSuccess && own_keys && dtype != SSE_F32)
+            e = sse::launch_key_norm(key_logits, dtype, total_tokens * H, c, lnz2, s);
+    }
     if (e != hipSuccess) return SSE_ERR_HIP;
-    // 2. piece states of the shared partition (bf16 inputs: the piece-state
-    //    pass, which also computes the key normalisers; fp32 inputs: the
-    //    chunk kernel's local-state mode)
+    // 2. piece states of the shared partition and its keys' normalisers
+    //    (bf16 inputs; the fp32-input kernels compute their own)
     trace_mark(1, s);
-    e = sse::launch_chunk_local(a, dtype, c, d, s);
+    e = sse::launch_chunk_local(ash, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
-    // 3. grouping into (sequence, head, partition) segments
     trace_mark(2, s);
-    e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N, topk,
-                              counts, seg_off, lnz2, seg_rec, s);
-    if (e != hipSuccess) return SSE_ERR_HIP;
-    e = sse::launch_seg_debug(seg_rec, seg_off, total_tokens * H * topk, (int64_t)num_seqs * H * N,
-                              H, topk, seg_offsets, seg_tok, seg_slot, s);
-    if (e != hipSuccess) return SSE_ERR_HIP;
+    if (!masked) {
+        // 3. grouping into (sequence, head, partition) segments
+        e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N,
+                                  topk, counts, seg_off, lnz2, seg_rec, s);
+        if (e != hipSuccess) return SSE_ERR_HIP;
+        e = sse::launch_seg_debug(seg_rec, seg_off, total_tokens * H * topk,
+                                  (int64_t)num_seqs * H * N, H, topk, seg_offsets, seg_tok,
+                                  seg_slot, s);
+        if (e != hipSuccess) return SSE_ERR_HIP;
+    }
     trace_mark(3, s);
     // 4. routed partitions: e-gated reads into the workspace slots
-    e = sse::launch_chunk_routed(a, dtype, c, d, s);
+    e = masked ? sse::launch_chunk_masked(a, dtype, c, d, s)
+               : sse::launch_chunk_routed(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(4, s);
     // 5. shared partition: o = shared read + the token's routed slots
-    e = sse::launch_chunk_shared(a, dtype, c, d, s);
+    e = sse::launch_chunk_shared(ash, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(5, s);
     if (g_trace.on) g_trace.calls++;
@@ -296,7 +371,39 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
     return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
                         max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
                         final_states, topk_idx, topk_w, seg_offsets, seg_tok, seg_slot, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, FwdOpts());
+}
+
+size_t sse_forward_ex_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                      int c, int d, int N, int topk, int read_topk) {
+    if (check_common(SSE_BF16, H, c, d, N, topk) != SSE_OK) return 0;
+    if (read_topk < 0 || read_topk > N || read_topk > sse::kMaxTopK) return 0;
+    FwdLayout L;
+    if (!forward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L, read_topk))
+        return 0;
+    return L.total;
+}
+
+int sse_forward_ex(const void* q, const void* key_logits, const void* v, const void* log_alpha,
+                   const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
+                   int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                   const void* q_shared, const void* key_logits_shared,
+                   const void* read_router_logits, int read_topk, int schedule,
+                   const float* initial_states, float* o, float* final_states,
+                   int32_t* topk_idx, float* topk_w, int32_t* read_topk_idx,
+                   int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    FwdOpts opt;
+    opt.q_sh = q_shared;
+    opt.kl_sh = key_logits_shared;
+    opt.zr = read_router_logits;
+    opt.kr = read_topk;
+    opt.schedule = schedule;
+    opt.ridx_out = read_topk_idx;
+    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
+                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
+                        final_states, topk_idx, topk_w, seg_offsets, seg_tok, seg_slot, workspace,
+                        workspace_bytes, stream, opt);
 }
 
 size_t sse_forward_noalloc_max_bytes(void) { return kScratchBytes; }
@@ -310,7 +417,7 @@ int sse_forward_noalloc(const void* q, const void* key_logits, const void* v,
     return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
                         max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
                         final_states, topk_idx, topk_w, nullptr, nullptr, nullptr, nullptr, 0,
-                        stream, true);
+                        stream, scratch_opts());
 }
 
 size_t sse_rowsparse_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,

@@ -52,6 +52,11 @@ hipError_t launch_group_fwd(const uint2* rinfo, const int32_t* cu, int num_seqs,
                             int64_t T, int H, int N, int K, int32_t* counts, int32_t* seg_offsets,
                             const float* lnz2, SegRec* seg, hipStream_t st);
 
+// Key-softmax log2 normaliser of every (token, head) row of c key logits:
+// lnz2 = log2 sum_j 2^(kl_j log2 e), so that kappa_j = 2^(kl_j log2 e - lnz2).
+hipError_t launch_key_norm(const void* kl, int dtype, int64_t rows, int c, float* lnz2,
+                           hipStream_t st);
+
 // Debug outputs of the forward's grouping: copies of the segment offsets
 // [nseg + 1] and, per record, its token t and top-k rank (any pointer may be
 // null).
@@ -68,8 +73,16 @@ struct ChunkArgs {
     const int32_t* cu;
     const int32_t* seg_offsets;  // routed segments
     const SegRec* seg_rec;       // routed records, segment by segment
-    const float* lnz2;           // [T, H] key-softmax log2 normaliser (shared pieces)
+    const float* lnz2;           // [T, H] key-softmax log2 normaliser of the keys
+                                 // this pass writes with (shared pass: the shared
+                                 // partition's keys)
     float* lnz2_out;             // where the bf16 piece-state pass stores lnz2
+    const float* lnz2_r;         // masked pass: normaliser of the routed keys
+    const int32_t* sel_idx;      // masked pass: write set [T, H, sel_k] and its
+    const float* sel_w;          //   router probabilities
+    const int32_t* rd_idx;       // masked pass: read set [T, H, rd_k] and its
+    const float* rd_w;           //   read weights (the write set by default)
+    int sel_k, rd_k;
     const float* init;           // [S, H, N+1, c, d] or null
     float* o;
     float* final_states;
@@ -90,9 +103,11 @@ struct ChunkArgs {
     int max_pieces;
 };
 
-// Passes of the chunked kernels: the routed partitions' segments, or the
-// shared partition's chain.
-enum { kModeShared = 1, kModeRouted = 2 };
+// Passes of the chunked kernels: the shared partition's chain, the routed
+// partitions' segments (records gathered by the grouping), or the masked
+// schedule (every token of a sequence is a record of every partition; those
+// outside the partition's write and read sets are padding).
+enum { kModeShared = 1, kModeRouted = 2, kModeMasked = 3 };
 
 // Records per shared piece of the bf16 kernels (the longest piece length).
 constexpr int kSharedPiece = 1024;
@@ -106,6 +121,9 @@ hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipSt
 hipError_t launch_piece_state(const ChunkArgs& a, int c, int d, hipStream_t st);
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+// masked schedule: one block per (sequence, head, partition) over every
+// token of the sequence, membership from sel_idx / rd_idx
+hipError_t launch_chunk_masked(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 // fp32 inputs: the fp64 chunk kernel (chunk_f64.hip), mode kModeRouted or
 // kModeShared.
 hipError_t launch_chunk_f64(int mode, const ChunkArgs& a, int c, int d, hipStream_t st);

@@ -34,6 +34,11 @@ def declare(L):
     L.sse_group_workspace_bytes.restype = SZ
     L.sse_group_by_partition.argtypes = [P, P, P, I, I, I64, I, I, I, P, P, P, P, P, SZ, P]
     L.sse_group_by_partition.restype = I
+    L.sse_forward_ex_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I, I]
+    L.sse_forward_ex_workspace_bytes.restype = SZ
+    L.sse_forward_ex.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, I, I, P,
+                                 P, P, P, P, P, P, P, P, P, SZ, P]
+    L.sse_forward_ex.restype = I
     L.sse_rowsparse_workspace_bytes.argtypes = [I64, I, I, I, I, I]
     L.sse_rowsparse_workspace_bytes.restype = SZ
     L.sse_rowsparse_forward.argtypes = [P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
@@ -85,6 +90,30 @@ NOALLOC_REJECTS = [
     # workspace beyond the static array: 8 sequences x 16 heads x 8192 tokens
     (dict(T=65536, S=8, maxlen=8192, H=16, c=128, d=128, N=16), WORKSPACE),
 ]
+
+def forward_ex(L, **kw):
+    a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, z=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16,
+             T=16, H=2, c=32, d=32, N=4, k=2, qs=None, ks=None, zr=None, kr=0, sched=0,
+             init=None, o=FAKE, fs=FAKE, idx=None, w=None, ridx=None, soff=None, stok=None,
+             sslot=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.sse_forward_ex(a["q"], a["kl"], a["v"], a["la"], a["z"], a["dtype"], a["cu"],
+                            a["S"], a["maxlen"], a["T"], a["H"], a["c"], a["d"], a["N"], a["k"],
+                            a["qs"], a["ks"], a["zr"], a["kr"], a["sched"], a["init"], a["o"],
+                            a["fs"], a["idx"], a["w"], a["ridx"], a["soff"], a["stok"],
+                            a["sslot"], a["ws"], a["wsb"], a["stream"])
+
+
+FORWARD_EX_REJECTS = [
+    (dict(q=None), INVALID), (dict(sched=2), INVALID),
+    (dict(zr=FAKE, kr=0, sched=1), INVALID), (dict(zr=FAKE, kr=5, sched=1), INVALID),
+    (dict(zr=FAKE, kr=2, sched=0), UNSUPPORTED),            # read sets need the masked schedule
+    (dict(N=16, zr=FAKE, kr=9, sched=1), UNSUPPORTED),
+    (dict(ridx=FAKE), INVALID),                             # read choices without read logits
+    (dict(sched=1, soff=FAKE), INVALID),                    # no grouping on the masked schedule
+    (dict(sched=1, wsb=16), WORKSPACE),
+]
+
 
 def rowsparse(L, **kw):
     a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16, T=16, H=2,
@@ -138,6 +167,13 @@ def exercise(L) -> int:
         got = decode(L, **kw)
         assert got == code, (kw, got, code)
         n += 1
+    for kw, code in FORWARD_EX_REJECTS:
+        got = forward_ex(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    assert L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 3) > \
+        L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 0) > 0
+    assert L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 9) == 0
     for kw, code in ROWSPARSE_REJECTS:
         got = rowsparse(L, **kw)
         assert got == code, (kw, got, code)

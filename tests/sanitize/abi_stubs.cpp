@@ -35,6 +35,8 @@ hipError_t launch_piece_state(const ChunkArgs&, int, int, hipStream_t) { return 
 hipError_t launch_chunk_shared(const ChunkArgs&, int, int, int, hipStream_t) { return stub(); }
 hipError_t launch_chunk_routed(const ChunkArgs&, int, int, int, hipStream_t) { return stub(); }
 hipError_t launch_chunk_f64(int, const ChunkArgs&, int, int, hipStream_t) { return stub(); }
+hipError_t launch_chunk_masked(const ChunkArgs&, int, int, int, hipStream_t) { return stub(); }
+hipError_t launch_key_norm(const void*, int, int64_t, int, float*, hipStream_t) { return stub(); }
 hipError_t launch_rowsparse_mask(const void*, const void*, int, int64_t, int, int, int, void*,
                                  void*, hipStream_t) {
     return stub();

@@ -60,3 +60,15 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_binding_constants_match_header():
+    """Status, dtype and schedule codes of the binding equal the header's."""
+    text = open(HEADER).read()
+    for name, val in (("SSE_SCHEDULE_VARLEN", sse.SSE_SCHEDULE_VARLEN),
+                      ("SSE_SCHEDULE_MASKED", sse.SSE_SCHEDULE_MASKED),
+                      ("SSE_F32", sse.SSE_F32), ("SSE_BF16", sse.SSE_BF16),
+                      ("SSE_ERR_WORKSPACE", sse.SSE_ERR_WORKSPACE)):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == val, name
+    assert sse.SCHEDULES == {"varlen": sse.SSE_SCHEDULE_VARLEN, "masked": sse.SSE_SCHEDULE_MASKED}
