@@ -65,6 +65,9 @@ def load(path: str | None = None):
     lib.sse_oracle_forward_ex.argtypes = [I, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P,
                                           P, P, P, P]
     lib.sse_oracle_forward_ex.restype = I
+    lib.sse_oracle_backward.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
+                                        P, P, P, I]
+    lib.sse_oracle_backward.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -243,3 +246,40 @@ def forward_ex(q, key_logits, v, log_alpha, router_logits, cu_seqlens, N, topk, 
     if rc != 0:
         raise ValueError("sse_oracle_forward_ex rejected its arguments")
     return {"o": o, "final_states": fs, "write_idx": widx, "read_idx": ridx}
+
+
+def backward(q, key_logits, v, log_alpha, router_logits, cu_seqlens, N, topk, do,
+             dfinal_states=None, initial_states=None, threads=1, lib=None):
+    """Gradients of L = <do, o> + <dfinal_states, final_states> with respect
+    to the five inputs and the initial states (fp64).  Returns a dict of dq,
+    dkey_logits, dlog_alpha [T,H,c], dv [T,H,d], drouter_logits [T,H,N] and
+    dinitial_states [S,H,N+1,c,d]."""
+    lib = lib or load()
+    dt, q = _raw(q)
+    arrs = [_raw(a) for a in (key_logits, v, log_alpha, router_logits)]
+    if any(a[0] != dt for a in arrs):
+        raise TypeError("all inputs must share one dtype")
+    kl, v, la, z = (a[1] for a in arrs)
+    T, H, c = q.shape
+    d = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    S = cu.shape[0] - 1
+    assert z.shape == (T, H, N) and int(cu[-1]) == T
+    do = np.ascontiguousarray(do, dtype=np.float64)
+    assert do.shape == (T, H, d)
+    init = None if initial_states is None else np.ascontiguousarray(initial_states, np.float64)
+    dfin = None if dfinal_states is None else np.ascontiguousarray(dfinal_states, np.float64)
+    for a in (init, dfin):
+        assert a is None or a.shape == (S, H, N + 1, c, d)
+    out = {"dq": np.empty((T, H, c)), "dkey_logits": np.empty((T, H, c)),
+           "dv": np.empty((T, H, d)), "dlog_alpha": np.empty((T, H, c)),
+           "drouter_logits": np.empty((T, H, N)),
+           "dinitial_states": np.empty((S, H, N + 1, c, d))}
+    rc = lib.sse_oracle_backward(dt, _ptr(q), _ptr(kl), _ptr(v), _ptr(la), _ptr(z), _ptr(cu), S,
+                                 H, c, d, N, topk, _ptr(init), _ptr(do), _ptr(dfin),
+                                 _ptr(out["dq"]), _ptr(out["dkey_logits"]), _ptr(out["dv"]),
+                                 _ptr(out["dlog_alpha"]), _ptr(out["drouter_logits"]),
+                                 _ptr(out["dinitial_states"]), int(threads))
+    if rc != 0:
+        raise ValueError("sse_oracle_backward rejected its arguments")
+    return out

@@ -600,3 +600,296 @@ int sse_oracle_forward_ex(int dtype, const void *q, const void *key_logits, cons
     }
     return 0;
 }
+
+/*
+ * Gradients of the forward (reverse mode over the definition above; the
+ * page's §2.3 notes that the same e on write and read gives the router a
+ * continuous gradient, while the discrete top-k indices carry none).  For
+ * one (sequence, head) unit over tokens [t0, t1), with L = <do, o> +
+ * <dS_final, S_final> as the scalar whose gradient is taken:
+ *   forward: at each token, for every touched partition p (the k selected
+ *     ones with w = e^p, then the shared one with w = 1) keep S_p before the
+ *     write, write S_p = diag(alpha) S_p + w kappa^T v and keep y_p = q S_p;
+ *   reverse: adjoints A_p start at dS_final[p]; for t = t1-1 .. t0 and each
+ *     touched p (A_p is dL/dS_p after the write of token t):
+ *       A_p += w q^T do_t                     (the read w q S_p)
+ *       dq  += w S_p do_t                     (S_p after the write)
+ *       dw  += y_p . do_t + kappa . (A_p v)   (read gate + write gate)
+ *       dkappa += w A_p v;  dv += w kappa A_p
+ *       dlog_alpha_j += alpha_j sum_m A_p[j,m] S_p_before[j,m]
+ *       A_p = diag(alpha) A_p                 (dL/dS_p before the write)
+ *     partitions not touched at t keep their adjoint (identity transition);
+ *     dkey_logits = kappa * (dkappa - kappa . dkappa)  (softmax, eq. 11);
+ *     drouter = e * (de - e . de), de_i = dw of selected partition i, 0
+ *     otherwise (softmax over N, eq. 9).
+ *   dS_init[p] = A_p at the end.
+ * Buffers: S [N+1, c, d] in = initial state (consumed); dS [N+1, c, d] in =
+ * dS_final or NULL (zeros), out = dS_init; do_ [(t1-t0), d]; outputs dq,
+ * dkl, dla [(t1-t0), c], dv [(t1-t0), d], dz [(t1-t0), N].
+ */
+int sse_oracle_backward_unit(int dtype, const void *q, const void *key_logits, const void *v,
+                             const void *log_alpha, const void *router_logits, int64_t t0,
+                             int64_t t1, int h, int H, int c, int d, int N, int k, double *S,
+                             const double *do_, double *dS, double *dq, double *dkl, double *dv,
+                             double *dla, double *dz)
+{
+    if (N < 1 || N > ORACLE_MAX_N || k < 1 || k > N || c < 1 || d < 1 || c > ORACLE_MAX_N ||
+        h < 0 || h >= H || t1 < t0)
+        return -1;
+    const int64_t L = t1 - t0, cd = (int64_t)c * d, np = k + 1;
+    double *saved = (double *)malloc(sizeof(double) * (size_t)(L * np * cd + 1));
+    double *ys = (double *)malloc(sizeof(double) * (size_t)(L * np * d + 1));
+    double *vv = (double *)malloc(sizeof(double) * (size_t)(d + 1));
+    int *selall = (int *)malloc(sizeof(int) * (size_t)(L * k + 1));
+    if (!saved || !ys || !vv || !selall) {
+        free(saved);
+        free(ys);
+        free(vv);
+        free(selall);
+        return -1;
+    }
+    double z[ORACLE_MAX_N], e[ORACLE_MAX_N], qq[ORACLE_MAX_N], kk[ORACLE_MAX_N],
+        ll[ORACLE_MAX_N], kap[ORACLE_MAX_N], alpha[ORACLE_MAX_N], dkap[ORACLE_MAX_N],
+        de[ORACLE_MAX_N];
+    /* load one token's inputs, router and key */
+#define LOAD_TOKEN(t)                                                                     \
+    do {                                                                                  \
+        int64_t rc_ = ((t)*H + h) * (int64_t)c, rd_ = ((t)*H + h) * (int64_t)d,           \
+                rn_ = ((t)*H + h) * (int64_t)N;                                           \
+        for (int i_ = 0; i_ < N; i_++)                                                    \
+            z[i_] = load_value(router_logits, dtype, rn_ + i_);                           \
+        for (int j_ = 0; j_ < c; j_++) {                                                  \
+            qq[j_] = load_value(q, dtype, rc_ + j_);                                      \
+            kk[j_] = load_value(key_logits, dtype, rc_ + j_);                             \
+            ll[j_] = load_value(log_alpha, dtype, rc_ + j_);                              \
+        }                                                                                 \
+        for (int m_ = 0; m_ < d; m_++)                                                    \
+            vv[m_] = load_value(v, dtype, rd_ + m_);                                      \
+        softmax(z, N, e);                                                                 \
+        softmax(kk, c, kap);                                                              \
+        for (int j_ = 0; j_ < c; j_++)                                                    \
+            alpha[j_] = exp(ll[j_]);                                                      \
+    } while (0)
+
+    /* forward, keeping the states before each write and the reads */
+    for (int64_t t = t0; t < t1; t++) {
+        const int64_t lt = t - t0;
+        LOAD_TOKEN(t);
+        int *sel = selall + lt * k;
+        top_k(z, N, k, sel);
+        for (int r = 0; r < np; r++) {
+            const int p = (r < k) ? sel[r] : N;
+            const double w = (r < k) ? e[p] : 1.0;
+            double *St = S + (int64_t)p * cd;
+            memcpy(saved + (lt * np + r) * cd, St, sizeof(double) * (size_t)cd);
+            for (int j = 0; j < c; j++)
+                for (int m = 0; m < d; m++)
+                    St[(int64_t)j * d + m] = alpha[j] * St[(int64_t)j * d + m] + w * kap[j] * vv[m];
+            double *y = ys + (lt * np + r) * d;
+            for (int m = 0; m < d; m++) {
+                double acc = 0.0;
+                for (int j = 0; j < c; j++)
+                    acc += qq[j] * St[(int64_t)j * d + m];
+                y[m] = acc;
+            }
+        }
+    }
+    /* reverse */
+    for (int64_t t = t1 - 1; t >= t0; t--) {
+        const int64_t lt = t - t0;
+        LOAD_TOKEN(t);
+        const int *sel = selall + lt * k;
+        const double *dot = do_ + lt * d;
+        double *gq = dq + lt * c, *gk = dkl + lt * c, *gv = dv + lt * d, *gl = dla + lt * c;
+        for (int j = 0; j < c; j++)
+            gq[j] = gl[j] = dkap[j] = 0.0;
+        for (int m = 0; m < d; m++)
+            gv[m] = 0.0;
+        for (int i = 0; i < N; i++)
+            de[i] = 0.0;
+        for (int r = 0; r < np; r++) {
+            const int p = (r < k) ? sel[r] : N;
+            const double w = (r < k) ? e[p] : 1.0;
+            double *Ap = dS + (int64_t)p * cd;
+            const double *Sb = saved + (lt * np + r) * cd;
+            const double *y = ys + (lt * np + r) * d;
+            /* the read: A += w q^T do */
+            for (int j = 0; j < c; j++)
+                for (int m = 0; m < d; m++)
+                    Ap[(int64_t)j * d + m] += w * qq[j] * dot[m];
+            double dw = 0.0;
+            for (int m = 0; m < d; m++)
+                dw += y[m] * dot[m];
+            for (int j = 0; j < c; j++) {
+                double sdo = 0.0, av = 0.0, as = 0.0;
+                for (int m = 0; m < d; m++) {
+                    const double snew = alpha[j] * Sb[(int64_t)j * d + m] + w * kap[j] * vv[m];
+                    sdo += snew * dot[m];
+                    av += Ap[(int64_t)j * d + m] * vv[m];
+                    as += Ap[(int64_t)j * d + m] * Sb[(int64_t)j * d + m];
+                }
+                gq[j] += w * sdo;
+                dkap[j] += w * av;
+                dw += kap[j] * av;
+                gl[j] += alpha[j] * as;
+            }
+            for (int m = 0; m < d; m++) {
+                double ka = 0.0;
+                for (int j = 0; j < c; j++)
+                    ka += kap[j] * Ap[(int64_t)j * d + m];
+                gv[m] += w * ka;
+            }
+            for (int j = 0; j < c; j++)
+                for (int m = 0; m < d; m++)
+                    Ap[(int64_t)j * d + m] *= alpha[j];
+            if (r < k)
+                de[p] = dw;
+        }
+        double kd = 0.0, ed = 0.0;
+        for (int j = 0; j < c; j++)
+            kd += kap[j] * dkap[j];
+        for (int j = 0; j < c; j++)
+            gk[j] = kap[j] * (dkap[j] - kd);
+        for (int i = 0; i < N; i++)
+            ed += e[i] * de[i];
+        for (int i = 0; i < N; i++)
+            dz[lt * N + i] = e[i] * (de[i] - ed);
+    }
+#undef LOAD_TOKEN
+    free(saved);
+    free(ys);
+    free(vv);
+    free(selall);
+    return 0;
+}
+
+/* Varlen backward, (sequence, head) units over n_threads threads.
+ *   init, dfinal: [S, H, N+1, c, d] or NULL (zeros); do_: [T, H, d]
+ *   dq, dkl, dla: [T, H, c]; dv: [T, H, d]; dz: [T, H, N]; dinit: [S,H,N+1,c,d] */
+struct bwd_job {
+    int dtype;
+    const void *q, *kl, *v, *la, *z;
+    const int32_t *cu;
+    int num_seqs, H, c, d, N, k;
+    const double *init, *dfinal, *do_;
+    double *dq, *dkl, *dv, *dla, *dz, *dinit;
+    int next_unit;
+    pthread_mutex_t mu;
+    int status;
+};
+
+static void *bwd_worker(void *arg)
+{
+    struct bwd_job *J = (struct bwd_job *)arg;
+    const int c = J->c, d = J->d, N = J->N, H = J->H;
+    const int64_t cd = (int64_t)c * d, st = (int64_t)(N + 1) * cd;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int u = J->next_unit++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->num_seqs * H)
+            break;
+        int s = u / H, h = u % H;
+        int64_t t0 = J->cu[s], t1 = J->cu[s + 1], L = t1 - t0;
+        double *S0 = (double *)malloc(sizeof(double) * (size_t)st);
+        double *dS = J->dinit + (int64_t)u * st;
+        double *dob = (double *)malloc(sizeof(double) * (size_t)(L * d + 1));
+        double *bq = (double *)malloc(sizeof(double) * (size_t)(L * c + 1));
+        double *bk = (double *)malloc(sizeof(double) * (size_t)(L * c + 1));
+        double *bl = (double *)malloc(sizeof(double) * (size_t)(L * c + 1));
+        double *bv = (double *)malloc(sizeof(double) * (size_t)(L * d + 1));
+        double *bz = (double *)malloc(sizeof(double) * (size_t)(L * N + 1));
+        int rc = -1;
+        if (S0 && dob && bq && bk && bl && bv && bz) {
+            if (J->init)
+                memcpy(S0, J->init + (int64_t)u * st, sizeof(double) * (size_t)st);
+            else
+                memset(S0, 0, sizeof(double) * (size_t)st);
+            if (J->dfinal)
+                memcpy(dS, J->dfinal + (int64_t)u * st, sizeof(double) * (size_t)st);
+            else
+                memset(dS, 0, sizeof(double) * (size_t)st);
+            for (int64_t t = 0; t < L; t++)
+                memcpy(dob + t * d, J->do_ + ((t0 + t) * H + h) * d, sizeof(double) * (size_t)d);
+            rc = sse_oracle_backward_unit(J->dtype, J->q, J->kl, J->v, J->la, J->z, t0, t1, h, H,
+                                          c, d, N, J->k, S0, dob, dS, bq, bk, bv, bl, bz);
+        }
+        if (rc == 0) {
+            for (int64_t t = 0; t < L; t++) {
+                const int64_t g = (t0 + t) * H + h;
+                memcpy(J->dq + g * c, bq + t * c, sizeof(double) * (size_t)c);
+                memcpy(J->dkl + g * c, bk + t * c, sizeof(double) * (size_t)c);
+                memcpy(J->dla + g * c, bl + t * c, sizeof(double) * (size_t)c);
+                memcpy(J->dv + g * d, bv + t * d, sizeof(double) * (size_t)d);
+                memcpy(J->dz + g * N, bz + t * N, sizeof(double) * (size_t)N);
+            }
+        } else {
+            J->status = -1;
+        }
+        free(S0);
+        free(dob);
+        free(bq);
+        free(bk);
+        free(bl);
+        free(bv);
+        free(bz);
+    }
+    return NULL;
+}
+
+int sse_oracle_backward(int dtype, const void *q, const void *key_logits, const void *v,
+                        const void *log_alpha, const void *router_logits,
+                        const int32_t *cu_seqlens, int num_seqs, int H, int c, int d, int N,
+                        int k, const double *init, const double *do_, const double *dfinal,
+                        double *dq, double *dkl, double *dv, double *dla, double *dz,
+                        double *dinit, int n_threads)
+{
+    if (num_seqs < 0 || H < 1 || n_threads < 1)
+        return -1;
+    for (int s = 0; s < num_seqs; s++)
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+    struct bwd_job J;
+    memset(&J, 0, sizeof J);
+    J.dtype = dtype;
+    J.q = q;
+    J.kl = key_logits;
+    J.v = v;
+    J.la = log_alpha;
+    J.z = router_logits;
+    J.cu = cu_seqlens;
+    J.num_seqs = num_seqs;
+    J.H = H;
+    J.c = c;
+    J.d = d;
+    J.N = N;
+    J.k = k;
+    J.init = init;
+    J.dfinal = dfinal;
+    J.do_ = do_;
+    J.dq = dq;
+    J.dkl = dkl;
+    J.dv = dv;
+    J.dla = dla;
+    J.dz = dz;
+    J.dinit = dinit;
+    pthread_mutex_init(&J.mu, NULL);
+    if (n_threads == 1) {
+        bwd_worker(&J);
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+        int started = 0;
+        for (int i = 0; i < n_threads; i++)
+            if (th && pthread_create(&th[i], NULL, bwd_worker, &J) == 0)
+                started++;
+            else
+                break;
+        if (started == 0)
+            bwd_worker(&J);
+        for (int i = 0; i < started; i++)
+            pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&J.mu);
+    return J.status;
+}

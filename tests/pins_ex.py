@@ -15,8 +15,10 @@ NAMES = ("q", "key_logits", "v", "log_alpha", "router_logits")
 
 def _rel(a, b):
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
     scale = max(np.sqrt(np.mean(b * b)), 1e-300)
-    return float(np.max(np.abs(a - b)) / scale) if a.size else 0.0
+    return float(np.max(np.abs(a - b)) / scale)
 
 
 def _weights(z, N, k):

@@ -16,8 +16,10 @@ NAMES4 = ("q", "key_logits", "v", "log_alpha")
 
 def _rel(a, b):
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
     scale = max(np.sqrt(np.mean(b * b)), 1e-300)
-    return float(np.max(np.abs(a - b)) / scale) if a.size else 0.0
+    return float(np.max(np.abs(a - b)) / scale)
 
 
 def row_topk_mask(kl, k):

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from pins import PINS
+from pins_backward import BACKWARD_PINS
 from pins_ex import EX_PINS
 from pins_rowsparse import ROWSPARSE_PINS
 
@@ -63,6 +64,21 @@ MUTANTS = {
     "ex_read_set_is_write_set": ("top_k(zr, N, krr, R);             /* read set */",
                                  "top_k(z, N, krr, R);"),
     "ex_no_shared_read": ("for (int r = 0; r <= krr; r++) {", "for (int r = 0; r < krr; r++) {"),
+    # backward
+    "bwd_adjoint_not_decayed": ("                    Ap[(int64_t)j * d + m] *= alpha[j];",
+                                "                    (void)0;"),
+    "bwd_no_read_gate_gradient": ("                dw += y[m] * dot[m];",
+                                  "                dw += 0.0 * y[m] * dot[m];"),
+    "bwd_key_softmax_jacobian_sign": ("gk[j] = kap[j] * (dkap[j] - kd);",
+                                      "gk[j] = kap[j] * (dkap[j] + kd);"),
+    "bwd_decay_gradient_without_alpha": ("gl[j] += alpha[j] * as;", "gl[j] += as;"),
+    "bwd_query_gradient_before_write": (
+        "const double snew = alpha[j] * Sb[(int64_t)j * d + m] + w * kap[j] * vv[m];",
+        "const double snew = Sb[(int64_t)j * d + m];"),
+    "bwd_router_jacobian_no_mean": ("dz[lt * N + i] = e[i] * (de[i] - ed);",
+                                    "dz[lt * N + i] = e[i] * de[i];"),
+    "bwd_read_adjoint_missing_gate": ("Ap[(int64_t)j * d + m] += w * qq[j] * dot[m];",
+                                      "Ap[(int64_t)j * d + m] += qq[j] * dot[m];"),
     "rowsparse_read_before_write": ("            o[(t - t0) * d + m] = acc;",
                                     "            o[(t - t0) * d + m] = acc - qq[0] * kappa[0] * vv[m];"),
 }
@@ -79,7 +95,7 @@ def test_mutant_is_caught(name, tmp_path):
                       extra_flags=("-Wno-error", "-w"))
     lib = oracle.load(so)
     failed = []
-    for pin in PINS + ROWSPARSE_PINS + EX_PINS:
+    for pin in PINS + ROWSPARSE_PINS + EX_PINS + BACKWARD_PINS:
         try:
             pin(lib)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
