@@ -249,6 +249,41 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of sse_forward (the default layer: varlen grouping, shared
+ * partition with the routed q/k, read set = write set).  Gradients of the
+ * scalar L = <d_o, o> + <d_final_states, final_states> with respect to the
+ * five token inputs and the initial states, through both gates (§2.3: the
+ * same router probability e gates the write and the read, so the router
+ * logits get a continuous gradient through e = softmax(router_logits); the
+ * discrete top-k choice itself carries none) and the key softmax.  The
+ * routing and grouping are recomputed from the inputs (the same top-k
+ * choice as the forward); the reverse pass runs over the same (sequence,
+ * head, partition) segments in reverse chunk order, from chunk-start states
+ * a forward sweep stores in the workspace.  Arithmetic in fp32 (fp32 MFMA
+ * 16x16x4), whatever the input type.
+ *   inputs as sse_forward; initial_states [num_seqs, H, N+1, c, d] or NULL
+ *   d_o                   [total_tokens, H, d] fp32
+ *   d_final_states        [num_seqs, H, N+1, c, d] fp32 or NULL (zeros)
+ *   dq, dkey_logits, dlog_alpha [total_tokens, H, c] fp32 (written)
+ *   dv                    [total_tokens, H, d] fp32 (written)
+ *   drouter_logits        [total_tokens, H, N] fp32 (written)
+ *   dinitial_states       [num_seqs, H, N+1, c, d] fp32 or NULL
+ *   workspace >= sse_backward_workspace_bytes(...) (chunk-start states and
+ *   per-record gradient slots: about 4 c d / 16 + 4 (k+1)(3c + d) bytes per
+ *   (token, head) plus the forward's grouping arrays).
+ * Deterministic: per-record gradients go to slots summed in a fixed order.
+ */
+size_t sse_backward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                    int c, int d, int N, int topk);
+int sse_backward(const void *q, const void *key_logits, const void *v, const void *log_alpha,
+                 const void *router_logits, int dtype, const int32_t *cu_seqlens, int num_seqs,
+                 int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                 const float *initial_states, const float *d_o, const float *d_final_states,
+                 float *dq, float *dkey_logits, float *dv, float *dlog_alpha,
+                 float *drouter_logits, float *dinitial_states, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
  * Row-sparse top-k key variant (§2.2, eqs. (7)-(8)): one state per head,
  * no partitions.  Per token t and head h:
  *   kappa_t = softmax over the row_topk largest key logits (descending,

@@ -28,6 +28,7 @@ SCHEDULES = {"varlen": SSE_SCHEDULE_VARLEN, "masked": SSE_SCHEDULE_MASKED}
 EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "sse_forward",
             "sse_forward_noalloc_max_bytes", "sse_forward_noalloc",
             "sse_forward_ex_workspace_bytes", "sse_forward_ex",
+            "sse_backward_workspace_bytes", "sse_backward",
             "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
             "sse_group_by_partition", "sse_rowsparse_workspace_bytes", "sse_rowsparse_forward",
             "sse_trace_enable", "sse_trace_read")
@@ -66,6 +67,11 @@ def lib():
     L.sse_forward_ex.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, I, I, P,
                                  P, P, P, P, P, P, P, P, P, SZ, P]
     L.sse_forward_ex.restype = I
+    L.sse_backward_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I]
+    L.sse_backward_workspace_bytes.restype = SZ
+    L.sse_backward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
+                               P, P, P, P, SZ, P]
+    L.sse_backward.restype = I
     L.sse_forward_noalloc_max_bytes.argtypes = []
     L.sse_forward_noalloc_max_bytes.restype = SZ
     L.sse_forward_noalloc.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
@@ -227,6 +233,59 @@ def sse_forward_ex(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqle
                               _ptr(seg_slot), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "sse_forward_ex")
     return o, final_states
+
+
+def sse_backward_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk) -> int:
+    return int(lib().sse_backward_workspace_bytes(total_tokens, num_seqs, max_seqlen, H, c, d, N,
+                                                  topk))
+
+
+def sse_backward(q, key_logits, v, log_alpha, router_logits, N, topk, cu_seqlens, d_o,
+                 max_seqlen=None, initial_states=None, d_final_states=None, *,
+                 want_dinitial=False, workspace=None, out=None):
+    """Gradients of <d_o, o> + <d_final_states, final_states> of sse_forward.
+    Returns a dict of fp32 tensors dq, dkey_logits, dlog_alpha [T,H,c], dv
+    [T,H,d], drouter_logits [T,H,N] and (want_dinitial) dinitial_states
+    [S,H,N+1,c,d].  ``out`` may hold preallocated tensors under those names."""
+    dev = q.device
+    T, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (T, H, c), "q"), (key_logits, (T, H, c), "key_logits"),
+                       (log_alpha, (T, H, c), "log_alpha"), (v, (T, H, d), "v"),
+                       (router_logits, (T, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    S = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens", dev)
+    _need(d_o, (T, H, d), torch.float32, "d_o", dev)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S > 0 else 0
+    for t, nm in ((initial_states, "initial_states"), (d_final_states, "d_final_states")):
+        if t is not None:
+            _need(t, (S, H, N + 1, c, d), torch.float32, nm, dev)
+    shapes = {"dq": (T, H, c), "dkey_logits": (T, H, c), "dlog_alpha": (T, H, c),
+              "dv": (T, H, d), "drouter_logits": (T, H, N)}
+    if want_dinitial:
+        shapes["dinitial_states"] = (S, H, N + 1, c, d)
+    res = {}
+    for nm, shp in shapes.items():
+        t = None if out is None else out.get(nm)
+        if t is None:
+            t = torch.empty(shp, dtype=torch.float32, device=dev)
+        _need(t, shp, torch.float32, nm, dev)
+        res[nm] = t
+    nbytes = sse_backward_workspace_bytes(T, S, max_seqlen, H, c, d, N, topk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sse_backward(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                            _ptr(router_logits), _dtype_code(q), _ptr(cu_seqlens), S,
+                            int(max_seqlen), T, H, c, d, N, topk, _ptr(initial_states),
+                            _ptr(d_o), _ptr(d_final_states), _ptr(res["dq"]),
+                            _ptr(res["dkey_logits"]), _ptr(res["dv"]), _ptr(res["dlog_alpha"]),
+                            _ptr(res["drouter_logits"]), _ptr(res.get("dinitial_states")),
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "sse_backward")
+    return res
 
 
 def sse_forward_noalloc_max_bytes() -> int:

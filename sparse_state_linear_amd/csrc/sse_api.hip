@@ -337,6 +337,32 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     return SSE_OK;
 }
 
+// ---- backward -----------------------------------------------------------------
+struct BwdLayout {
+    FwdLayout f;              // routing and grouping part (no slots of its own)
+    size_t ckpt, g_dq, g_dkl, g_dla, g_dv, g_dw, total;
+    int64_t ckpt_shared;
+};
+
+bool backward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N, int K,
+                     BwdLayout& L) {
+    if (!forward_layout(T, S, max_seqlen, H, 0, 0, N, K, L.f)) return false;
+    const int64_t SH = (int64_t)S * H;
+    L.ckpt_shared = sse::bwd_ckpt_chunks(T * H, SH);
+    const int64_t chunks = L.ckpt_shared + sse::bwd_ckpt_chunks(T * H * K, SH * N);
+    const int64_t slots = T * H * (K + 1);
+    if (slots >= INT_MAX) return false;
+    size_t off = L.f.part;   // the forward layout's slot area is not used
+    L.ckpt = off;  off += align_up(sizeof(float) * (size_t)chunks * (size_t)c * (size_t)d);
+    L.g_dq = off;  off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
+    L.g_dkl = off; off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
+    L.g_dla = off; off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
+    L.g_dv = off;  off += align_up(sizeof(float) * (size_t)slots * (size_t)d);
+    L.g_dw = off;  off += align_up(sizeof(float) * (size_t)slots);
+    L.total = off;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -479,6 +505,86 @@ int sse_rowsparse_forward(const void* q, const void* key_logits, const void* v,
     e = sse::launch_chunk_local(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     return hip_status(sse::launch_chunk_shared(a, dtype, c, d, s));
+}
+
+size_t sse_backward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
+                                    int c, int d, int N, int topk) {
+    if (check_common(SSE_BF16, H, c, d, N, topk) != SSE_OK) return 0;
+    BwdLayout L;
+    if (!backward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L)) return 0;
+    return L.total;
+}
+
+int sse_backward(const void* q, const void* key_logits, const void* v, const void* log_alpha,
+                 const void* router_logits, int dtype, const int32_t* cu_seqlens, int num_seqs,
+                 int max_seqlen, int64_t total_tokens, int H, int c, int d, int N, int topk,
+                 const float* initial_states, const float* d_o, const float* d_final_states,
+                 float* dq, float* dkey_logits, float* dv, float* dlog_alpha,
+                 float* drouter_logits, float* dinitial_states, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int st = check_common(dtype, H, c, d, N, topk);
+    if (st != SSE_OK) return st;
+    if (total_tokens < 0 || num_seqs < 0 || max_seqlen < 0) return SSE_ERR_INVALID_ARG;
+    if (total_tokens > 0 && num_seqs == 0) return SSE_ERR_INVALID_ARG;
+    if (!cu_seqlens) return SSE_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !d_o ||
+                             !dq || !dkey_logits || !dv || !dlog_alpha || !drouter_logits))
+        return SSE_ERR_INVALID_ARG;
+    BwdLayout L;
+    if (!backward_layout(total_tokens, num_seqs, max_seqlen, H, c, d, N, topk, L))
+        return SSE_ERR_UNSUPPORTED;
+    if (total_tokens * H * (topk + 1) * (c > d ? c : d) >= (int64_t(1) << 31))
+        return SSE_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.f.idx);
+    float* w = reinterpret_cast<float*>(ws + L.f.w);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + L.f.counts);
+    int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.f.seg_off);
+    uint2* rinfo = reinterpret_cast<uint2*>(ws + L.f.rinfo);
+    sse::SegRec* seg_rec = reinterpret_cast<sse::SegRec*>(ws + L.f.seg_rec);
+    float* lnz2 = reinterpret_cast<float*>(ws + L.f.lnz2);
+    // the forward's routing and grouping (the segments the reverse pass walks)
+    hipError_t e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
+                                           max_seqlen, total_tokens, H, c, N, topk, idx, w,
+                                           counts, rinfo, lnz2, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N, topk,
+                              counts, seg_off, lnz2, seg_rec, s);
+    if (e != hipSuccess) return SSE_ERR_HIP;
+    sse::BwdArgs a = {};
+    a.q = q;
+    a.kl = key_logits;
+    a.v = v;
+    a.la = log_alpha;
+    a.z = router_logits;
+    a.cu = cu_seqlens;
+    a.seg_offsets = seg_off;
+    a.seg_rec = seg_rec;
+    a.sel_idx = idx;
+    a.init = initial_states;
+    a.dfinal = d_final_states;
+    a.dout = d_o;
+    a.ckpt = reinterpret_cast<float*>(ws + L.ckpt);
+    a.ckpt_shared_chunks = L.ckpt_shared;
+    a.g_dq = reinterpret_cast<float*>(ws + L.g_dq);
+    a.g_dkl = reinterpret_cast<float*>(ws + L.g_dkl);
+    a.g_dla = reinterpret_cast<float*>(ws + L.g_dla);
+    a.g_dv = reinterpret_cast<float*>(ws + L.g_dv);
+    a.g_dw = reinterpret_cast<float*>(ws + L.g_dw);
+    a.dq = dq;
+    a.dkl = dkey_logits;
+    a.dla = dlog_alpha;
+    a.dv = dv;
+    a.dz = drouter_logits;
+    a.dinit = dinitial_states;
+    a.rows = total_tokens * H;
+    a.num_seqs = num_seqs;
+    a.H = H;
+    a.N = N;
+    a.topk = topk;
+    return hip_status(sse::launch_backward(a, dtype, c, d, s));
 }
 
 int sse_trace_enable(int enable) {

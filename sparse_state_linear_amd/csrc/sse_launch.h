@@ -135,6 +135,34 @@ hipError_t launch_chunk_f64(int mode, const ChunkArgs& a, int c, int d, hipStrea
 hipError_t launch_rowsparse_mask(const void* kl, const void* la, int dtype, int64_t rows, int c,
                                  int k, int identity, void* kl_out, void* la_out, hipStream_t st);
 
+// Arguments of the backward pass (backward.hip).
+struct BwdArgs {
+    const void *q, *kl, *v, *la, *z;
+    const int32_t* cu;
+    const int32_t* seg_offsets;   // routed segments of the forward's grouping
+    const SegRec* seg_rec;
+    const int32_t* sel_idx;       // [T, H, topk] the forward's top-k choices
+    const float* init;            // [S, H, N+1, c, d] or null
+    const float* dfinal;          // gradient of the final states, or null
+    const float* dout;            // [T, H, d] gradient of o
+    float* ckpt;                  // chunk-start states: shared chains, then routed segments
+    int64_t ckpt_shared_chunks;   // checkpoints reserved for the shared chains
+    float *g_dq, *g_dkl, *g_dla;  // per-record slots [T*H*(topk+1), c]
+    float* g_dv;                  // [T*H*(topk+1), d]
+    float* g_dw;                  // [T*H*(topk+1)]
+    float *dq, *dkl, *dla, *dv, *dz, *dinit;   // outputs (dinit may be null)
+    int64_t rows;                 // T*H
+    int num_seqs, H, N, topk;
+};
+
+// Checkpoints (chunks of 16 records) the backward reserves: each segment
+// of n records starts at floor(first record / 16) + 2 * (segment index).
+inline int64_t bwd_ckpt_chunks(int64_t records, int64_t segments) {
+    return records / 16 + 2 * segments + 2;
+}
+
+hipError_t launch_backward(const BwdArgs& a, int dtype, int c, int d, hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* kl, const void* v, const void* la,
                          const void* z, int dtype, int B, int H, int c, int d, int N, int K,
                          float* states, float* o, int32_t* topk_idx, hipStream_t st);

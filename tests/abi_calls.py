@@ -39,6 +39,11 @@ def declare(L):
     L.sse_forward_ex.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, I, I, P,
                                  P, P, P, P, P, P, P, P, P, SZ, P]
     L.sse_forward_ex.restype = I
+    L.sse_backward_workspace_bytes.argtypes = [I64, I, I, I, I, I, I, I]
+    L.sse_backward_workspace_bytes.restype = SZ
+    L.sse_backward.argtypes = [P, P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P, P, P,
+                               P, P, P, P, SZ, P]
+    L.sse_backward.restype = I
     L.sse_rowsparse_workspace_bytes.argtypes = [I64, I, I, I, I, I]
     L.sse_rowsparse_workspace_bytes.restype = SZ
     L.sse_rowsparse_forward.argtypes = [P, P, P, P, I, P, I, I, I64, I, I, I, I, I, P, P, P, P,
@@ -115,6 +120,25 @@ FORWARD_EX_REJECTS = [
 ]
 
 
+def backward(L, **kw):
+    a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, z=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16,
+             T=16, H=2, c=32, d=32, N=4, k=2, init=None, do=FAKE, dfin=None, dq=FAKE, dkl=FAKE,
+             dv=FAKE, dla=FAKE, dz=FAKE, dinit=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.sse_backward(a["q"], a["kl"], a["v"], a["la"], a["z"], a["dtype"], a["cu"], a["S"],
+                          a["maxlen"], a["T"], a["H"], a["c"], a["d"], a["N"], a["k"], a["init"],
+                          a["do"], a["dfin"], a["dq"], a["dkl"], a["dv"], a["dla"], a["dz"],
+                          a["dinit"], a["ws"], a["wsb"], a["stream"])
+
+
+BACKWARD_REJECTS = [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dz=None), INVALID),
+    (dict(dla=None), INVALID), (dict(k=5), INVALID), (dict(S=0), INVALID),
+    (dict(c=48), UNSUPPORTED), (dict(wsb=64), WORKSPACE), (dict(ws=None), WORKSPACE),
+    (dict(T=1 << 25, S=1, maxlen=1 << 25, H=16, c=128, d=128), UNSUPPORTED),
+]
+
+
 def rowsparse(L, **kw):
     a = dict(q=FAKE, kl=FAKE, v=FAKE, la=FAKE, dtype=BF16, cu=FAKE, S=1, maxlen=16, T=16, H=2,
              c=32, d=32, k=8, ident=1, init=None, o=FAKE, fs=FAKE, ws=FAKE, wsb=1 << 30,
@@ -174,6 +198,12 @@ def exercise(L) -> int:
     assert L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 3) > \
         L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 0) > 0
     assert L.sse_forward_ex_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2, 9) == 0
+    for kw, code in BACKWARD_REJECTS:
+        got = backward(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    assert L.sse_backward_workspace_bytes(1000, 2, 600, 4, 64, 64, 8, 2) > 0
+    assert L.sse_backward_workspace_bytes(1000, 2, 600, 4, 48, 64, 8, 2) == 0
     for kw, code in ROWSPARSE_REJECTS:
         got = rowsparse(L, **kw)
         assert got == code, (kw, got, code)

@@ -41,6 +41,7 @@ hipError_t launch_rowsparse_mask(const void*, const void*, int, int64_t, int, in
                                  void*, hipStream_t) {
     return stub();
 }
+hipError_t launch_backward(const BwdArgs&, int, int, int, hipStream_t) { return stub(); }
 hipError_t launch_decode(const void*, const void*, const void*, const void*, const void*, int, int,
                          int, int, int, int, int, float*, float*, int32_t*, hipStream_t) {
     return stub();
