@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SSE fwd tokens/s (T=8K,c=d=128,N=16,k=2) + decode tok/s; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 NAMES = ("q", "key_logits", "v", "log_alpha", "router_logits")
 
 
@@ -77,7 +78,8 @@ def chunk_flops(records, c, d, C=64):
     return records * 2 * (C * c / 2 + C * d / 2 + 2 * c * d)
 
 
-def run_forward(args, w, si, sse, torch, inp=None):
+def run_forward(args, w, si, sse, torch, inp=None, schedule=None):
+    """Time sse_forward (or sse_forward_ex with the given schedule) on w."""
     if inp is None:
         inp = si.forward_inputs(w)
     cu = inp["cu_seqlens"]
@@ -92,8 +94,12 @@ def run_forward(args, w, si, sse, torch, inp=None):
                      dtype=torch.uint8, device="cuda")
 
     def step():
-        sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], max_len,
-                        o=o, final_states=fs, workspace=ws)
+        if schedule is None:
+            sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], max_len,
+                            o=o, final_states=fs, workspace=ws)
+        else:
+            sse.sse_forward_ex(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"],
+                               max_len, schedule=schedule, o=o, final_states=fs, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -134,18 +140,107 @@ def fig6_sweep(args, si, sse, torch):
                             T=L // 2)
             inp = dict(base)
             inp["router_logits"] = np.ascontiguousarray(base["router_logits"][..., :N])
-            T, S, total_ms, stages, _ = run_forward(ns, w, si, sse, torch, inp=inp)
-            ms = total_ms / ns.steps
-            rows.append({"L": L, "N": N, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
-                         "stage_ms": stages})
-            log(f"fig6 L={L} N={N}: {ms:.3f} ms")
-    spread = {}
+            for sched in ("varlen", "masked"):
+                T, S, total_ms, stages, _ = run_forward(ns, w, si, sse, torch, inp=inp,
+                                                        schedule=sched)
+                ms = total_ms / ns.steps
+                rows.append({"L": L, "N": N, "schedule": sched, "ms": ms,
+                             "tokens_per_s": T / (ms * 1e-3), "stage_ms": stages})
+                log(f"fig6 L={L} N={N} {sched}: {ms:.3f} ms")
+    spread, faster = {}, {}
     for L in sorted({r["L"] for r in rows}):
-        t = [r["ms"] for r in rows if r["L"] == L]
+        t = [r["ms"] for r in rows if r["L"] == L and r["schedule"] == "varlen"]
         spread[str(L)] = max(t) / min(t)
+        for N in (4, 8, 16):
+            tv = [r["ms"] for r in rows if r["L"] == L and r["N"] == N and r["schedule"] == "varlen"][0]
+            tm = [r["ms"] for r in rows if r["L"] == L and r["N"] == N and r["schedule"] == "masked"][0]
+            faster[f"L{L}_N{N}"] = "masked" if tm < tv else "varlen"
     return {"setting": "H=8, c=d=128, k=1, cu_seqlens=[0, L/2, L], N in {4, 8, 16}, bf16 "
-                       "inputs, router logits N(0,1), forward only",
-            "rows": rows, "max_over_min_across_N": spread}
+                       "inputs, router logits N(0,1), forward only, varlen and masked schedules",
+            "rows": rows, "varlen_max_over_min_across_N": spread, "faster_schedule": faster}
+
+
+def timed(torch, fn, steps, warmup):
+    """Mean ms of fn over `steps` calls after `warmup` calls (HIP events on
+    the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_backward(args, w, si, sse, torch):
+    """sse_backward on the main workload: all five input gradients and the
+    initial-state gradient."""
+    inp = si.forward_inputs(w)
+    cu = inp["cu_seqlens"]
+    T, S = int(cu[-1]), len(cu) - 1
+    max_len = int((cu[1:] - cu[:-1]).max())
+    d_in = {n: to_dev(inp[n]) for n in NAMES + ("cu_seqlens",)}
+    del inp
+    do = torch.randn((T, w.H, w.d), dtype=torch.float32, device="cuda")
+    out = {nm: torch.empty(shp, dtype=torch.float32, device="cuda") for nm, shp in (
+        ("dq", (T, w.H, w.c)), ("dkey_logits", (T, w.H, w.c)), ("dlog_alpha", (T, w.H, w.c)),
+        ("dv", (T, w.H, w.d)), ("drouter_logits", (T, w.H, w.N)),
+        ("dinitial_states", (S, w.H, w.N + 1, w.c, w.d)))}
+    ws = torch.empty(sse.sse_backward_workspace_bytes(T, S, max_len, w.H, w.c, w.d, w.N, w.topk),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        sse.sse_backward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], do,
+                         max_len, want_dinitial=True, workspace=ws, out=out)
+
+    ms = timed(torch, step, args.bwd_steps, 1)
+    HT = T * w.H
+    records = HT * (w.topk + 1)
+    # inputs read once (bf16), do read once, the five input gradients written
+    # once, the initial-state gradients written once (fp32)
+    nbytes = (HT * 2 * (3 * w.c + w.d + w.N) + HT * 4 * w.d + HT * 4 * (3 * w.c + w.d + w.N)
+              + S * w.H * (w.N + 1) * w.c * w.d * 4)
+    # five c x d products and three causal C x c / C x d pairs per record (C = 64)
+    C = 64
+    flops = records * 2 * (5 * w.c * w.d + 1.5 * C * w.c + 1.5 * C * w.d)
+    roof_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_F32_PEAK_TFLOPS * 1e12)) * 1e3
+    return {"workload": w.notes + ", gradients of all five inputs and the initial states",
+            "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops, "roofline_ms": roof_ms, "frac": roof_ms / ms,
+            "bound": "mfma fp32 (the backward computes in fp32: 157.3 TFLOP/s)"}
+
+
+def run_rowsparse(args, si, sse, torch):
+    """Row-sparse top-k key variant on the main shape (B=4, H=16, T=8192,
+    c=d=128), k = 32 of 128 rows, identity transition on unselected rows."""
+    w = si.Workload("rowsparse_main", "bf16", H=16, c=128, d=128, N=1, topk=1, B=4, T=8192)
+    inp = si.forward_inputs(w)
+    cu = inp["cu_seqlens"]
+    T, S = int(cu[-1]), len(cu) - 1
+    d_in = {n: to_dev(inp[n]) for n in ("q", "key_logits", "v", "log_alpha", "cu_seqlens")}
+    del inp
+    o = torch.empty((T, w.H, w.d), dtype=torch.float32, device="cuda")
+    fs = torch.empty((S, w.H, w.c, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sse.sse_rowsparse_workspace_bytes(T, S, w.T, w.H, w.c, w.d),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        sse.sse_rowsparse_forward(d_in["q"], d_in["key_logits"], d_in["v"], d_in["log_alpha"], 32,
+                                  d_in["cu_seqlens"], w.T, o=o, final_states=fs, workspace=ws)
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    HT = T * w.H
+    nbytes = HT * 2 * (3 * w.c + w.d) + HT * 4 * w.d + S * w.H * w.c * w.d * 4
+    flops = chunk_flops(HT, w.c, w.d)
+    roof_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    return {"workload": "bf16, B=4 H=16 T=8192 c=d=128, row top-k 32 of 128, identity on "
+                        "unselected rows", "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "roofline_ms": roof_ms,
+            "frac": roof_ms / ms}
 
 
 def run_decode(args, si, sse, torch):
@@ -312,6 +407,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the varlen forward timing")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration")
+    ap.add_argument("--bwd-steps", type=int, default=5, help="timed backward calls")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the backward, masked-schedule and row-sparse timings")
     ap.add_argument("--fig6", action="store_true",
                     help="also time the forward over L and N in the operator-timing setting (Fig. 6)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -390,6 +488,27 @@ def main():
             peaks["decode_frac"] = decode["achieved_GBs"] / peaks["inplace_rmw_GBs"]
         log(f"measured peaks {peaks}")
 
+    extra = None
+    if not args.no_extra:
+        log("masked schedule forward", w.notes)
+        Tm, _, m_total_ms, m_stages, _ = run_forward(args, w, si, sse, torch, schedule="masked")
+        m_ms = m_total_ms / args.steps
+        log(f"masked forward {m_ms:.3f} ms/step; stages {m_stages}")
+        log("backward", w.notes)
+        bwd = run_backward(args, w, si, sse, torch)
+        log(f"backward {bwd['ms_per_step']:.3f} ms/step")
+        log("row-sparse forward")
+        rs = run_rowsparse(args, si, sse, torch)
+        log(f"row-sparse forward {rs['ms_per_step']:.3f} ms/step")
+        extra = {
+            "masked_forward": {"workload": w.notes + ", masked schedule",
+                               "ms_per_step": m_ms, "tokens_per_s": Tm / (m_ms * 1e-3),
+                               "roofline_ms": roof_ms, "frac": roof_ms / m_ms,
+                               "stage_ms": m_stages},
+            "backward": bwd,
+            "rowsparse_forward": rs,
+        }
+
     fig6 = fig6_sweep(args, si, sse, torch) if args.fig6 else None
 
     cpu = None
@@ -440,6 +559,9 @@ def main():
         "varlen_forward": varlen,
         "measured_peaks": peaks,
         "decode": decode,
+        "masked_forward": None if extra is None else extra["masked_forward"],
+        "backward": None if extra is None else extra["backward"],
+        "rowsparse_forward": None if extra is None else extra["rowsparse_forward"],
         "fig6_sweep": fig6,
         "cpu_baseline": cpu,
     }
