@@ -209,6 +209,29 @@ int sse_decode_step(const void *q, const void *key_logits, const void *v, const 
                     int topk, float *states, float *o, int32_t *topk_idx, void *stream);
 
 /*
+ * General decode step: sse_decode_step with the options of sse_forward_ex
+ * (§2.5 the shared partition's own query and key; §2.3 a read set chosen
+ * apart from the write set).  Each optional pointer may be NULL:
+ *   q_shared, key_logits_shared [B, H, c] (dtype): NULL -> q / key_logits
+ *   read_router_logits          [B, H, N] (dtype): the read set is its
+ *             read_topk largest entries (descending, equal logits -> lower
+ *             index), read weights their softmax over N; NULL -> the write
+ *             set and weights (read_topk is then ignored)
+ *   read_topk_idx               [B, H, read_topk] int32 or NULL
+ * The write set's states are updated (eq. 12); each read partition is read
+ * after the writes (a partition read but not written keeps its state and is
+ * not stored); o = sum over the read set of e_r q S + q_shared S_shared.
+ * States that are neither written nor read are not touched.  No workspace;
+ * deterministic.  1 <= read_topk <= N, <= 8 when read_router_logits is set.
+ */
+int sse_decode_step_ex(const void *q, const void *key_logits, const void *v,
+                       const void *log_alpha, const void *router_logits, int dtype, int B, int H,
+                       int c, int d, int N, int topk, const void *q_shared,
+                       const void *key_logits_shared, const void *read_router_logits,
+                       int read_topk, float *states, float *o, int32_t *topk_idx,
+                       int32_t *read_topk_idx, void *stream);
+
+/*
  * Stage entry point: the router alone (§2.3 eqs. 9-10) for `rows` rows of
  * N logits (rows = tokens x heads).
  *   router_logits [rows, N] (dtype) -> topk_idx [rows, topk] int32,

@@ -29,7 +29,7 @@ EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "
             "sse_forward_noalloc_max_bytes", "sse_forward_noalloc",
             "sse_forward_ex_workspace_bytes", "sse_forward_ex",
             "sse_backward_workspace_bytes", "sse_backward",
-            "sse_decode_step", "sse_router_topk", "sse_group_workspace_bytes",
+            "sse_decode_step", "sse_decode_step_ex", "sse_router_topk", "sse_group_workspace_bytes",
             "sse_group_by_partition", "sse_rowsparse_workspace_bytes", "sse_rowsparse_forward",
             "sse_trace_enable", "sse_trace_read")
 
@@ -79,6 +79,9 @@ def lib():
     L.sse_forward_noalloc.restype = I
     L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
     L.sse_decode_step.restype = I
+    L.sse_decode_step_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
+                                     P]
+    L.sse_decode_step_ex.restype = I
     L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
     L.sse_router_topk.restype = I
     L.sse_group_workspace_bytes.argtypes = [I64, I, I, I, I, I]
@@ -342,6 +345,37 @@ def sse_decode_step(q, key_logits, v, log_alpha, router_logits, N, topk, states,
                                _ptr(router_logits), _dtype_code(q), B, H, c, d, N, topk,
                                _ptr(states), _ptr(o), _ptr(topk_idx), _stream(dev))
     _check(st, "sse_decode_step")
+    return o
+
+
+def sse_decode_step_ex(q, key_logits, v, log_alpha, router_logits, N, topk, states, *,
+                       q_shared=None, key_logits_shared=None, read_router_logits=None,
+                       read_topk=0, o=None, topk_idx=None, read_topk_idx=None):
+    """Decode step with the shared partition's own query / key logits and a
+    read set from its own router logits (each optional).  ``states``
+    [B,H,N+1,c,d] fp32 is updated in place.  Returns o [B,H,d] fp32."""
+    dev = q.device
+    B, H, c = q.shape
+    d = v.shape[2]
+    dt = q.dtype
+    for t, shp, nm in ((q, (B, H, c), "q"), (key_logits, (B, H, c), "key_logits"),
+                       (log_alpha, (B, H, c), "log_alpha"), (v, (B, H, d), "v"),
+                       (router_logits, (B, H, N), "router_logits")):
+        _need(t, shp, dt, nm, dev)
+    for t, shp, nm in ((q_shared, (B, H, c), "q_shared"),
+                       (key_logits_shared, (B, H, c), "key_logits_shared"),
+                       (read_router_logits, (B, H, N), "read_router_logits")):
+        if t is not None:
+            _need(t, shp, dt, nm, dev)
+    _need(states, (B, H, N + 1, c, d), torch.float32, "states", dev)
+    if o is None:
+        o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    st = lib().sse_decode_step_ex(_ptr(q), _ptr(key_logits), _ptr(v), _ptr(log_alpha),
+                                  _ptr(router_logits), _dtype_code(q), B, H, c, d, N, topk,
+                                  _ptr(q_shared), _ptr(key_logits_shared),
+                                  _ptr(read_router_logits), int(read_topk), _ptr(states),
+                                  _ptr(o), _ptr(topk_idx), _ptr(read_topk_idx), _stream(dev))
+    _check(st, "sse_decode_step_ex")
     return o
 
 

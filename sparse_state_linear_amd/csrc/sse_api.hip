@@ -635,6 +635,30 @@ int sse_decode_step(const void* q, const void* key_logits, const void* v, const 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int sse_decode_step_ex(const void* q, const void* key_logits, const void* v,
+                       const void* log_alpha, const void* router_logits, int dtype, int B, int H,
+                       int c, int d, int N, int topk, const void* q_shared,
+                       const void* key_logits_shared, const void* read_router_logits,
+                       int read_topk, float* states, float* o, int32_t* topk_idx,
+                       int32_t* read_topk_idx, void* stream) {
+    int st = check_common(dtype, H, c, d, N, topk);
+    if (st != SSE_OK) return st;
+    if (B < 0) return SSE_ERR_INVALID_ARG;
+    if (read_router_logits) {
+        if (read_topk < 1 || read_topk > N) return SSE_ERR_INVALID_ARG;
+        if (read_topk > sse::kMaxTopK) return SSE_ERR_UNSUPPORTED;
+    } else if (read_topk_idx) {
+        return SSE_ERR_INVALID_ARG;
+    }
+    if ((int64_t)B * H * (d / 32) * 256 >= ((int64_t)1 << 32)) return SSE_ERR_UNSUPPORTED;
+    if (B > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !states || !o))
+        return SSE_ERR_INVALID_ARG;
+    return hip_status(sse::launch_decode_ex(
+        q, key_logits, v, log_alpha, router_logits, q_shared, key_logits_shared,
+        read_router_logits, dtype, B, H, c, d, N, topk, read_router_logits ? read_topk : 0, states,
+        o, topk_idx, read_topk_idx, static_cast<hipStream_t>(stream)));
+}
+
 int sse_router_topk(const void* router_logits, int dtype, int64_t rows, int N, int topk,
                     int32_t* topk_idx, float* topk_w, void* stream) {
     if (dtype != SSE_F32 && dtype != SSE_BF16) return SSE_ERR_INVALID_ARG;

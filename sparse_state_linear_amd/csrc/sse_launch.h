@@ -163,6 +163,13 @@ inline int64_t bwd_ckpt_chunks(int64_t records, int64_t segments) {
 
 hipError_t launch_backward(const BwdArgs& a, int dtype, int c, int d, hipStream_t st);
 
+// General decode step: own shared q/k and read set (each may be null).
+hipError_t launch_decode_ex(const void* q, const void* kl, const void* v, const void* la,
+                            const void* z, const void* q_sh, const void* kl_sh, const void* zr,
+                            int dtype, int B, int H, int c, int d, int N, int K, int KR,
+                            float* states, float* o, int32_t* topk_idx, int32_t* read_idx,
+                            hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* kl, const void* v, const void* la,
                          const void* z, int dtype, int B, int H, int c, int d, int N, int K,
                          float* states, float* o, int32_t* topk_idx, hipStream_t st);

@@ -28,6 +28,9 @@ def declare(L):
     L.sse_forward_noalloc.restype = I
     L.sse_decode_step.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P]
     L.sse_decode_step.restype = I
+    L.sse_decode_step_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
+                                     P]
+    L.sse_decode_step_ex.restype = I
     L.sse_router_topk.argtypes = [P, I, I64, I, I, P, P, P]
     L.sse_router_topk.restype = I
     L.sse_group_workspace_bytes.argtypes = [I64, I, I, I, I, I]
@@ -170,6 +173,20 @@ def decode(L, **kw):
                              a["d"], a["N"], a["k"], a["states"], FAKE, None, None)
 
 
+DECODE_EX_REJECTS = DECODE_REJECTS + [
+    (dict(zr=FAKE, kr=0), INVALID), (dict(zr=FAKE, kr=5), INVALID),
+    (dict(zr=FAKE, kr=9, N=12), UNSUPPORTED), (dict(ridx=FAKE), INVALID),
+]
+
+
+def decode_ex(L, **kw):
+    a = dict(B=4, H=2, c=32, d=32, N=4, k=2, states=FAKE, dtype=F32, zr=None, kr=0, ridx=None)
+    a.update(kw)
+    return L.sse_decode_step_ex(FAKE, FAKE, FAKE, FAKE, FAKE, a["dtype"], a["B"], a["H"], a["c"],
+                                a["d"], a["N"], a["k"], None, None, a["zr"], a["kr"],
+                                a["states"], FAKE, None, a["ridx"], None)
+
+
 def exercise(L) -> int:
     """Run every rejection case; raise AssertionError on a wrong status.
     Returns the number of calls made."""
@@ -189,6 +206,10 @@ def exercise(L) -> int:
         n += 1
     for kw, code in DECODE_REJECTS:
         got = decode(L, **kw)
+        assert got == code, (kw, got, code)
+        n += 1
+    for kw, code in DECODE_EX_REJECTS:
+        got = decode_ex(L, **kw)
         assert got == code, (kw, got, code)
         n += 1
     for kw, code in FORWARD_EX_REJECTS:

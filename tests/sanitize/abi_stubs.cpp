@@ -47,4 +47,10 @@ hipError_t launch_decode(const void*, const void*, const void*, const void*, con
     return stub();
 }
 
+hipError_t launch_decode_ex(const void*, const void*, const void*, const void*, const void*,
+                            const void*, const void*, const void*, int, int, int, int, int, int,
+                            int, int, float*, float*, int32_t*, int32_t*, hipStream_t) {
+    return stub();
+}
+
 }  // namespace sse
