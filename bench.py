@@ -130,7 +130,7 @@ def fig6_sweep(args, si, sse, torch):
     from types import SimpleNamespace
     ns = SimpleNamespace(warmup=2, steps=10)
     rows = []
-    for L in (2048, 4096, 8192, 16384, 32768, 65536):
+    for L in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536):
         # one draw per L; the router logits of N partitions are the first N
         # columns of the N = 16 draw (still N(0, 1) and free of ties)
         base = si.forward_inputs(si.Workload(f"fig6_L{L}", "bf16", H=8, c=128, d=128, N=16,

@@ -340,7 +340,11 @@ int sse_rowsparse_forward(const void *q, const void *key_logits, const void *v,
  * inputs), 1 = states of the pieces of long shared chains (+ the key-softmax
  * normalisers for bf16 inputs), 2 = grouping scan and scatter,
  * 3 = routed partitions (store their e-gated reads into the workspace
- * slots), 4 = shared partition (writes o = shared read + slots).
+ * slots), 4 = shared partition (writes o = shared read + slots).  When the
+ * routed segments are cut into pieces (bf16 inputs, fewer (sequence, head,
+ * partition) segments than 256), the grouping runs first and the states of
+ * the routed pieces run with the shared pieces: stage 1 then holds both and
+ * stage 2 is empty.
  * Events of the last 256 calls are kept.  Tracing assumes
  * one device per process.  The first sse_trace_enable(1) creates the HIP
  * events it records into (256 x 6 events, kept until the process ends):

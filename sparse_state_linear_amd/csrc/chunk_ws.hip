@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
 
     // ---------------- which records this block runs ----------------
     int s, h, part, piece = 0, npieces = 1;
-    int64_t lo, n;
+    int64_t lo, n, rslot = 0;
     if constexpr (kPart) {
         // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD
         // b % 8).  Map the N partitions of one (sequence, head) to the same
@@ -161,6 +161,18 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         if constexpr (MODE == kModeRouted) {
             lo = a.seg_offsets[g];
             n = a.seg_offsets[g + 1] - lo;
+            if (a.rpiece_len > 0) {
+                // a long segment runs as pieces of rpiece_len records; the
+                // local state of its piece p is in slot
+                // floor(first record / P) + g + p
+                const int P = a.rpiece_len;
+                npieces = n > 0 ? (int)((n + P - 1) / P) : 1;
+                piece = blockIdx.y;
+                if (piece >= npieces) return;  // uniform
+                rslot = lo / P + g;
+                lo += (int64_t)piece * P;
+                n = min<int64_t>(P, n - (int64_t)piece * P);
+            }
         } else {
             lo = a.cu[s];
             n = a.cu[s + 1] - lo;
@@ -209,16 +221,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void chunk_ws_kernel(const ChunkArgs
         }
         // S_in(p) = D_{p-1} S_in(p-1) + S_loc(p-1), from the piece-state pass,
         // whose piece states are stored fragment-major (the 16 values of
-        // this lane's 32x32 tile (rt, wv) contiguous: 16-byte loads)
+        // this lane's 32x32 tile (rt, wv) contiguous: 16-byte loads); a
+        // routed segment's pieces have their own slots
+        const float* const pS = kPart ? a.ragg_S : a.agg_S;
+        const float* const pD = kPart ? a.ragg_D : a.agg_D;
         for (int p = 0; p < piece; p++) {
-            const int64_t ab = abase + p;
+            const int64_t ab = (kPart ? rslot : abase) + p;
 #pragma unroll
             for (int rt = 0; rt < RT_N; rt++) {
                 const float4* fs = reinterpret_cast<const float4*>(
-                    a.agg_S + (((ab * RT_N + rt) * NS + wv) * kWave + lane) * 16);
+                    pS + (((ab * RT_N + rt) * NS + wv) * kWave + lane) * 16);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&a.agg_D[ab * CK + 32 * rt + 8 * q4 + 4 * hh]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&pD[ab * CK + 32 * rt + 8 * q4 + 4 * hh]);
                     const float4 s4 = fs[q4];
                     S[rt][4 * q4 + 0] = d4.x * S[rt][4 * q4 + 0] + s4.x;
                     S[rt][4 * q4 + 1] = d4.y * S[rt][4 * q4 + 1] + s4.y;
@@ -977,7 +992,9 @@ namespace {
 template <int CK, int DV, int MODE>
 void launch_ws_cfg(const ChunkArgs& a, hipStream_t st) {
     dim3 grid;
-    if (MODE != kModeShared)
+    if (MODE == kModeRouted && a.rpiece_len > 0)
+        grid = dim3((unsigned)(a.num_seqs * a.H * a.N), (unsigned)a.rmax_pieces);
+    else if (MODE != kModeShared)
         grid = dim3((unsigned)(a.num_seqs * a.H * a.N));
     else
         grid = dim3((unsigned)(a.num_seqs * a.H), (unsigned)a.max_pieces);

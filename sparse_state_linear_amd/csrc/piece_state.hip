@@ -31,6 +31,15 @@
 //      accumulates its state tiles.
 // The last piece of a sequence needs no state: its block only computes the
 // normalisers.
+//
+// The same kernel, in its gathered form, gives the piece states of long
+// routed segments (§2.6: each partition's records form a sub-sequence of
+// their own; splitting one into pieces is the same unrolling over its
+// records).  The records come from the grouping's segment records (input
+// row and exponent offset cr = lnz2 - log2 e_i, so that K~ carries the
+// router weight: K~_r = e_r kappa_r exp(R_r)).  The routed pass combines
+// them into each piece's start state, start(p+1) = D(p) start(p) + S_loc(p)
+// with start(0) the segment's initial state.
 #include "chunk_common.h"
 
 namespace sse {
@@ -42,6 +51,7 @@ constexpr int kPsThreads = kPsWaves * kWave;
 constexpr int kPsRec = 16;  // records per step
 constexpr int kDepth = 2;   // steps whose row loads are in flight
 static_assert(kSharedPiece % kPsRec == 0, "pieces must be whole steps");
+static_assert(kMaxRoutedPiece % kPsRec == 0, "pieces must be whole steps");
 
 // Row stride (elements) of an LDS stage row of `cols` bf16 values.  The
 // transpose reads of a half-wave touch 4 records x 64 bytes; a stride of
@@ -67,8 +77,23 @@ __device__ __forceinline__ u16x8 tr_operand(const uint16_t* tile, int col0, int 
     return cat_tr(lds_tr(tile + rec * STRIDE + col), lds_tr(tile + (rec + 4) * STRIDE + col));
 }
 
-template <int CK, int DV>
-__global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs a) {
+// Aggregate slot of piece p of routed segment g (records [off, off + n) of
+// the grouping): floor(off / P) + g + p.  Segments are in record order, so
+// the slots of consecutive segments never overlap and all fit in
+// records / P + segments + 1 slots.
+__device__ __forceinline__ int64_t rpiece_slot(int64_t off, int g, int p, int P) {
+    return off / P + g + p;
+}
+
+// One block's work: shared piece `piece` of (sequence, head) unit `bx`, or
+// (GATHER) full piece `piece` of routed segment `bx`.  LDS comes from the
+// kernel: the two operand stages, and lnz_all (the shared piece's
+// normalisers: kSharedPiece floats) or g_row / g_cr (the routed records'
+// rows and exponent offsets: kMaxRoutedPiece each).
+template <int CK, int DV, bool GATHER>
+__device__ __forceinline__ void piece_body(const ChunkArgs& a, const int bx, const int piece,
+                                           PsStage<CK, DV>* st, float* lnz_all, uint32_t* g_row,
+                                           float* g_cr) {
     constexpr int KS = ps_stride(CK), VS = ps_stride(DV);
     constexpr int RT = CK / 32, CT = DV / 32;         // 32-row / 32-column tiles of the state
     constexpr int WPR = kPsWaves / RT;                // waves sharing one row tile
@@ -76,26 +101,47 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     constexpr int LPR = CK / 8, LPRV = DV / 8;        // lanes per record (16-byte pieces)
     static_assert(RT >= 1 && RT <= kPsWaves && kPsWaves % RT == 0, "unsupported c");
     static_assert(kPsRec * LPR <= kPsThreads && kPsRec * LPRV <= kPsThreads, "unsupported shape");
-    __shared__ __attribute__((aligned(16))) PsStage<CK, DV> st[2];
-    // the piece's normalisers, written to global memory once at the end: a
-    // store inside the step loop would be counted with the loads in flight
-    // (one vector-memory counter), so every step would wait for it
-    __shared__ __attribute__((aligned(16))) float lnz_all[kSharedPiece];
-
+    // (the piece's normalisers are written to global memory once at the
+    // end: a store inside the step loop would be counted with the loads in
+    // flight (one vector-memory counter), so every step would wait for it)
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int H = a.H;
-    const int sh = blockIdx.x, piece = blockIdx.y;
-    const int s = sh / H, h = sh % H;
-    const int64_t t0 = a.cu[s], len = a.cu[s + 1] - t0;
-    const int npieces = len > 0 ? (int)((len + a.piece_len - 1) / a.piece_len) : 1;
-    if (piece >= npieces || len == 0) return;  // uniform
-    const int64_t lo = t0 + (int64_t)piece * a.piece_len;
-    const int n = (int)min<int64_t>(a.piece_len, len - (int64_t)piece * a.piece_len);
-    const bool state = piece < npieces - 1;  // full piece whose state is needed
+    int s = 0, h = 0, n;
+    int64_t lo, slot;
+    bool state;
+    if constexpr (GATHER) {
+        // routed segment g, full piece `piece` of rpiece_len records (the
+        // segment's last piece needs no state)
+        const int g = bx, P = a.rpiece_len;
+        const int64_t off = a.seg_offsets[g], len = a.seg_offsets[g + 1] - off;
+        const int npieces = len > 0 ? (int)((len + P - 1) / P) : 1;
+        if (piece >= npieces - 1) return;  // uniform
+        lo = off + (int64_t)piece * P;
+        n = P;
+        state = true;
+        slot = rpiece_slot(off, g, piece, P);
+        for (int r = tid; r < n; r += kPsThreads) {
+            const SegRec rec = a.seg_rec[lo + r];
+            g_row[r] = rec.row;
+            g_cr[r] = rec.cr;
+        }
+        __syncthreads();
+    } else {
+        const int sh = bx;
+        s = sh / H;
+        h = sh % H;
+        const int64_t t0 = a.cu[s], len = a.cu[s + 1] - t0;
+        const int npieces = len > 0 ? (int)((len + a.piece_len - 1) / a.piece_len) : 1;
+        if (piece >= npieces || len == 0) return;  // uniform
+        lo = t0 + (int64_t)piece * a.piece_len;
+        n = (int)min<int64_t>(a.piece_len, len - (int64_t)piece * a.piece_len);
+        state = piece < npieces - 1;  // full piece whose state is needed
+        slot = ((int64_t)s * H + h) * a.max_pieces + piece;
+    }
     const int nsteps = (n + kPsRec - 1) / kPsRec;
 
-    const uint16_t* __restrict__ gk = static_cast<const uint16_t*>(a.kl);
+    const uint16_t* __restrict__ gk = static_cast<const uint16_t*>(GATHER ? a.kl_r : a.kl);
     const uint16_t* __restrict__ gl = static_cast<const uint16_t*>(a.la);
     const uint16_t* __restrict__ gv = static_cast<const uint16_t*>(a.v);
 
@@ -121,11 +167,13 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
     auto load = [&](auto stI, int i, Raw& R) {
         constexpr bool STATE = decltype(stI)::value;
         const int rk = min(rr, kPsRec - 1), rvv = min(rv, kPsRec - 1);
-        const int64_t row = (lo + clamp_rec(rec_of(i, rk))) * H + h;
+        const int64_t row = GATHER ? (int64_t)g_row[clamp_rec(rec_of(i, rk))]
+                                   : (lo + clamp_rec(rec_of(i, rk))) * H + h;
         R.k = *reinterpret_cast<const uint4*>(gk + row * CK + kc % CK);
         if constexpr (STATE) {
             R.l = *reinterpret_cast<const uint4*>(gl + row * CK + kc % CK);
-            const int64_t rowv = (lo + clamp_rec(rec_of(i, rvv))) * H + h;
+            const int64_t rowv = GATHER ? (int64_t)g_row[clamp_rec(rec_of(i, rvv))]
+                                        : (lo + clamp_rec(rec_of(i, rvv))) * H + h;
             R.v = *reinterpret_cast<const uint4*>(gv + rowv * DV + vc % DV);
         }
     };
@@ -154,7 +202,17 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
         PsStage<CK, DV>& S = st[i & 1];
         // 1. normaliser of this thread's record (max-shifted log-sum-exp over
         //    the LPR lanes of the record), rows into the stage
-        if (krow) {
+        if (GATHER && krow) {
+            // the exponent offset comes with the record.  (The rows are
+            // copied member by member: a whole-struct copy out of the load
+            // ring kept the ring in scratch memory, and every step then
+            // waited for its own prefetch.)
+            if constexpr (STATE) {
+                *reinterpret_cast<uint4*>(&S.kl[rr][kc]) = make_uint4(R.k.x, R.k.y, R.k.z, R.k.w);
+                *reinterpret_cast<uint4*>(&S.la[rr][kc]) = make_uint4(R.l.x, R.l.y, R.l.z, R.l.w);
+                if (kc == 0) S.lnz2[rr] = g_cr[rec_of(i, rr)];
+            }
+        } else if (krow) {
             const uint32_t w4[4] = {R.k.x, R.k.y, R.k.z, R.k.w};
             float x[8];
 #pragma unroll
@@ -244,33 +302,70 @@ __global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs
         for (int p = 0; p < kRing - 1; p++)
             if (i0 + p < nsteps) step(stI, i0 + p, ring[p], ring[(p + kDepth) % kRing]);
     };
-    if (state)
+    if (GATHER || state)
         run(std::true_type{});
-    else
+    else if constexpr (!GATHER)
         run(std::false_type{});
     // ---- the piece's normalisers
-    __syncthreads();
-    for (int r = tid; r < n; r += kPsThreads) a.lnz2_out[(lo + r) * H + h] = lnz_all[r];
+    if constexpr (!GATHER) {
+        __syncthreads();
+        for (int r = tid; r < n; r += kPsThreads) a.lnz2_out[(lo + r) * H + h] = lnz_all[r];
+    }
     if (!state) return;
 
     // ---- the piece's state (fragment-major: tile (rt, ct) of the piece,
     //      lane, its 16 accumulator values) and total decay
-    const int64_t ab = ((int64_t)s * H + h) * a.max_pieces + piece;
+    float* const aS = GATHER ? a.ragg_S : a.agg_S;
+    float* const aD = GATHER ? a.ragg_D : a.agg_D;
 #pragma unroll
     for (int u = 0; u < NT; u++) {
         const int ct = ct0 + WPR * u;
         if (kAllTiles || ct < CT) {
-            float4* fs = reinterpret_cast<float4*>(a.agg_S + (((ab * RT + rt) * CT + ct) * kWave + lane) * 16);
+            float4* fs = reinterpret_cast<float4*>(aS + (((slot * RT + rt) * CT + ct) * kWave + lane) * 16);
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++)
                 fs[q4] = make_float4(acc[u][4 * q4], acc[u][4 * q4 + 1], acc[u][4 * q4 + 2], acc[u][4 * q4 + 3]);
         }
     }
-    if (ct0 == 0 && half == 0) a.agg_D[ab * CK + j] = __builtin_amdgcn_exp2f(carry * kLog2e);
+    if (ct0 == 0 && half == 0) aD[slot * CK + j] = __builtin_amdgcn_exp2f(carry * kLog2e);
+}
+
+// Shared pieces only: grid (S*H, max_pieces).
+template <int CK, int DV>
+__global__ __launch_bounds__(kPsThreads) void piece_state_kernel(const ChunkArgs a) {
+    __shared__ __attribute__((aligned(16))) PsStage<CK, DV> st[2];
+    __shared__ float lnz_all[kSharedPiece];
+    piece_body<CK, DV, false>(a, blockIdx.x, blockIdx.y, st, lnz_all, nullptr, nullptr);
+}
+
+// Shared pieces (blocks [0, S*H*max_pieces)) and the full pieces of routed
+// segments (the rest, G*(rmax_pieces - 1) blocks) in one launch, so the two
+// kinds of blocks fill the chip together.
+template <int CK, int DV>
+__global__ __launch_bounds__(kPsThreads) void piece_state_both_kernel(const ChunkArgs a) {
+    __shared__ __attribute__((aligned(16))) PsStage<CK, DV> st[2];
+    __shared__ uint32_t g_row[kMaxRoutedPiece];
+    __shared__ float g_cr[kMaxRoutedPiece];   // the shared blocks' normalisers
+    static_assert(kMaxRoutedPiece >= kSharedPiece, "normalisers share g_cr");
+    const int SH = a.num_seqs * a.H;
+    const int nsh = SH * a.max_pieces;
+    const int b = blockIdx.x;
+    if (b < nsh) {
+        piece_body<CK, DV, false>(a, b % SH, b / SH, st, g_cr, nullptr, nullptr);
+    } else {
+        const int G = SH * a.N, r = b - nsh;
+        piece_body<CK, DV, true>(a, r % G, r / G, st, nullptr, g_row, g_cr);
+    }
 }
 
 template <int CK, int DV>
 void launch_ps(const ChunkArgs& a, hipStream_t st) {
+    if (a.rpiece_len > 0 && a.rmax_pieces > 1) {
+        const int64_t SH = (int64_t)a.num_seqs * a.H;
+        const int64_t nb = SH * a.max_pieces + SH * a.N * (a.rmax_pieces - 1);
+        piece_state_both_kernel<CK, DV><<<(unsigned)nb, kPsThreads, 0, st>>>(a);
+        return;
+    }
     const dim3 grid((unsigned)(a.num_seqs * a.H), (unsigned)a.max_pieces);
     piece_state_kernel<CK, DV><<<grid, kPsThreads, 0, st>>>(a);
 }

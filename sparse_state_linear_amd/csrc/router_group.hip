@@ -153,8 +153,8 @@ __device__ __forceinline__ void load_row(const float* p, float (&x)[CK]) {
 // and the head-major records rinfo[(h T + t) K + j] = (i | rank << 16, w).
 // With lnz2 given, it also stores lnz2 = log2 of the key-softmax denominator
 // sum_j 2^((kl_j - m) log2 e) plus m log2 e, so that kappa_j =
-// 2^(kl_j log2 e - lnz2); the key normaliser spreads each row over CK/8
-// (bf16) or CK/4 (fp32) lanes.
+// 2^(kl_j log2 e - lnz2), for the rows of its tokens and heads; the key
+// normaliser spreads each row over CK/8 (bf16) or CK/4 (fp32) lanes.
 constexpr int kHG = 4;  // heads per block (one wave per head in the ranking phase)
 template <int NMAX, int CK, typename TIn>
 __global__ __launch_bounds__(256) void route_count_kernel(
@@ -245,8 +245,10 @@ __global__ __launch_bounds__(256) void route_count_kernel(
         }
         __syncthreads();
     }
-    if (lnz2 && blockIdx.z == 0) {  // fp32 inputs: the normalisers of all heads' rows
-        const int64_t r0 = tb * H, r1 = ntok > 0 ? (tb + ntok) * H : r0;  // rows [r0, r1)
+    if (lnz2) {  // the normalisers of this block's rows (its heads' rows of its tokens)
+        const int hgc = H - hgb < kHG ? H - hgb : kHG;
+        const int nrows = ntok * hgc;                // row rl: token rl / hgc, head hgb + rl % hgc
+        auto row_of = [&](int rl) { return (tb + rl / hgc) * H + hgb + rl % hgc; };
         constexpr int VPL = 16 / (int)sizeof(TIn);  // values per lane
         constexpr int LPR = CK / VPL;                // lanes per row
         constexpr int RPW = kWave / LPR;             // rows per wave and pass
@@ -254,18 +256,19 @@ __global__ __launch_bounds__(256) void route_count_kernel(
         // kB passes per batch: all their loads are issued before any of
         // them is reduced, so the batch waits for memory once
         constexpr int kB = 8;
-        const int64_t step = (int64_t)nw * RPW;
-        for (int64_t rb0 = r0 + (int64_t)wv * RPW; rb0 < r1; rb0 += kB * step) {
+        const int step = nw * RPW;
+        for (int rb0 = wv * RPW; rb0 < nrows; rb0 += kB * step) {
         uint4 vb[kB];
 #pragma unroll
         for (int b = 0; b < kB; b++) {
-            const int64_t r = rb0 + b * step + rr;
-            vb[b] = reinterpret_cast<const uint4*>(kl + (r < r1 ? r : r0) * CK)[sub];
+            const int rl = rb0 + b * step + rr;
+            vb[b] = reinterpret_cast<const uint4*>(kl + row_of(rl < nrows ? rl : 0) * CK)[sub];
         }
 #pragma unroll
         for (int b = 0; b < kB; b++) {
-            const int64_t r = rb0 + b * step + rr;
-            const bool ok = r < r1;
+            const int rl = rb0 + b * step + rr;
+            const bool ok = rl < nrows;
+            const int64_t r = row_of(ok ? rl : 0);
             const uint4 v = vb[b];
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
             float x[VPL];

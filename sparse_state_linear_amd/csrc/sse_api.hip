@@ -30,8 +30,9 @@ int check_common(int dtype, int H, int c, int d, int N, int topk) {
 }
 
 struct FwdLayout {
-    size_t idx, w, ridx, rw, counts, seg_off, rinfo, seg_rec, lnz2, lnz2_sh, agg_S, agg_D, trash,
-        part, total;
+    size_t idx, w, ridx, rw, counts, seg_off, rinfo, seg_rec, lnz2, lnz2_sh, agg_S, agg_D, ragg_S,
+        ragg_D, trash, part, total;
+    int rpiece_len, rmax_pieces;
 };
 
 // Piece length of the shared partition's chain (bf16 inputs; the fp32-input
@@ -51,6 +52,28 @@ int shared_piece_len(int64_t S, int H, int max_seqlen) {
 
 int max_pieces(int max_seqlen, int piece_len) {
     return max_seqlen <= 0 ? 1 : (max_seqlen + piece_len - 1) / piece_len;
+}
+
+// Records per piece of a routed segment (bf16 inputs, varlen schedule), or
+// 0 to run every segment in one block.  With fewer (sequence, head,
+// partition) segments than the chip has compute units, one block per
+// segment leaves CUs idle while a few blocks walk long segments, so the
+// segments are cut into pieces when they hold 512 records or more on
+// average (shorter ones cost less than the piece states would): the
+// smallest power of two from 64 records up that gives at most one piece per
+// compute unit and at most 16 pieces per segment, capped at 2048 records.
+// No segment is longer than max_seqlen records (a token enters a partition
+// at most once).
+constexpr int kComputeUnits = 256;
+int routed_piece_len(int64_t T, int S, int max_seqlen, int H, int N, int K) {
+    const int64_t segs = (int64_t)S * H * N;
+    const int64_t recs = T * H * K;
+    if (segs >= kComputeUnits || recs < 512 * segs) return 0;
+    int p = 64;
+    while (p < sse::kMaxRoutedPiece &&
+           (recs / p > kComputeUnits || (max_seqlen + p - 1) / p > sse::kMaxRoutedPieces))
+        p *= 2;
+    return max_seqlen > p ? p : 0;
 }
 
 // Workspace carving.  c, d = 0 sizes the grouping part only; Kr > 0
@@ -86,6 +109,13 @@ bool forward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N
     L.lnz2_sh = off; off += align_up(sizeof(float) * (size_t)(T * H));
     L.agg_S = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c * d));
     L.agg_D = off;   off += align_up(sizeof(float) * (size_t)((int64_t)S * H * maxp * c));
+    // start states of routed pieces: records / P + segments + 1 slots
+    L.rpiece_len = Kr > 0 ? 0 : routed_piece_len(T, S, max_seqlen, H, N, K);
+    L.rmax_pieces = L.rpiece_len > 0 ? max_pieces(max_seqlen, L.rpiece_len) : 1;
+    const int64_t rslots = L.rpiece_len > 0 ? recs / L.rpiece_len + (int64_t)S * H * N + 1 : 0;
+    if (L.rmax_pieces >= 65536) return false;
+    L.ragg_S = off;  off += align_up(sizeof(float) * (size_t)(rslots * c * d));
+    L.ragg_D = off;  off += align_up(sizeof(float) * (size_t)(rslots * c));
     L.trash = off;   off += align_up(sizeof(float) * (size_t)(d > 0 ? 2 * d : 1));
     // fp32 slots: `slots` rows of d floats; bf16 slots: slots + 1 rows of d
     // int16 values, then slots + 1 rows of d/32 fp32 steps
@@ -281,6 +311,12 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     a.topk = kslot;
     a.piece_len = shared_piece_len(num_seqs, H, max_seqlen);
     a.max_pieces = max_pieces(max_seqlen, a.piece_len);
+    const bool rsplit = dtype == SSE_BF16 && !masked && L.rpiece_len > 0;
+    a.kl_r = key_logits;
+    a.rpiece_len = rsplit ? L.rpiece_len : 0;
+    a.rmax_pieces = rsplit ? L.rmax_pieces : 1;
+    a.ragg_S = reinterpret_cast<float*>(ws + L.ragg_S);
+    a.ragg_D = reinterpret_cast<float*>(ws + L.ragg_D);
     // the shared partition's passes: its own query and keys when given
     sse::ChunkArgs ash = a;
     if (opt.q_sh) ash.q = opt.q_sh;
@@ -292,11 +328,12 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     trace_mark(0, s);
     if (!masked) {
         // 1. router + per-block counts (+ the routed keys' normalisers when
-        //    the piece-state pass will not compute them: fp32 inputs, or a
-        //    shared partition with its own keys)
+        //    the piece-state pass will not compute them before the grouping
+        //    needs them: fp32 inputs, a shared partition with its own keys,
+        //    or split routed segments, whose piece states need the grouping)
         e = sse::launch_route_count(router_logits, key_logits, dtype, cu_seqlens, num_seqs,
                                     max_seqlen, total_tokens, H, c, N, topk, idx, w, counts, rinfo,
-                                    (dtype == SSE_F32 || own_keys) ? lnz2 : nullptr, s);
+                                    (dtype == SSE_F32 || own_keys || rsplit) ? lnz2 : nullptr, s);
     } else {
         // 1. routers of the write set and the read set (no grouping), the
         //    routed keys' normalisers when the shared pass has its own keys
@@ -308,21 +345,25 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     }
     if (e != hipSuccess) return SSE_ERR_HIP;
     // 2. piece states of the shared partition and its keys' normalisers
-    //    (bf16 inputs; the fp32-input kernels compute their own)
+    //    (bf16 inputs; the fp32-input kernels compute their own), and, when
+    //    routed segments are split, the states of their pieces in the same
+    //    launch, after the grouping
+    // 3. grouping into (sequence, head, partition) segments
+    auto group = [&]() {
+        e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N,
+                                  topk, counts, seg_off, lnz2, seg_rec, s);
+        if (e == hipSuccess)
+            e = sse::launch_seg_debug(seg_rec, seg_off, total_tokens * H * topk,
+                                      (int64_t)num_seqs * H * N, H, topk, seg_offsets, seg_tok,
+                                      seg_slot, s);
+        return e == hipSuccess;
+    };
     trace_mark(1, s);
+    if (rsplit && !group()) return SSE_ERR_HIP;
     e = sse::launch_chunk_local(ash, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
     trace_mark(2, s);
-    if (!masked) {
-        // 3. grouping into (sequence, head, partition) segments
-        e = sse::launch_group_fwd(rinfo, cu_seqlens, num_seqs, max_seqlen, total_tokens, H, N,
-                                  topk, counts, seg_off, lnz2, seg_rec, s);
-        if (e != hipSuccess) return SSE_ERR_HIP;
-        e = sse::launch_seg_debug(seg_rec, seg_off, total_tokens * H * topk,
-                                  (int64_t)num_seqs * H * N, H, topk, seg_offsets, seg_tok,
-                                  seg_slot, s);
-        if (e != hipSuccess) return SSE_ERR_HIP;
-    }
+    if (!masked && !rsplit && !group()) return SSE_ERR_HIP;
     trace_mark(3, s);
     // 4. routed partitions: e-gated reads into the workspace slots
     e = masked ? sse::launch_chunk_masked(a, dtype, c, d, s)

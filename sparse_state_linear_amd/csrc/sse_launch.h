@@ -101,6 +101,19 @@ struct ChunkArgs {
     int num_seqs, H, N, topk;
     int piece_len;               // records per shared piece
     int max_pieces;
+    // routed segments split into pieces (bf16 inputs, few segments): 0 =
+    // every segment in one block; else records per piece, the most pieces a
+    // segment can have, and the local states of the pieces (fragment-major
+    // like agg_S, one c x d slot per piece but the last) with the piece
+    // decays [slots, c]
+    int rpiece_len;
+    int rmax_pieces;
+    float* ragg_S;
+    float* ragg_D;
+    const void* kl_r;            // the routed keys' logits (the piece states of
+                                 // routed pieces run in the shared pass's
+                                 // piece launch, whose kl may be the shared
+                                 // partition's own keys)
 };
 
 // Passes of the chunked kernels: the shared partition's chain, the routed
@@ -111,13 +124,21 @@ enum { kModeShared = 1, kModeRouted = 2, kModeMasked = 3 };
 
 // Records per shared piece of the bf16 kernels (the longest piece length).
 constexpr int kSharedPiece = 1024;
+// Longest piece of a split routed segment, and the most pieces per segment
+// the piece length aims for (the routed pass combines all earlier pieces'
+// states in its prologue; only sequences past 32K tokens exceed it).
+constexpr int kMaxRoutedPiece = 2048;
+constexpr int kMaxRoutedPieces = 16;
 inline int chunk_piece_len() { return kSharedPiece; }
 
 // bf16 inputs: key-softmax normalisers of every token and the shared
-// partition's piece states (piece_state.hip); fp32 inputs: nothing (the fp64
+// partition's piece states (piece_state.hip), plus, with rpiece_len > 0, the
+// local states and decays of every piece but the last of the split routed
+// segments (then it runs after the grouping); fp32 inputs: nothing (the fp64
 // kernel walks each shared chain in one block and computes its own
 // normalisers).
 hipError_t launch_chunk_local(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
+
 hipError_t launch_piece_state(const ChunkArgs& a, int c, int d, hipStream_t st);
 hipError_t launch_chunk_shared(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
 hipError_t launch_chunk_routed(const ChunkArgs& a, int dtype, int c, int d, hipStream_t st);
