@@ -10,7 +10,8 @@ reported under "decode".
 
 roofline: the dominant kernel is the chunked GLA pass with the longest
 time (the routed pass); its duration comes from HIP events recorded around it
-on the library's stream during the timed steps (sse_trace_*).  Its
+on the library's stream (sse_trace_*) in a second run of the same number of
+steps, after the timed steps (which run without events).  Its
 algorithmic bytes per launch are what the pass itself must move: the routed
 pass reads every token's q, key logits, log decay and v rows once and writes
 the routed partitions' final states (its e-gated reads go to workspace
@@ -104,16 +105,19 @@ def run_forward(args, w, si, sse, torch, inp=None, schedule=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    sse.sse_trace_enable(True)
+    # the timed steps run without stage events (each event in the stream
+    # costs time of its own); a second, traced run gives the stage split
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
         step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    sse.sse_trace_enable(True)
+    for _ in range(args.steps):
+        step()
     stages, calls = sse.sse_trace_read()
     sse.sse_trace_enable(False)
     return T, S, total_ms, {k: v / max(calls, 1) for k, v in stages.items()}, calls
