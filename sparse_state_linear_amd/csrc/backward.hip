@@ -1,5 +1,7 @@
-// backward.hip -- gradients of the SSE forward for gfx950: the chunked
-// reverse pass over every partition segment, and the per-token combine.
+// backward.hip -- gradients of the SSE forward for gfx950: two sequential
+// sweeps per partition segment give the states and state gradients at the
+// chunk boundaries, then every chunk's record gradients run in parallel,
+// then a per-token combine.
 //
 // Method: "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记",
 // §2.3 eqs. (9)-(14) (the same router probability e gates the write and the
@@ -11,34 +13,40 @@
 //
 // The scalar whose gradient is taken is L = <do, o> + <dS_final, S_final>.
 // One segment: records r in time order, gate w_r (= e, or 1 for the shared
-// partition), chunks of C = 16 records.  In a chunk, with b the in-chunk
-// cumulative log decay (per state row), D = diag(e^{b_C}),
+// partition), chunks of C = 32 records.  In a chunk, with b the in-chunk
+// inclusive cumulative log decay (per state row), D = diag(e^{b_C}),
 //   Qt = q e^b,  K0 = kappa e^{-b},  Kh = w K0,  g_r = w_r do_r,
 //   A  = (Qt Kh^T) masked to s <= r,  GV = (g V^T) masked to s <= r,
-//   y  = Qt S_in + A V                 (the read before its gate)
-// and, with G the gradient of the state after the chunk (G~ = D G),
-//   dQt = g S_in^T + GV Kh,   dKh = GV^T Qt + V G~^T,
-//   dV  = A^T g + Kh G~,      dS_in = Qt^T g + G~,
-//   db  = Qt . dQt - Kh . dKh (per record and row), plus, at the chunk's
-//         last record, sum_m S_out . G (the decay of the whole chunk);
-//   dlog_alpha = reverse cumulative sum of db over the chunk's records,
-//   dq = dQt e^b,  dkappa = w e^{-b} dKh,
-//   dw = y . do + K0 . dKh   (the read gate and the write gate).
-// S_in of every chunk comes from a forward sweep of the same block that
-// stores it (checkpoints) before the reverse sweep.  The reverse sweep
-// carries G in MFMA accumulator registers: wave w owns 16-column tiles
-// w, w + 4, ... of the c x d state (all rows), like S_in.  Products that
-// contract over state rows (Qt S_in, Kh G~, Qt^T g) use those registers as
-// the MFMA B operand directly; products that contract over columns (g S_in^T,
-// V G~^T) take them through a per-wave LDS transpose, 16 rows at a time, and
-// the four waves' partial sums are added through LDS.  Every product runs on
-// fp32 16x16x4 MFMA with fp32 operands.
+//   y  = Qt S_in + A V                 (the read before its gate),
+//   S_out = D S_in + Kt^T V,  Kt_r = w_r kappa_r e^{b_C - b_r} (exponents <= 0),
+// and, with G the gradient of the state after the chunk and G~ = D G,
+//   G_in = D G + Qt^T g                (the gradient of the state before it),
+//   dQt = g S_in^T + GV Kh,   dKh = V G~^T + GV^T Qt,   dV = A^T g + Kh G~,
+//   db  = Qt . dQt - Kh . dKh  (per record and row),
+//   t   = sum_m S_out . G = rowsum(S_in . G~) + sum_s Kh_s . (V G~^T)_s
+//         (the decay of the whole chunk, through S_out),
+//   dlog_alpha_r = t + sum_{u >= r in the chunk} db_u,
+//   dq = dQt e^b,  dkey_logits = kappa (dkappa - kappa . dkappa) with
+//   dkappa = w e^{-b} dKh,  dw = y . do + K0 . dKh  (read and write gates).
 //
-// Each record's gradients (dq, dkappa turned into key-logit gradients, dv,
-// dlog_alpha, dw) go to its own slot [token, head, rank] (rank = its place
-// in the token's top-k list, k for the shared partition); the combine kernel
-// sums a token's k + 1 slots and applies the router softmax Jacobian, so no
-// atomics are used and every run gives the same bits.
+// Launch 1 (sweeps): one block per segment and direction.  The forward
+// sweep carries S from the initial state and stores S_in of every chunk;
+// the reverse sweep carries G from dS_final and stores the G of every chunk,
+// and its last G is the gradient of the segment's initial state.  A step is
+// one c x C by C x d product on fp32 MFMA (16x16x4) into the carried state
+// tiles (registers).  The forward sweep also writes every chunk's record
+// list (input row, gradient slot, gate, key normaliser) for launch 2.
+// Launch 2 (chunks): one block per chunk of every segment, reading the S_in
+// and G of its chunk, so all chunks run in parallel; 8 waves, wave w owning
+// the 16-column block w of the d-side outputs (y, dV) and the 16-row block w
+// of the c-side ones (dQt, dKh).  The state operands are read straight from
+// the stored states in the MFMA operand layout (rows, or transposed for the
+// products that contract over d).  Every product runs on fp32 MFMA.
+// Launch 3 (combine): each record's gradients went to its own slot [token,
+// head, rank] (rank = its place in the token's top-k list, k for the shared
+// partition); one block per (token, head) sums the token's k + 1 slots and
+// applies the router softmax Jacobian.  No atomics: every run gives the
+// same bits.
 #include "chunk_common.h"
 
 namespace sse {
@@ -47,500 +55,662 @@ namespace {
 
 typedef float f32x4b __attribute__((ext_vector_type(4)));
 
-constexpr int kBC = 16;          // records per chunk
-constexpr int kBW = 4;           // waves per block
-constexpr int kBThreads = kBW * kWave;
+constexpr int kBC = kBwdChunk;     // records per chunk
+// waves of a sweep block: 8, or one per 16x16 state tile when fewer
+template <int CK, int DV>
+constexpr int sweep_waves() { return (CK / 16) * (DV / 16) < 8 ? (CK / 16) * (DV / 16) : 8; }
+constexpr int kCW = 8;             // waves of a chunk block
+
+// Row stride (floats) of the LDS operand arrays.  MFMA operands are read
+// two ways: lane (l16, g4) reads row l16 and column g4 (A operands), or row
+// g4 and column l16 (B operands).  A stride of 34 modulo 64 banks puts the
+// 32 lanes of each half-wave on distinct banks in both patterns.
+constexpr int lds_stride(int n) { return n + (n % 64 == 0 ? 34 : 2); }
 
 // 16x16x4 fp32 MFMA: lane l supplies A[l%16][l/16] and B[l/16][l%16]; the
 // output gives lane l column l%16 and rows 4 (l/16) + i, i = 0..3.
 __device__ __forceinline__ f32x4b mf(float a, float b, f32x4b c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ int drow(int g4, int i) { return 4 * g4 + i; }
 
-// LDS writes of this wave complete before its next LDS reads are issued
-// (for data exchanged between lanes of one wave).
-__device__ __forceinline__ void wave_lds_sync() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-}
+// One segment of the backward: the shared chain of unit u < S*H, or routed
+// segment g = u - S*H (partition g % N of unit g / N).
+struct Seg {
+    int s, h, part;
+    bool shared;
+    int64_t lo, n;      // first record (token of a shared chain, grouping record
+                        // of a routed segment) and record count
+    int64_t base;       // checkpoint slot of its first chunk
+    int64_t sbase;      // offset of its c x d state in [S, H, N+1, c, d]
+};
 
 template <int CK, int DV>
-struct BwSmem {
-    static constexpr int KS = CK + 1, VS = DV + 1;
-    float qt[kBC][KS];           // Qt
-    float k0[kBC][KS];           // K0 = kappa e^{-b}
-    float bb[kBC][KS];           // b (natural log, in-chunk cumulative)
-    float v[kBC][VS];
-    float g[kBC][VS];            // g = w do
-    float dob[kBC][VS];          // do
-    float a[kBW][kBC][kBC + 1];  // partial A tiles (state-row quarters)
-    float gv[kBW][kBC][kBC + 1]; // partial GV tiles (column quarters)
-    float xp[kBW][16][33];       // per-wave transpose of 16 state rows x 32 columns
-    float red[kBW][kBC][KS];     // per-wave partial of a column contraction
-    float dqt[kBC][KS];
-    float dkh[kBC][KS];
-    float ebc[CK];               // e^{b_C}
-    float dbc[kBW][CK];          // per-wave partial of sum_m S_out . G
-    float dwp[kBW][kBC];         // per-wave partial of y . do
-    float dww[kBC];              // K0 . dKh
-    float lnz[kBC];
-    float w[kBC];
-    uint32_t row[kBC];           // input row t*H + h
-    uint32_t slot[kBC];          // gradient slot row (t*H + h)*(k+1) + rank
-    int valid[kBC];
+__device__ __forceinline__ Seg seg_of(const BwdArgs& a, int u) {
+    Seg q;
+    const int H = a.H, N = a.N, SH = a.num_seqs * H;
+    if (u < SH) {
+        q.s = u / H;
+        q.h = u % H;
+        q.part = N;
+        q.shared = true;
+        const int64_t t0 = a.cu[q.s];
+        q.n = a.cu[q.s + 1] - t0;
+        q.lo = t0;
+        // shared chains numbered in a record space of their own: chain (s, h)
+        // holds records [cu[s] H + h len_s, cu[s] H + (h + 1) len_s)
+        q.base = bwd_slot_base(t0 * H + (int64_t)q.h * q.n, u);
+    } else {
+        const int g = u - SH;
+        q.part = g % N;
+        q.s = g / N / H;
+        q.h = g / N % H;
+        q.shared = false;
+        q.lo = a.seg_offsets[g];
+        q.n = a.seg_offsets[g + 1] - q.lo;
+        q.base = a.sh_slots + bwd_slot_base(q.lo, g);
+    }
+    q.sbase = (((int64_t)q.s * H + q.h) * (N + 1) + q.part) * CK * DV;
+    return q;
+}
+
+// Record r of segment q (r < n): input row t*H + h, gate w, gradient slot row.
+struct Rec {
+    uint32_t row, slot;
+    float w;
+};
+__device__ __forceinline__ Rec rec_of(const BwdArgs& a, const Seg& q, int64_t r) {
+    Rec x;
+    const uint32_t K = (uint32_t)a.topk;
+    if (q.shared) {
+        x.row = (uint32_t)(q.lo + r) * (uint32_t)a.H + (uint32_t)q.h;
+        x.slot = x.row * (K + 1) + K;
+        x.w = 1.f;
+    } else {
+        const SegRec s = a.seg_rec[q.lo + r];
+        x.row = s.row;
+        x.slot = s.row * (K + 1) + s.orow % K;
+        x.w = s.w;
+    }
+    return x;
+}
+
+// 8 consecutive elements of a row, loaded with 16-byte loads.
+template <typename T>
+struct Row8;
+template <>
+struct Row8<bf16_t> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = i < 2 ? u.x : i < 4 ? u.y : i < 6 ? u.z : u.w;
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <>
+struct Row8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ float get(int i) const {
+        const float4& h = i < 4 ? a : b;
+        const int k = i & 3;
+        return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    }
+};
+
+template <int CK, int DV>
+struct SwSmem {
+    static constexpr int KS = lds_stride(CK), VS = lds_stride(DV);
+    float x[kBC][KS];        // A side: Kt (forward) or Qt (reverse)
+    float la[kBC][KS];       // log decay, then its in-chunk sums
+    float y[kBC][VS];        // B side: V (forward) or g = w do (reverse)
+    float ebc[CK];           // e^{b_C}
+    // metadata of three chunks (the current one and the two ahead)
+    float lnz[3][kBC];       // key normalisers (log2)
+    float w[3][kBC];
+    uint32_t row[3][kBC];
+    int valid[3][kBC];
 };
 
 }  // namespace
 
-// Blocks [0, S*H) run the shared partition's chain of (s, h); blocks
-// [S*H, S*H*(N+1)) run routed segment g = block - S*H.
+// Blocks [0, NSEG) run the forward sweep of segment u = block, blocks
+// [NSEG, 2 NSEG) the reverse sweep of segment u = block - NSEG.
 template <int CK, int DV, typename TIn>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_kernel(const BwdArgs a) {
-    using SM = BwSmem<CK, DV>;
-    constexpr int RT = CK / 16;              // 16-row tiles of the state
-    constexpr int NCT = DV / 16;             // 16-column tiles
-    constexpr int CTW = NCT >= kBW ? NCT / kBW : 1;
+__global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_kernel(const BwdArgs a) {
+    using SM = SwSmem<CK, DV>;
+    constexpr int kSW = sweep_waves<CK, DV>();
+    constexpr int CT = DV / 16;
+    constexpr int NTILE = (CK / 16) * CT;
+    constexpr int TPW = NTILE / kSW;               // state tiles per wave
+    static_assert(NTILE % kSW == 0, "every wave owns the same number of tiles");
     __shared__ SM sm;
 
+    const int nseg = a.num_seqs * a.H * (a.N + 1);
+    const bool rev = (int)blockIdx.x >= nseg;
+    const int u = rev ? (int)blockIdx.x - nseg : (int)blockIdx.x;
+    const Seg q = seg_of<CK, DV>(a, u);
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, g4 = lane / 16;
-    const bool owner = wv < NCT;
-    const int H = a.H, N = a.N, K = a.topk;
-    const int SH = a.num_seqs * H;
-
-    // ---------------- which records ----------------
-    const bool shared = (int)blockIdx.x < SH;
-    int s, h, part;
-    int64_t lo, n, cbase;   // first record, count, first checkpoint
-    if (shared) {
-        const int u = blockIdx.x;
-        s = u / H;
-        h = u % H;
-        part = N;
-        lo = a.cu[s];
-        n = a.cu[s + 1] - lo;
-        cbase = ((int64_t)a.cu[s] * H + (int64_t)h * n) / kBC + 2 * (int64_t)u;
-    } else {
-        const int g = blockIdx.x - SH;
-        part = g % N;
-        s = g / N / H;
-        h = g / N % H;
-        lo = a.seg_offsets[g];
-        n = a.seg_offsets[g + 1] - lo;
-        cbase = a.ckpt_shared_chunks + lo / kBC + 2 * (int64_t)g;
-    }
-    const int64_t nchunks = (n + kBC - 1) / kBC;
-    const int64_t sbase = (((int64_t)s * H + h) * (N + 1) + part) * CK * DV;
+    const int64_t nch = (q.n + kBC - 1) / kBC;
     const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
     const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
     const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
     const TIn* __restrict__ gl = static_cast<const TIn*>(a.la);
 
-    // register tiles (rt, ct = wv + 4 u): lane holds rows 16 rt + drow(g4, i)
-    // and column 16 ct + l16
-    auto tile_row = [&](int rt, int i) { return 16 * rt + drow(g4, i); };
-    auto tile_col = [&](int u) { return 16 * (wv + kBW * u) + l16; };
-    auto ckpt = [&](int64_t ci) { return a.ckpt + (cbase + ci) * (int64_t)(CK * DV); };
-    auto store_state = [&](float* dst, const f32x4b (&X)[RT][CTW]) {
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-            for (int u = 0; u < CTW; u++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) dst[tile_row(rt, i) * DV + tile_col(u)] = X[rt][u][i];
-    };
-    auto load_state = [&](const float* src, f32x4b (&X)[RT][CTW]) {
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-            for (int u = 0; u < CTW; u++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) X[rt][u][i] = src[tile_row(rt, i) * DV + tile_col(u)];
-    };
-
-    // ---------------- per-chunk records and rows ----------------
-    auto meta = [&](int64_t c) {
-        if (tid < kBC) {
-            const int64_t idx = c * kBC + tid;
-            const bool valid = idx < n;
-            const int64_t ci = valid ? idx : n - 1;   // a real row for padded records
-            uint32_t row, slot;
-            float w;
-            if (shared) {
-                row = (uint32_t)(lo + ci) * (uint32_t)H + (uint32_t)h;
-                slot = row * (uint32_t)(K + 1) + (uint32_t)K;
-                w = 1.f;
-            } else {
-                const SegRec r = a.seg_rec[lo + ci];
-                row = r.row;
-                slot = row * (uint32_t)(K + 1) + r.orow % (uint32_t)K;
-                w = r.w;
-            }
-            sm.row[tid] = row;
-            sm.slot[tid] = slot;
-            sm.w[tid] = valid ? w : 0.f;
-            sm.valid[tid] = valid;
-        }
-    };
-    // rows into LDS (fp32); padded records: no decay, no key, no gradient
-    auto load_rows = [&](bool with_q) {
-        for (int e = tid; e < kBC * CK; e += kBThreads) {
-            const int r = e / CK, j = e % CK;
-            const int64_t off = (int64_t)sm.row[r] * CK + j;
-            const bool valid = sm.valid[r] != 0;
-            if (with_q) sm.qt[r][j] = to_f32(gq[off]);
-            sm.k0[r][j] = to_f32(gk[off]);
-            sm.bb[r][j] = valid ? to_f32(gl[off]) : 0.f;
-        }
-        for (int e = tid; e < kBC * DV; e += kBThreads) {
-            const int r = e / DV, m = e % DV;
-            const int64_t off = (int64_t)sm.row[r] * DV + m;
-            sm.v[r][m] = to_f32(gv[off]);
-            if (with_q) {
-                const float dov = sm.valid[r] ? a.dout[off] : 0.f;
-                sm.dob[r][m] = dov;
-                sm.g[r][m] = sm.w[r] * dov;
-            }
-        }
-    };
-    // key normalisers (wave wv: records 4 wv .. +3), in-chunk cumulative
-    // decay (thread j: state row j), then K0 (and Qt)
-    auto prep = [&](bool with_q) {
-#pragma unroll
-        for (int rr = 0; rr < kBC / kBW; rr++) {
-            const int r = (kBC / kBW) * wv + rr;
-            float m = -INFINITY;
-            for (int j = lane; j < CK; j += kWave) m = fmaxf(m, sm.k0[r][j]);
-            m = wave_max(m);
-            float z = 0.f;
-            for (int j = lane; j < CK; j += kWave) z += expf(sm.k0[r][j] - m);
-            z = wave_sum(z);
-            if (lane == 0) sm.lnz[r] = m + logf(z);
-        }
-        if (tid < CK) {
-            float b = 0.f;
-#pragma unroll
-            for (int r = 0; r < kBC; r++) {
-                b += sm.bb[r][tid];
-                sm.bb[r][tid] = b;
-            }
-            sm.ebc[tid] = expf(b);
-        }
-        __syncthreads();
-        for (int e = tid; e < kBC * CK; e += kBThreads) {
-            const int r = e / CK, j = e % CK;
-            const float b = sm.bb[r][j];
-            if (with_q) sm.qt[r][j] *= expf(b);
-            sm.k0[r][j] = sm.valid[r] ? expf(sm.k0[r][j] - sm.lnz[r] - b) : 0.f;
-        }
-    };
-
-    // ================= forward sweep: checkpoints S_in of every chunk =================
-    f32x4b S[RT][CTW];
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-        for (int u = 0; u < CTW; u++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                S[rt][u][i] = (owner && a.init) ? a.init[sbase + (int64_t)tile_row(rt, i) * DV + tile_col(u)] : 0.f;
-    for (int64_t c = 0; c < nchunks; c++) {
-        meta(c);
-        __syncthreads();
-        load_rows(false);
-        __syncthreads();
-        prep(false);
-        __syncthreads();
-        if (owner) {
-            store_state(ckpt(c), S);
-            // S = D (S + Kh^T V)
-#pragma unroll
-            for (int u = 0; u < CTW; u++) {
-                const int ct = wv + kBW * u;
-#pragma unroll
-                for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                    for (int ks = 0; ks < kBC / 4; ks++) {
-                        const int rec = 4 * ks + g4;
-                        S[rt][u] = mf(sm.w[rec] * sm.k0[rec][16 * rt + l16], sm.v[rec][16 * ct + l16],
-                                      S[rt][u]);
-                    }
-            }
-#pragma unroll
-            for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const float dd = sm.ebc[tile_row(rt, i)];
-#pragma unroll
-                    for (int u = 0; u < CTW; u++) S[rt][u][i] *= dd;
-                }
-        }
-        __syncthreads();
+    // the slots after this segment's chunks, up to the next segment's first
+    // slot, hold no chunk: the forward sweep marks them (the chunk launch
+    // skips a slot whose first record is marked)
+    if (!rev) {
+        const int64_t next = u + 1 < nseg ? seg_of<CK, DV>(a, u + 1).base : a.nslot;
+        for (int64_t x = q.base + nch + tid; x < next; x += kSW * kWave)
+            a.slot_meta[x * kBC] = BwdRec{0u, kNoSlot, 0.f, 0.f};
     }
-    if (owner) store_state(ckpt(nchunks), S);   // the final state (S_out of the last chunk)
 
-    // ================= reverse sweep =================
-    // G: gradient of the state after the current chunk
-    f32x4b G[RT][CTW];
+    // both directions as one body with the direction fixed at compile time
+    auto sweep = [&](auto revC) {
+        constexpr bool REV = decltype(revC)::value;
+        // state tiles of this wave: tile t = wv + kSW i holds rows
+        // 16 (t / CT) + 4 g4 + e and column 16 (t % CT) + l16
+        f32x4b X[TPW];
+        const float* src0 = REV ? a.dfinal : a.init;
 #pragma unroll
-    for (int rt = 0; rt < RT; rt++)
+        for (int i = 0; i < TPW; i++) {
+            const int t = wv + kSW * i;
 #pragma unroll
-        for (int u = 0; u < CTW; u++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                G[rt][u][i] = (owner && a.dfinal) ? a.dfinal[sbase + (int64_t)tile_row(rt, i) * DV + tile_col(u)] : 0.f;
+            for (int e = 0; e < 4; e++) {
+                float v0 = 0.f;
+                if (src0)
+                    v0 = src0[q.sbase + (int64_t)(16 * (t / CT) + 4 * g4 + e) * DV + 16 * (t % CT) + l16];
+                X[i][e] = v0;
+            }
+        }
 
-    // out[r][j] (partial over this wave's columns) = sum_m X[r][m] Y[j][m],
-    // Y given as the wave's register tiles, X in LDS: per 16-row tile of Y,
-    // the wave writes its 16 x 32 slice to xp and reads it back transposed
-    auto col_contract = [&](const float (*X)[SM::VS], const f32x4b (&Y)[RT][CTW]) {
+        // Pipelined over chunks: the metadata of chunk ci + 2 and the rows of
+        // chunk ci + 1 are loaded while chunk ci is prepared and multiplied.
+        constexpr int NT = kSW * kWave;
+        static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
+        auto order = [&](int64_t ci) { return REV ? nch - 1 - ci : ci; };
+        auto meta = [&](int64_t ci) {
+            if (tid < kBC) {
+                const int p = (int)(ci % 3);
+                const int64_t r = order(ci) * kBC + tid;
+                const bool valid = r < q.n;
+                const Rec x = rec_of(a, q, valid ? r : q.n - 1);
+                const float lz = a.lnz2[x.row];
+                sm.row[p][tid] = x.row;
+                sm.w[p][tid] = valid ? x.w : 0.f;
+                sm.valid[p][tid] = valid;
+                sm.lnz[p][tid] = lz;
+                // the forward sweep also writes the chunk's record list for
+                // the chunk launch
+                if (!REV)
+                    a.slot_meta[(q.base + order(ci)) * kBC + tid] =
+                        BwdRec{x.row, valid ? x.slot : kNoSlot, valid ? x.w : 0.f, lz};
+            }
+        };
+        // this thread's 8-element pieces (key side: record rk, columns jk..;
+        // value side: record rv, columns mv..): forward key logits, log
+        // decay, v; reverse q, log decay, do
+        const int rk = tid / (CK / 8), jk = 8 * (tid % (CK / 8));
+        const int rv = tid / (DV / 8), mv = 8 * (tid % (DV / 8));
+        const bool kpiece = tid < kBC * CK / 8, vpiece = tid < kBC * DV / 8;
+        Row8<TIn> px, pl, pv;
+        Row8<float> pd;
+        auto rows = [&](int64_t ci) {
+            const int p = (int)(ci % 3);
+            if (kpiece) {
+                const int64_t off = (int64_t)sm.row[p][rk] * CK + jk;
+                px.load((REV ? gq : gk) + off);
+                pl.load(gl + off);
+            }
+            if (vpiece) {
+                const int64_t off = (int64_t)sm.row[p][rv] * DV + mv;
+                if constexpr (REV)
+                    pd.load(a.dout + off);
+                else
+                    pv.load(gv + off);
+            }
+        };
+        if (nch > 0) meta(0);
+        if (nch > 1) meta(1);
+        __syncthreads();
+        if (nch > 0) rows(0);
+
+        for (int64_t ci = 0; ci < nch; ci++) {
+            const int64_t c = order(ci);
+            const int p = (int)(ci % 3);
+            __syncthreads();   // the previous chunk's products are done with x, y
+            // padded records: no decay, no key, no output gradient
+            if (kpiece) {
+                const bool ok = sm.valid[p][rk] != 0;
 #pragma unroll
-        for (int jt = 0; jt < RT; jt++) {
-#pragma unroll
-            for (int u = 0; u < CTW; u++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) sm.xp[wv][drow(g4, i)][16 * u + l16] = Y[jt][u][i];
-            wave_lds_sync();
-            f32x4b acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < CTW; u++) {
-                const int ct = wv + kBW * u;
-#pragma unroll
-                for (int kk = 0; kk < 4; kk++) {
-                    const int mloc = 4 * kk + g4;
-                    acc = mf(X[l16][16 * ct + mloc], sm.xp[wv][l16][16 * u + mloc], acc);
+                for (int i = 0; i < 8; i++) {
+                    sm.x[rk][jk + i] = px.get(i);
+                    sm.la[rk][jk + i] = ok ? pl.get(i) : 0.f;
                 }
             }
+            if (vpiece) {
+                const float wr = sm.w[p][rv];
 #pragma unroll
-            for (int i = 0; i < 4; i++) sm.red[wv][drow(g4, i)][16 * jt + l16] = acc[i];
-            wave_lds_sync();
+                for (int i = 0; i < 8; i++) sm.y[rv][mv + i] = REV ? wr * pd.get(i) : pv.get(i);
+            }
+            if (ci + 2 < nch) meta(ci + 2);
+            __syncthreads();
+            if (ci + 1 < nch) rows(ci + 1);
+            // in-chunk sums of the log decay, one state row per thread:
+            // forward the suffix sums b_C - b_r, reverse the inclusive prefix
+            // sums b_r
+            for (int j = tid; j < CK; j += NT) {
+                float run = 0.f;
+                if constexpr (REV) {
+                    for (int r = 0; r < kBC; r++) {
+                        run += sm.la[r][j];
+                        sm.la[r][j] = run;
+                    }
+                } else {
+                    for (int r = kBC - 1; r >= 0; r--) {
+                        const float x = sm.la[r][j];
+                        sm.la[r][j] = run;
+                        run += x;
+                    }
+                }
+                sm.ebc[j] = expf(run);
+            }
+            __syncthreads();
+            for (int e = tid; e < kBC * CK; e += NT) {
+                const int r = e / CK, j = e % CK;
+                const float s = sm.la[r][j];
+                if constexpr (REV)
+                    sm.x[r][j] *= expf(s);
+                else
+                    sm.x[r][j] = sm.valid[p][r] ? sm.w[p][r] * __builtin_amdgcn_exp2f(
+                                                                   (sm.x[r][j] + s) * kLog2e - sm.lnz[p][r])
+                                                : 0.f;
+            }
+            __syncthreads();
+            // store the carried state (S_in of chunk c, or the G after chunk
+            // c), then X = D X + x^T y
+            float* ck = (REV ? a.ckG : a.ckS) + (q.base + c) * (int64_t)(CK * DV);
+#pragma unroll
+            for (int i = 0; i < TPW; i++) {
+                const int t = wv + kSW * i;
+                const int jt = t / CT, mt = t % CT;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int j = 16 * jt + 4 * g4 + e;
+                    ck[(int64_t)j * DV + 16 * mt + l16] = X[i][e];
+                    X[i][e] *= sm.ebc[j];
+                }
+            }
+            // k-steps outermost (not unrolled): each step's operands are read
+            // once for all of the wave's tiles, and few are live at a time
+#pragma unroll 1
+            for (int ks = 0; ks < kBC / 4; ks++) {
+                const int r = 4 * ks + g4;
+#pragma unroll
+                for (int i = 0; i < TPW; i++) {
+                    const int t = wv + kSW * i;
+                    X[i] = mf(sm.x[r][16 * (t / CT) + l16], sm.y[r][16 * (t % CT) + l16], X[i]);
+                }
+            }
+        }
+        // the reverse sweep's last G is the gradient of the initial state
+        if (REV && a.dinit) {
+#pragma unroll
+            for (int i = 0; i < TPW; i++) {
+                const int t = wv + kSW * i;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    a.dinit[q.sbase + (int64_t)(16 * (t / CT) + 4 * g4 + e) * DV + 16 * (t % CT) + l16] =
+                        X[i][e];
+            }
         }
     };
-    // out[r][j] over records: sum_s Mt[r][s] B[s][j] with Mt from the sum of
-    // the four partial tiles P (transposed when `tr`), B[s][j] in LDS scaled
-    // by the record gate when `gate` (Kh = w K0)
-    auto rec_contract = [&](const float (*P)[kBC][kBC + 1], bool tr, const float (*B)[SM::KS],
-                            bool gate, int jt) {
+    if (rev)
+        sweep(std::true_type{});
+    else
+        sweep(std::false_type{});
+}
+
+namespace {
+
+template <int CK, int DV>
+struct ChSmem {
+    static constexpr int KS = lds_stride(CK), VS = lds_stride(DV);
+    float qt[kBC][KS];           // Qt
+    float k0[kBC][KS];           // K0
+    float eb[kBC][KS];           // b, then e^b
+    float v[kBC][VS];
+    float g[kBC][VS];            // g = w do
+    float A[kBC][lds_stride(kBC)];    // A (masked)
+    float GV[kBC][lds_stride(kBC)];   // GV (masked)
+    float ebc[CK];               // e^{b_C}
+    float dwp[kCW][kBC];         // per-wave partials of y . g
+    float kdp[kCW][kBC];         // per-wave partials of K0 . dKh
+    // record lists of the current chunk and the next one
+    float w[2][kBC];
+    float lnz[2][kBC];
+    uint32_t row[2][kBC];
+    uint32_t slot[2][kBC];
+};
+
+}  // namespace
+
+// One block per checkpoint slot (a slot that holds no chunk exits at once):
+// the chunk's state operands are loaded first, so that their latency
+// overlaps the record-side work.
+template <int CK, int DV, typename TIn>
+__global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs a) {
+    using SM = ChSmem<CK, DV>;
+    constexpr int CT = DV / 16, RT = CK / 16;
+    constexpr int NT = kCW * kWave;
+    constexpr int NKC = CK / 4, NKD = DV / 4;
+    static_assert(CT <= kCW && RT <= kCW, "one column and one row block per wave");
+    static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
+    static_assert(DV % 32 == 0, "column quarters of whole 8-column pieces");
+    __shared__ SM sm;
+    const int64_t x = blockIdx.x;
+    if (a.slot_meta[x * kBC].slot == kNoSlot) return;  // uniform: no chunk here
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int l16 = lane % 16, g4 = lane / 16;
+    const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
+    const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
+    const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
+    const TIn* __restrict__ gl = static_cast<const TIn*>(a.la);
+    constexpr int cur = 0;
+
+    // ---- this wave's state operands.  Column block wv of S_in and G~ (the
+    //      products that contract over state rows): lane (l16, g4) takes row
+    //      4 ks + g4, column 16 wv + l16.  Row block wv (the products that
+    //      contract over columns; any order of the columns will do): lane
+    //      (l16, g4) takes row 16 wv + l16 and the columns g4 DV/4 + ks, so
+    //      each lane reads one contiguous quarter row with 16-byte loads.
+    const float* __restrict__ Sin = a.ckS + x * (int64_t)(CK * DV);
+    const float* __restrict__ Gc = a.ckG + x * (int64_t)(CK * DV);
+    float sc[NKC], gc[NKC], sr[NKD], gr[NKD];
+    if (wv < CT) {
+#pragma unroll
+        for (int ks = 0; ks < NKC; ks++) {
+            const int64_t o = (int64_t)(4 * ks + g4) * DV + 16 * wv + l16;
+            sc[ks] = Sin[o];
+            gc[ks] = Gc[o];
+        }
+    }
+    if (wv < RT) {
+        const float4* s4 = reinterpret_cast<const float4*>(Sin + (int64_t)(16 * wv + l16) * DV + g4 * NKD);
+        const float4* g4p = reinterpret_cast<const float4*>(Gc + (int64_t)(16 * wv + l16) * DV + g4 * NKD);
+#pragma unroll
+        for (int i = 0; i < NKD / 4; i++) {
+            const float4 u = s4[i], w4 = g4p[i];
+            sr[4 * i] = u.x; sr[4 * i + 1] = u.y; sr[4 * i + 2] = u.z; sr[4 * i + 3] = u.w;
+            gr[4 * i] = w4.x; gr[4 * i + 1] = w4.y; gr[4 * i + 2] = w4.z; gr[4 * i + 3] = w4.w;
+        }
+    }
+
+    // ---- the chunk's records, then its rows (8-element pieces): Qt, K0 and
+    //      b start as q, key logits and log decay; padded records have no
+    //      decay, key or output gradient
+    if (tid < kBC) {
+        const BwdRec m = a.slot_meta[x * kBC + tid];
+        sm.row[cur][tid] = m.row;
+        sm.slot[cur][tid] = m.slot;
+        sm.w[cur][tid] = m.w;
+        sm.lnz[cur][tid] = m.lnz;
+    }
+    __syncthreads();
+    {
+        const int rk = tid / (CK / 8), jk = 8 * (tid % (CK / 8));
+        const int rv = tid / (DV / 8), mv = 8 * (tid % (DV / 8));
+        if (tid < kBC * CK / 8) {
+            Row8<TIn> pq, pk, pl;
+            const int64_t off = (int64_t)sm.row[cur][rk] * CK + jk;
+            pq.load(gq + off);
+            pk.load(gk + off);
+            pl.load(gl + off);
+            const bool ok = sm.slot[cur][rk] != kNoSlot;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                sm.qt[rk][jk + i] = pq.get(i);
+                sm.k0[rk][jk + i] = pk.get(i);
+                sm.eb[rk][jk + i] = ok ? pl.get(i) : 0.f;
+            }
+        }
+        if (tid < kBC * DV / 8) {
+            Row8<TIn> pv;
+            Row8<float> pd;
+            const int64_t off = (int64_t)sm.row[cur][rv] * DV + mv;
+            pv.load(gv + off);
+            pd.load(a.dout + off);
+            const float wr = sm.w[cur][rv];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                sm.v[rv][mv + i] = pv.get(i);
+                sm.g[rv][mv + i] = wr * pd.get(i);
+            }
+        }
+    }
+    __syncthreads();
+    // inclusive in-chunk cumulative log decay b (one state row per thread)
+    for (int j = tid; j < CK; j += NT) {
+        float run = 0.f;
+        for (int r = 0; r < kBC; r++) {
+            run += sm.eb[r][j];
+            sm.eb[r][j] = run;
+        }
+        sm.ebc[j] = expf(run);
+    }
+    __syncthreads();
+    for (int e = tid; e < kBC * CK; e += NT) {
+        const int r = e / CK, j = e % CK;
+        const float b = sm.eb[r][j];
+        sm.qt[r][j] *= expf(b);
+        sm.k0[r][j] = sm.slot[cur][r] != kNoSlot
+                          ? __builtin_amdgcn_exp2f((sm.k0[r][j] - b) * kLog2e - sm.lnz[cur][r])
+                          : 0.f;
+        sm.eb[r][j] = expf(b);
+    }
+    __syncthreads();
+
+    // ---- A = Qt Kh^T and GV = g V^T masked to s <= r: the 16x16 tiles
+    //      (0,0), (1,0), (1,1) of each, one wave per tile; tile (0,1) is zero
+    if (wv < 6) {
+        const bool isA = wv < 3;
+        const int tt = wv % 3;
+        const int rt = tt == 0 ? 0 : 1, st = tt == 2 ? 1 : 0;
         f32x4b acc = {0.f, 0.f, 0.f, 0.f};
+        if (isA) {
+            for (int ks = 0; ks < CK / 4; ks++) {
+                const int j = 4 * ks + g4;
+                acc = mf(sm.qt[16 * rt + l16][j], sm.w[cur][16 * st + l16] * sm.k0[16 * st + l16][j], acc);
+            }
+        } else {
+            for (int ks = 0; ks < DV / 4; ks++) {
+                const int m = 4 * ks + g4;
+                acc = mf(sm.g[16 * rt + l16][m], sm.v[16 * st + l16][m], acc);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r = 16 * rt + 4 * g4 + e, s = 16 * st + l16;
+            (isA ? sm.A : sm.GV)[r][s] = s <= r ? acc[e] : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) (wv == 6 ? sm.A : sm.GV)[4 * g4 + e][16 + l16] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- d-side outputs of column block wv: y (for y . g) and dV
+    float yg[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (wv < CT) {
+        const int m = 16 * wv + l16;
+        f32x4b y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4b dv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // over state rows: y += Qt S_in, dV += Kh G~
+#pragma unroll
+        for (int ks = 0; ks < NKC; ks++) {
+            const int jj = 4 * ks + g4;
+            const float bs = sc[ks];
+            const float bg = sm.ebc[jj] * gc[ks];
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++) {
+                const int r = 16 * rt + l16;
+                y[rt] = mf(sm.qt[r][jj], bs, y[rt]);
+                dv[rt] = mf(sm.w[cur][r] * sm.k0[r][jj], bg, dv[rt]);
+            }
+        }
+        // over records s: y += A V, dV += A^T g
 #pragma unroll
         for (int ks = 0; ks < kBC / 4; ks++) {
-            const int sidx = 4 * ks + g4;
-            float m = 0.f;
+            const int s = 4 * ks + g4;
 #pragma unroll
-            for (int w2 = 0; w2 < kBW; w2++) m += tr ? P[w2][sidx][l16] : P[w2][l16][sidx];
-            const float bv = B[sidx][16 * jt + l16] * (gate ? sm.w[sidx] : 1.f);
-            acc = mf(m, bv, acc);
-        }
-        return acc;
-    };
-
-    f32x4b Sin[RT][CTW];
-    for (int64_t c = nchunks - 1; c >= 0; c--) {
-        meta(c);
-        __syncthreads();
-        load_rows(true);
-        __syncthreads();
-        prep(true);
-        __syncthreads();
-        // ---- S_in of this chunk; sum_m S_out . G (before G is rescaled) ----
-        if (owner) {
-            load_state(ckpt(c), Sin);
-            const float* so = ckpt(c + 1);
-            float part[RT][4];
-#pragma unroll
-            for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    float x = 0.f;
-#pragma unroll
-                    for (int u = 0; u < CTW; u++)
-                        x += so[tile_row(rt, i) * DV + tile_col(u)] * G[rt][u][i];
-                    part[rt][i] = row_reduce<16>(x, [](float p, float q) { return p + q; });
-                }
-            if (l16 == 0)
-#pragma unroll
-                for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) sm.dbc[wv][tile_row(rt, i)] = part[rt][i];
-            // G~ = D G
-#pragma unroll
-            for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const float dd = sm.ebc[tile_row(rt, i)];
-#pragma unroll
-                    for (int u = 0; u < CTW; u++) G[rt][u][i] *= dd;
-                }
-        } else {
-            for (int j = lane; j < CK; j += kWave) sm.dbc[wv][j] = 0.f;
-        }
-        // ---- partial A (state rows [wv CK/4, (wv+1) CK/4)) and GV (columns
-        //      [wv DV/4, (wv+1) DV/4)), masked to s <= r ----
-        {
-            f32x4b aa = {0.f, 0.f, 0.f, 0.f}, gg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < CK / (4 * kBW); kk++) {
-                const int j = wv * (CK / kBW) + 4 * kk + g4;
-                aa = mf(sm.qt[l16][j], sm.w[l16] * sm.k0[l16][j], aa);
-            }
-#pragma unroll
-            for (int kk = 0; kk < DV / (4 * kBW); kk++) {
-                const int m = wv * (DV / kBW) + 4 * kk + g4;
-                gg = mf(sm.g[l16][m], sm.v[l16][m], gg);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = drow(g4, i);
-                sm.a[wv][r][l16] = l16 <= r ? aa[i] : 0.f;
-                sm.gv[wv][r][l16] = l16 <= r ? gg[i] : 0.f;
+            for (int rt = 0; rt < 2; rt++) {
+                y[rt] = mf(sm.A[16 * rt + l16][s], sm.v[s][m], y[rt]);
+                dv[rt] = mf(sm.A[s][16 * rt + l16], sm.g[s][m], dv[rt]);
             }
         }
-        __syncthreads();
-        // ---- column-owned outputs: y (for y . do) and dV ----
-        if (owner) {
-            float dwpart[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < CTW; u++) {
-                const int ct = wv + kBW * u, col = 16 * ct + l16;
-                f32x4b y = {0.f, 0.f, 0.f, 0.f}, dv = {0.f, 0.f, 0.f, 0.f};
-                // y = Qt S_in + A V;  dV = A^T g + Kh G~
+        for (int rt = 0; rt < 2; rt++)
 #pragma unroll
-                for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int j = tile_row(rt, i);
-                        y = mf(sm.qt[l16][j], Sin[rt][u][i], y);
-                        dv = mf(sm.w[l16] * sm.k0[l16][j], G[rt][u][i], dv);
-                    }
-#pragma unroll
-                for (int ks = 0; ks < kBC / 4; ks++) {
-                    const int sidx = 4 * ks + g4;
-                    float am = 0.f, at = 0.f;
-#pragma unroll
-                    for (int w2 = 0; w2 < kBW; w2++) {
-                        am += sm.a[w2][l16][sidx];   // A[r = l16][s]
-                        at += sm.a[w2][sidx][l16];   // A^T[r = l16][s] = A[s][r]
-                    }
-                    y = mf(am, sm.v[sidx][col], y);
-                    dv = mf(at, sm.g[sidx][col], dv);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int r = drow(g4, i);
-                    dwpart[i] += y[i] * sm.dob[r][col];
-                    if (sm.valid[r]) a.g_dv[(int64_t)sm.slot[r] * DV + col] = dv[i];
-                }
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * rt + 4 * g4 + e;
+                if (sm.slot[cur][r] != kNoSlot) a.g_dv[(int64_t)sm.slot[cur][r] * DV + m] = dv[rt][e];
+                yg[rt][e] = y[rt][e] * sm.g[r][m];
             }
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float x = row_reduce<16>(dwpart[i], [](float p, float q) { return p + q; });
-                if (l16 == 0) sm.dwp[wv][drow(g4, i)] = x;
-            }
-        } else if (lane < kBC) {
-            sm.dwp[wv][lane] = 0.f;
-        }
-        // ---- dQt = g S_in^T (column partials) + GV Kh ----
-        if (owner) col_contract(sm.g, Sin);
-        __syncthreads();
-        for (int jt = wv; jt < RT; jt += kBW) {
-            const f32x4b cpart = rec_contract(sm.gv, false, sm.k0, true, jt);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = drow(g4, i), j = 16 * jt + l16;
-                float x = cpart[i];
-#pragma unroll
-                for (int w2 = 0; w2 < kBW; w2++)
-                    if (w2 < NCT) x += sm.red[w2][r][j];
-                sm.dqt[r][j] = x;
-            }
-        }
-        __syncthreads();
-        // ---- dKh = V G~^T (column partials) + GV^T Qt ----
-        if (owner) col_contract(sm.v, G);
-        __syncthreads();
-        for (int jt = wv; jt < RT; jt += kBW) {
-            const f32x4b cpart = rec_contract(sm.gv, true, sm.qt, false, jt);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = drow(g4, i), j = 16 * jt + l16;
-                float x = cpart[i];
-#pragma unroll
-                for (int w2 = 0; w2 < kBW; w2++)
-                    if (w2 < NCT) x += sm.red[w2][r][j];
-                sm.dkh[r][j] = x;
-            }
-        }
-        // ---- G = G~ + Qt^T g (gradient of S_in: G of the previous chunk) ----
-        if (owner) {
-#pragma unroll
-            for (int u = 0; u < CTW; u++) {
-                const int col = tile_col(u);
-#pragma unroll
-                for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-                    for (int ks = 0; ks < kBC / 4; ks++) {
-                        const int rec = 4 * ks + g4;
-                        G[rt][u] = mf(sm.qt[rec][16 * rt + l16], sm.g[rec][col], G[rt][u]);
-                    }
-            }
-        }
-        __syncthreads();
-        // ---- K0 . dKh per record (wave wv: records 4 wv .. +3) ----
-#pragma unroll
-        for (int rr = 0; rr < kBC / kBW; rr++) {
-            const int r = (kBC / kBW) * wv + rr;
-            float x = 0.f;
-            for (int j = lane; j < CK; j += kWave) x += sm.k0[r][j] * sm.dkh[r][j];
-            x = wave_sum(x);
-            if (lane == 0) sm.dww[r] = x;
-        }
-        __syncthreads();
-        // ---- per record and state row: dq, key-logit gradient, dlog_alpha
-        //      (reverse cumulative sum over the chunk), and dw ----
-        if (tid < CK) {
-            const int j = tid;
-            float dbc = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < kBW; w2++) dbc += sm.dbc[w2][j];
-            float run = dbc;   // the chunk decay acts at its last record
-#pragma unroll
-            for (int r = kBC - 1; r >= 0; r--) {
-                const float b = sm.bb[r][j], w = sm.w[r];
-                const float dqt = sm.dqt[r][j], dkh = sm.dkh[r][j];
-                run += sm.qt[r][j] * dqt - w * sm.k0[r][j] * dkh;
-                if (sm.valid[r]) {
-                    const int64_t o = (int64_t)sm.slot[r] * CK + j;
-                    const float kap = sm.k0[r][j] * expf(b);
-                    // dkappa = w e^{-b} dKh; kappa . dkappa = w (K0 . dKh)
-                    const float dkap = w * expf(-b) * dkh;
-                    a.g_dq[o] = dqt * expf(b);
-                    a.g_dkl[o] = kap * (dkap - w * sm.dww[r]);
-                    a.g_dla[o] = run;
-                }
-            }
-        }
-        if (tid >= CK && tid < CK + kBC) {
-            const int r = tid - CK;
-            if (sm.valid[r]) {
-                float x = sm.dww[r];
-#pragma unroll
-                for (int w2 = 0; w2 < kBW; w2++) x += sm.dwp[w2][r];
-                a.g_dw[sm.slot[r]] = x;
-            }
-        }
-        __syncthreads();
     }
-    // gradient of the segment's initial state
-    if (owner && a.dinit) {
+
+    // ---- c-side outputs of row block wv: dQt, dKh, the chunk decay term,
+    //      dlog_alpha and dq
+    float dkh[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float kd[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int j = 16 * wv + l16;
+    if (wv < RT) {
+        f32x4b dq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4b vg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4b dk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const float ebj = sm.ebc[j];
+        float sg = 0.f;   // this lane's part of rowsum(S_in . G~) of row j
+        // over the columns m = g4 DV/4 + ks: dQt += g S_in^T, V G~^T
 #pragma unroll
-        for (int rt = 0; rt < RT; rt++)
+        for (int ks = 0; ks < NKD; ks++) {
+            const int mm = g4 * NKD + ks;
+            const float st = sr[ks];
+            const float gt = ebj * gr[ks];
+            sg += st * gt;
 #pragma unroll
-            for (int u = 0; u < CTW; u++)
+            for (int rt = 0; rt < 2; rt++) {
+                const int r = 16 * rt + l16;
+                dq[rt] = mf(sm.g[r][mm], st, dq[rt]);
+                vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
+            }
+        }
+        // over records s: dQt += GV Kh, dKh += GV^T Qt
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    a.dinit[sbase + (int64_t)tile_row(rt, i) * DV + tile_col(u)] = G[rt][u][i];
+        for (int ks = 0; ks < kBC / 4; ks++) {
+            const int s = 4 * ks + g4;
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++) {
+                dq[rt] = mf(sm.GV[16 * rt + l16][s], sm.w[cur][s] * sm.k0[s][j], dq[rt]);
+                dk[rt] = mf(sm.GV[s][16 * rt + l16], sm.qt[s][j], dk[rt]);
+            }
+        }
+        // the chunk decay term t of row j: rowsum(S_in . G~) over the four
+        // lane groups, plus sum_s Kh[s][j] (V G~^T)[s][j]
+        float t2 = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int s = 16 * rt + 4 * g4 + e;
+                t2 += sm.w[cur][s] * sm.k0[s][j] * vg[rt][e];
+            }
+        float tj = sg + t2;
+        tj += __shfl_xor(tj, 16, kWave);
+        tj += __shfl_xor(tj, 32, kWave);
+        // db and its reverse cumulative sum over the chunk's records
+        // s = 16 rt + 4 g4 + e: within the lane, then the lane groups above,
+        // then the second row tile into the first
+        float db[2][4], tot[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) {
+            float run = 0.f;
+#pragma unroll
+            for (int e = 3; e >= 0; e--) {
+                const int s = 16 * rt + 4 * g4 + e;
+                dkh[rt][e] = vg[rt][e] + dk[rt][e];
+                run += sm.qt[s][j] * dq[rt][e] - sm.w[cur][s] * sm.k0[s][j] * dkh[rt][e];
+                db[rt][e] = run;
+                kd[rt][e] = sm.k0[s][j] * dkh[rt][e];
+            }
+            tot[rt] = run;
+        }
+        float above[2], all1 = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) {
+            const float T0 = __shfl(tot[rt], l16, kWave);
+            const float T1 = __shfl(tot[rt], l16 + 16, kWave);
+            const float T2 = __shfl(tot[rt], l16 + 32, kWave);
+            const float T3 = __shfl(tot[rt], l16 + 48, kWave);
+            above[rt] = (g4 < 1 ? T1 : 0.f) + (g4 < 2 ? T2 : 0.f) + (g4 < 3 ? T3 : 0.f);
+            if (rt == 1) all1 = T0 + T1 + T2 + T3;
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int s = 16 * rt + 4 * g4 + e;
+                if (sm.slot[cur][s] != kNoSlot) {
+                    const int64_t o = (int64_t)sm.slot[cur][s] * CK + j;
+                    a.g_dla[o] = db[rt][e] + above[rt] + (rt == 0 ? all1 : 0.f) + tj;
+                    a.g_dq[o] = dq[rt][e] * sm.eb[s][j];
+                }
+            }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float x1 = row_reduce<16>(yg[rt][e], [](float p, float o) { return p + o; });
+            const float x2 = row_reduce<16>(kd[rt][e], [](float p, float o) { return p + o; });
+            if (l16 == 0) {
+                sm.dwp[wv][16 * rt + 4 * g4 + e] = x1;
+                sm.kdp[wv][16 * rt + 4 * g4 + e] = x2;
+            }
+        }
+    __syncthreads();
+
+    // ---- key-logit gradients (kappa . dkappa = w K0 . dKh over all rows)
+    //      and the gate gradients
+    if (wv < RT) {
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int s = 16 * rt + 4 * g4 + e;
+                if (sm.slot[cur][s] != kNoSlot) {
+                    float kds = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < kCW; w2++) kds += sm.kdp[w2][s];
+                    a.g_dkl[(int64_t)sm.slot[cur][s] * CK + j] =
+                        sm.w[cur][s] * sm.k0[s][j] * (dkh[rt][e] - sm.eb[s][j] * kds);
+                }
+            }
+    }
+    if (tid < kBC && sm.slot[cur][tid] != kNoSlot) {
+        float yg2 = 0.f, kds = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kCW; w2++) {
+            yg2 += sm.dwp[w2][tid];
+            kds += sm.kdp[w2][tid];
+        }
+        // y . do = (y . g) / w; a gate of zero has no gradient through e
+        const float wr = sm.w[cur][tid];
+        a.g_dw[sm.slot[cur][tid]] = (wr > 0.f ? yg2 / wr : 0.f) + kds;
     }
 }
 
@@ -590,9 +760,10 @@ namespace {
 
 template <int CK, int DV, typename TIn>
 void launch_bwd_cfg(const BwdArgs& a, hipStream_t st) {
-    const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.H * (a.N + 1));
-    if (grid == 0) return;
-    bwd_kernel<CK, DV, TIn><<<grid, kBThreads, 0, st>>>(a);
+    const int64_t nseg = (int64_t)a.num_seqs * a.H * (a.N + 1);
+    if (nseg == 0) return;
+    bwd_sweep_kernel<CK, DV, TIn><<<(unsigned)(2 * nseg), sweep_waves<CK, DV>() * kWave, 0, st>>>(a);
+    if (a.nslot > 0) bwd_chunk_kernel<CK, DV, TIn><<<(unsigned)a.nslot, kCW * kWave, 0, st>>>(a);
 }
 
 template <typename TIn>

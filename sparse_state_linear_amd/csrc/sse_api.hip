@@ -381,20 +381,24 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
 // ---- backward -----------------------------------------------------------------
 struct BwdLayout {
     FwdLayout f;              // routing and grouping part (no slots of its own)
-    size_t ckpt, g_dq, g_dkl, g_dla, g_dv, g_dw, total;
-    int64_t ckpt_shared;
+    size_t ckS, ckG, tab, g_dq, g_dkl, g_dla, g_dv, g_dw, total;
+    int64_t nslot, sh_slots;
 };
 
 bool backward_layout(int64_t T, int S, int max_seqlen, int H, int c, int d, int N, int K,
                      BwdLayout& L) {
     if (!forward_layout(T, S, max_seqlen, H, 0, 0, N, K, L.f)) return false;
     const int64_t SH = (int64_t)S * H;
-    L.ckpt_shared = sse::bwd_ckpt_chunks(T * H, SH);
-    const int64_t chunks = L.ckpt_shared + sse::bwd_ckpt_chunks(T * H * K, SH * N);
+    // chunk slots: shared chains first, then the routed segments
+    L.sh_slots = sse::bwd_slots(T * H, SH);
+    L.nslot = L.sh_slots + sse::bwd_slots(T * H * K, SH * N);
+    if (L.nslot >= INT_MAX || 2 * SH * (N + 1) >= INT_MAX) return false;
     const int64_t slots = T * H * (K + 1);
     if (slots >= INT_MAX) return false;
     size_t off = L.f.part;   // the forward layout's slot area is not used
-    L.ckpt = off;  off += align_up(sizeof(float) * (size_t)chunks * (size_t)c * (size_t)d);
+    L.ckS = off;   off += align_up(sizeof(float) * (size_t)L.nslot * (size_t)c * (size_t)d);
+    L.ckG = off;   off += align_up(sizeof(float) * (size_t)L.nslot * (size_t)c * (size_t)d);
+    L.tab = off;   off += align_up(sizeof(sse::BwdRec) * sse::kBwdChunk * (size_t)L.nslot);
     L.g_dq = off;  off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
     L.g_dkl = off; off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
     L.g_dla = off; off += align_up(sizeof(float) * (size_t)slots * (size_t)c);
@@ -604,11 +608,15 @@ int sse_backward(const void* q, const void* key_logits, const void* v, const voi
     a.seg_offsets = seg_off;
     a.seg_rec = seg_rec;
     a.sel_idx = idx;
+    a.lnz2 = lnz2;
     a.init = initial_states;
     a.dfinal = d_final_states;
     a.dout = d_o;
-    a.ckpt = reinterpret_cast<float*>(ws + L.ckpt);
-    a.ckpt_shared_chunks = L.ckpt_shared;
+    a.ckS = reinterpret_cast<float*>(ws + L.ckS);
+    a.ckG = reinterpret_cast<float*>(ws + L.ckG);
+    a.slot_meta = reinterpret_cast<sse::BwdRec*>(ws + L.tab);
+    a.nslot = L.nslot;
+    a.sh_slots = L.sh_slots;
     a.g_dq = reinterpret_cast<float*>(ws + L.g_dq);
     a.g_dkl = reinterpret_cast<float*>(ws + L.g_dkl);
     a.g_dla = reinterpret_cast<float*>(ws + L.g_dla);

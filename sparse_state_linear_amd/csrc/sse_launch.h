@@ -157,17 +157,29 @@ hipError_t launch_rowsparse_mask(const void* kl, const void* la, int dtype, int6
                                  int k, int identity, void* kl_out, void* la_out, hipStream_t st);
 
 // Arguments of the backward pass (backward.hip).
+// One record of a backward chunk: input row t*H + h, gradient slot row
+// (kNoSlot for padding; on a slot's first record: the slot holds no
+// chunk), gate, key normaliser (log2).
+constexpr uint32_t kNoSlot = 0xffffffffu;
+struct BwdRec {
+    uint32_t row, slot;
+    float w, lnz;
+};
+
 struct BwdArgs {
     const void *q, *kl, *v, *la, *z;
     const int32_t* cu;
     const int32_t* seg_offsets;   // routed segments of the forward's grouping
     const SegRec* seg_rec;
     const int32_t* sel_idx;       // [T, H, topk] the forward's top-k choices
+    const float* lnz2;            // [T, H] key-softmax log2 normalisers
     const float* init;            // [S, H, N+1, c, d] or null
     const float* dfinal;          // gradient of the final states, or null
     const float* dout;            // [T, H, d] gradient of o
-    float* ckpt;                  // chunk-start states: shared chains, then routed segments
-    int64_t ckpt_shared_chunks;   // checkpoints reserved for the shared chains
+    float* ckS;                   // [nslot, c, d] state at the start of each chunk
+    float* ckG;                   // [nslot, c, d] state gradient after each chunk
+    BwdRec* slot_meta;            // [nslot, 32] the records of each slot's chunk
+    int64_t nslot, sh_slots;      // slots in all; slots of the shared chains
     float *g_dq, *g_dkl, *g_dla;  // per-record slots [T*H*(topk+1), c]
     float* g_dv;                  // [T*H*(topk+1), d]
     float* g_dw;                  // [T*H*(topk+1)]
@@ -176,10 +188,16 @@ struct BwdArgs {
     int num_seqs, H, N, topk;
 };
 
-// Checkpoints (chunks of 16 records) the backward reserves: each segment
-// of n records starts at floor(first record / 16) + 2 * (segment index).
-inline int64_t bwd_ckpt_chunks(int64_t records, int64_t segments) {
-    return records / 16 + 2 * segments + 2;
+// Records per chunk of the backward, and the checkpoint slot of the first
+// chunk of segment `idx` whose records start at `first` (segments numbered
+// in record order): floor(first / C) + idx.  Consecutive segments' slots
+// never overlap, and records / C + segments + 1 slots hold them all.
+constexpr int kBwdChunk = 32;
+__host__ __device__ inline int64_t bwd_slot_base(int64_t first, int64_t idx) {
+    return first / kBwdChunk + idx;
+}
+inline int64_t bwd_slots(int64_t records, int64_t segments) {
+    return records / kBwdChunk + segments + 1;
 }
 
 hipError_t launch_backward(const BwdArgs& a, int dtype, int c, int d, hipStream_t st);
