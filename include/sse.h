@@ -280,10 +280,13 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  * logits get a continuous gradient through e = softmax(router_logits); the
  * discrete top-k choice itself carries none) and the key softmax.  The
  * routing and grouping are recomputed from the inputs (the same top-k
- * choice as the forward); the reverse pass runs over the same (sequence,
- * head, partition) segments in reverse chunk order, from chunk-start states
- * a forward sweep stores in the workspace.  Arithmetic in fp32 (fp32 MFMA
- * 16x16x4), whatever the input type.
+ * choice as the forward).  Over the same (sequence, head, partition)
+ * segments, in chunks of 32 records: a forward sweep stores every chunk's
+ * starting state and a reverse sweep every chunk's state gradient in the
+ * workspace, then all chunks' gradients are computed in parallel from them.
+ * Arithmetic in fp32 (fp32 MFMA 16x16x4), whatever the input type; the
+ * chunked factorisation needs the sum of log_alpha over any 32 consecutive
+ * records of one partition to stay above -80, for either input type.
  *   inputs as sse_forward; initial_states [num_seqs, H, N+1, c, d] or NULL
  *   d_o                   [total_tokens, H, d] fp32
  *   d_final_states        [num_seqs, H, N+1, c, d] fp32 or NULL (zeros)
@@ -291,9 +294,10 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  *   dv                    [total_tokens, H, d] fp32 (written)
  *   drouter_logits        [total_tokens, H, N] fp32 (written)
  *   dinitial_states       [num_seqs, H, N+1, c, d] fp32 or NULL
- *   workspace >= sse_backward_workspace_bytes(...) (chunk-start states and
- *   per-record gradient slots: about 4 c d / 16 + 4 (k+1)(3c + d) bytes per
- *   (token, head) plus the forward's grouping arrays).
+ *   workspace >= sse_backward_workspace_bytes(...) (chunk states and state
+ *   gradients, per-record gradient slots: about 8 c d (k+1) / 32 +
+ *   4 (k+1)(3c + d) bytes per (token, head) plus the forward's grouping
+ *   arrays).
  * Deterministic: per-record gradients go to slots summed in a fixed order.
  */
 size_t sse_backward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,

@@ -229,28 +229,41 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
             }
         }
 
-        // Pipelined over chunks: the metadata of chunk ci + 2 and the rows of
-        // chunk ci + 1 are loaded while chunk ci is prepared and multiplied.
+        // Pipelined over chunks: the record list of chunk ci + 3 and the rows
+        // of chunk ci + 1 are loaded while chunk ci is prepared and multiplied.
         constexpr int NT = kSW * kWave;
         static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
         auto order = [&](int64_t ci) { return REV ? nch - 1 - ci : ci; };
-        auto meta = [&](int64_t ci) {
+        // a chunk's record list: loaded into registers one step before it
+        // is written to LDS, so no barrier waits for those loads
+        Rec mx = {0u, 0u, 0.f};
+        float mlz = 0.f;
+        bool mvalid = false;
+        auto meta_load = [&](int64_t ci) {
+            if (tid < kBC) {
+                const int64_t r = order(ci) * kBC + tid;
+                mvalid = r < q.n;
+                mx = rec_of(a, q, mvalid ? r : q.n - 1);
+                mlz = a.lnz2[mx.row];
+            }
+        };
+        auto meta_store = [&](int64_t ci) {
             if (tid < kBC) {
                 const int p = (int)(ci % 3);
-                const int64_t r = order(ci) * kBC + tid;
-                const bool valid = r < q.n;
-                const Rec x = rec_of(a, q, valid ? r : q.n - 1);
-                const float lz = a.lnz2[x.row];
-                sm.row[p][tid] = x.row;
-                sm.w[p][tid] = valid ? x.w : 0.f;
-                sm.valid[p][tid] = valid;
-                sm.lnz[p][tid] = lz;
+                sm.row[p][tid] = mx.row;
+                sm.w[p][tid] = mvalid ? mx.w : 0.f;
+                sm.valid[p][tid] = mvalid;
+                sm.lnz[p][tid] = mlz;
                 // the forward sweep also writes the chunk's record list for
                 // the chunk launch
                 if (!REV)
                     a.slot_meta[(q.base + order(ci)) * kBC + tid] =
-                        BwdRec{x.row, valid ? x.slot : kNoSlot, valid ? x.w : 0.f, lz};
+                        BwdRec{mx.row, mvalid ? mx.slot : kNoSlot, mvalid ? mx.w : 0.f, mlz};
             }
+        };
+        auto meta = [&](int64_t ci) {
+            meta_load(ci);
+            meta_store(ci);
         };
         // this thread's 8-element pieces (key side: record rk, columns jk..;
         // value side: record rv, columns mv..): forward key logits, log
@@ -277,6 +290,7 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
         };
         if (nch > 0) meta(0);
         if (nch > 1) meta(1);
+        if (nch > 2) meta_load(2);
         __syncthreads();
         if (nch > 0) rows(0);
 
@@ -298,9 +312,10 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
 #pragma unroll
                 for (int i = 0; i < 8; i++) sm.y[rv][mv + i] = REV ? wr * pd.get(i) : pv.get(i);
             }
-            if (ci + 2 < nch) meta(ci + 2);
+            if (ci + 2 < nch) meta_store(ci + 2);
             __syncthreads();
             if (ci + 1 < nch) rows(ci + 1);
+            if (ci + 3 < nch) meta_load(ci + 3);
             // in-chunk sums of the log decay, one state row per thread:
             // forward the suffix sums b_C - b_r, reverse the inclusive prefix
             // sums b_r
