@@ -418,6 +418,8 @@ def main():
                     help="also time the forward over L and N in the operator-timing setting (Fig. 6)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--only", choices=("varlen", "decode", "masked", "backward", "rowsparse"),
+                    help="run only this leg (for kernel traces) and print its record")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -433,6 +435,22 @@ def main():
         calib_copy(torch)
         return
     w = si.WORKLOADS["main_bf16"]
+    if args.only:
+        if args.only == "varlen":
+            wv = si.WORKLOADS["varlen_bf16"]
+            Tv, _, v_total_ms, v_stages, _ = run_forward(args, wv, si, sse, torch)
+            rec = {"ms_per_step": v_total_ms / args.steps, "tokens": Tv, "stage_ms": v_stages}
+        elif args.only == "decode":
+            rec = run_decode(args, si, sse, torch)
+        elif args.only == "masked":
+            _, _, m_total_ms, m_stages, _ = run_forward(args, w, si, sse, torch, schedule="masked")
+            rec = {"ms_per_step": m_total_ms / args.steps, "stage_ms": m_stages}
+        elif args.only == "backward":
+            rec = run_backward(args, w, si, sse, torch)
+        else:
+            rec = run_rowsparse(args, si, sse, torch)
+        print(json.dumps({"only": args.only, **rec}), flush=True)
+        return
     log("forward", w.notes)
     T, S, total_ms, stages, calls = run_forward(args, w, si, sse, torch)
     ms = total_ms / args.steps
