@@ -110,3 +110,16 @@ def test_routed_pieces_long_sequence():
     w = si.Workload("rpieces_long", "bf16", H=1, c=64, d=64, N=1, topk=1)
     assert _piece_len(40000, 1, 40000, 1, 1, 1) == 2048
     _check(w, [40000], seed=860)
+
+
+def test_routed_pieces_with_own_shared_query_key():
+    """Split routed segments beside a shared partition with its own query
+    and key logits: the routed pieces' states come from the routed keys in
+    the same launch as the shared pieces', which use the shared keys."""
+    from test_gpu_forward_ex import _check as check_ex
+    w = si.Workload("rpieces_own", "bf16", H=2, c=128, d=128, N=4, topk=2)
+    lengths = [4000, 2600]
+    assert _piece_len(sum(lengths), 2, max(lengths), w.H, w.N, w.topk) == 256
+    rng = np.random.default_rng(870)
+    init = (0.5 * rng.standard_normal((2, w.H, w.N + 1, w.c, w.d))).astype(np.float32)
+    check_ex(w, lengths, "varlen", seed=871, init=init, own_shared=True)
