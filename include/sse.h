@@ -363,6 +363,29 @@ int sse_rowsparse_forward(const void *q, const void *key_logits, const void *v,
 int sse_trace_enable(int enable);
 int sse_trace_read(float *ms_per_stage, int n_stages, int64_t *calls);
 
+/*
+ * Debug mode (a development aid, not part of the method).  It is off unless
+ * the environment variable SSE_DEBUG_CHECKS holds anything but "0" when the
+ * library is first used, or sse_debug_checks(1) switches it on.  While it is
+ * on:
+ *   - every entry point that takes cu_seqlens (sse_forward, sse_forward_ex,
+ *     sse_forward_noalloc, sse_backward, sse_rowsparse_forward,
+ *     sse_group_by_partition) checks, before any launch, the precondition
+ *     the kernels rely on: cu_seqlens[0] == 0, cu_seqlens never decreases,
+ *     cu_seqlens[num_seqs] == total_tokens, and no sequence is longer than
+ *     max_seqlen.  A violation returns SSE_ERR_INVALID_ARG and launches
+ *     nothing.  The check copies cu_seqlens to the host, which synchronises
+ *     the stream.
+ *   - every entry point synchronises its stream before returning, so a
+ *     kernel that failed is reported (SSE_ERR_HIP) by the call that
+ *     launched it.
+ * The synchronisations make debug mode unusable under HIP graph capture.
+ * sse_debug_checks(0) or (1) sets the mode, and any other value only
+ * queries it.  Returns the mode in effect (0 or 1).  Results are the same
+ * bits in either mode.
+ */
+int sse_debug_checks(int mode);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ EXPORTED = ("sse_status_string", "sse_version", "sse_forward_workspace_bytes", "
             "sse_backward_workspace_bytes", "sse_backward",
             "sse_decode_step", "sse_decode_step_ex", "sse_router_topk", "sse_group_workspace_bytes",
             "sse_group_by_partition", "sse_rowsparse_workspace_bytes", "sse_rowsparse_forward",
-            "sse_trace_enable", "sse_trace_read")
+            "sse_trace_enable", "sse_trace_read", "sse_debug_checks")
 
 _lib = None
 
@@ -95,6 +95,8 @@ def lib():
     L.sse_rowsparse_forward.restype = I
     L.sse_trace_enable.argtypes = [I]
     L.sse_trace_enable.restype = I
+    L.sse_debug_checks.argtypes = [I]
+    L.sse_debug_checks.restype = I
     L.sse_trace_read.argtypes = [P, I, P]
     L.sse_trace_read.restype = I
     _lib = L
@@ -463,6 +465,14 @@ def sse_rowsparse_forward(q, key_logits, v, log_alpha, row_topk, cu_seqlens, max
                                      _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "sse_rowsparse_forward")
     return o, final_states
+
+
+def sse_debug_checks(mode=None) -> bool:
+    """Switch the library's debug mode on (True) or off (False), or query it
+    (None): host checks of cu_seqlens before any launch and a stream
+    synchronisation after every call.  Returns the mode in effect."""
+    m = -1 if mode is None else int(bool(mode))
+    return bool(lib().sse_debug_checks(m))
 
 
 TRACE_STAGES = ("route_count", "piece_state", "group", "routed", "shared")

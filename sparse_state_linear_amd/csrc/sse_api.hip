@@ -3,8 +3,12 @@
 // Every check runs before the first HIP call, so invalid arguments are
 // reported without touching a device.
 #include <limits.h>
+#include <stdlib.h>
+#include <string.h>
 
+#include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "sse.h"
 #include "sse_launch.h"
@@ -172,6 +176,48 @@ inline void trace_mark(int mark, hipStream_t s) {
     if (g_trace.on) (void)hipEventRecord(g_trace.ev[g_trace.calls % kTraceCalls][mark], s);
 }
 
+// ---- debug mode: host checks of cu_seqlens, synchronous errors --------------
+// Off unless the environment variable SSE_DEBUG_CHECKS is set to anything
+// but "0" when the library is first used, or sse_debug_checks(1) is called.
+std::atomic<int> g_debug{-1};   // -1: environment not read yet
+
+bool debug_on() {
+    int v = g_debug.load();
+    if (v < 0) {
+        const char* e = getenv("SSE_DEBUG_CHECKS");
+        int want = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+        g_debug.compare_exchange_strong(v, want);
+        v = g_debug.load();
+    }
+    return v == 1;
+}
+
+// The preconditions on cu_seqlens that the kernels rely on: it starts at 0,
+// never decreases, ends at total_tokens, and no sequence is longer than
+// max_seqlen.  Copies the array to the host, which synchronises the stream.
+int debug_check_cu(const int32_t* cu, int num_seqs, int64_t total_tokens, int max_seqlen,
+                   hipStream_t s) {
+    std::vector<int32_t> h((size_t)num_seqs + 1);
+    if (hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return SSE_ERR_HIP;
+    if (h[0] != 0 || (int64_t)h[num_seqs] != total_tokens) return SSE_ERR_INVALID_ARG;
+    for (int i = 0; i < num_seqs; i++) {
+        const int64_t len = (int64_t)h[i + 1] - (int64_t)h[i];
+        if (len < 0 || len > max_seqlen) return SSE_ERR_INVALID_ARG;
+    }
+    return SSE_OK;
+}
+
+// A call's status in debug mode: the stream is synchronised, so a kernel
+// that failed is reported by the call that launched it.
+int debug_finish(int status, void* stream) {
+    if (status != SSE_OK || !debug_on()) return status;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SSE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? SSE_OK : SSE_ERR_HIP;
+}
+
 // ---- no-allocation forward: the workspace in a static device array ----------
 // Callers that cannot allocate device memory (code under graph capture,
 // serving loops, harnesses that forbid hipMalloc) use sse_forward_noalloc,
@@ -259,6 +305,10 @@ int forward_impl(const void* q, const void* key_logits, const void* v, const voi
     if (!ws_ptr || ws_bytes < L.total) return SSE_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        st = debug_check_cu(cu_seqlens, num_seqs, total_tokens, max_seqlen, s);
+        if (st != SSE_OK) return st;
+    }
     char* ws = static_cast<char*>(ws_ptr);
     int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
@@ -439,10 +489,11 @@ int sse_forward(const void* q, const void* key_logits, const void* v, const void
                 const float* initial_states, float* o, float* final_states, int32_t* topk_idx,
                 float* topk_w, int32_t* seg_offsets, int32_t* seg_tok, int32_t* seg_slot,
                 void* workspace, size_t workspace_bytes, void* stream) {
-    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
-                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
-                        final_states, topk_idx, topk_w, seg_offsets, seg_tok, seg_slot, workspace,
-                        workspace_bytes, stream, FwdOpts());
+    const int st = forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens,
+                                num_seqs, max_seqlen, total_tokens, H, c, d, N, topk,
+                                initial_states, o, final_states, topk_idx, topk_w, seg_offsets,
+                                seg_tok, seg_slot, workspace, workspace_bytes, stream, FwdOpts());
+    return debug_finish(st, stream);
 }
 
 size_t sse_forward_ex_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
@@ -471,10 +522,11 @@ int sse_forward_ex(const void* q, const void* key_logits, const void* v, const v
     opt.kr = read_topk;
     opt.schedule = schedule;
     opt.ridx_out = read_topk_idx;
-    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
-                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
-                        final_states, topk_idx, topk_w, seg_offsets, seg_tok, seg_slot, workspace,
-                        workspace_bytes, stream, opt);
+    const int st = forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens,
+                                num_seqs, max_seqlen, total_tokens, H, c, d, N, topk,
+                                initial_states, o, final_states, topk_idx, topk_w, seg_offsets,
+                                seg_tok, seg_slot, workspace, workspace_bytes, stream, opt);
+    return debug_finish(st, stream);
 }
 
 size_t sse_forward_noalloc_max_bytes(void) { return kScratchBytes; }
@@ -485,10 +537,11 @@ int sse_forward_noalloc(const void* q, const void* key_logits, const void* v,
                         int64_t total_tokens, int H, int c, int d, int N, int topk,
                         const float* initial_states, float* o, float* final_states,
                         int32_t* topk_idx, float* topk_w, void* stream) {
-    return forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens, num_seqs,
-                        max_seqlen, total_tokens, H, c, d, N, topk, initial_states, o,
-                        final_states, topk_idx, topk_w, nullptr, nullptr, nullptr, nullptr, 0,
-                        stream, scratch_opts());
+    const int st = forward_impl(q, key_logits, v, log_alpha, router_logits, dtype, cu_seqlens,
+                                num_seqs, max_seqlen, total_tokens, H, c, d, N, topk,
+                                initial_states, o, final_states, topk_idx, topk_w, nullptr,
+                                nullptr, nullptr, nullptr, 0, stream, scratch_opts());
+    return debug_finish(st, stream);
 }
 
 size_t sse_rowsparse_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
@@ -517,6 +570,10 @@ int sse_rowsparse_forward(const void* q, const void* key_logits, const void* v,
     if (total_tokens * H * (c > d ? c : d) >= (int64_t(1) << 30)) return SSE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        st = debug_check_cu(cu_seqlens, num_seqs, total_tokens, max_seqlen, s);
+        if (st != SSE_OK) return st;
+    }
     char* ws = static_cast<char*>(workspace);
     sse::ChunkArgs a = {};
     a.q = q;
@@ -546,10 +603,10 @@ int sse_rowsparse_forward(const void* q, const void* key_logits, const void* v,
                                               row_topk, identity_unselected, ws + L.kl,
                                               ws + L.la, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
-    if (num_seqs == 0) return SSE_OK;
+    if (num_seqs == 0) return debug_finish(SSE_OK, stream);
     e = sse::launch_chunk_local(a, dtype, c, d, s);
     if (e != hipSuccess) return SSE_ERR_HIP;
-    return hip_status(sse::launch_chunk_shared(a, dtype, c, d, s));
+    return debug_finish(hip_status(sse::launch_chunk_shared(a, dtype, c, d, s)), stream);
 }
 
 size_t sse_backward_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H,
@@ -582,6 +639,10 @@ int sse_backward(const void* q, const void* key_logits, const void* v, const voi
         return SSE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total) return SSE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_on()) {
+        st = debug_check_cu(cu_seqlens, num_seqs, total_tokens, max_seqlen, s);
+        if (st != SSE_OK) return st;
+    }
     char* ws = static_cast<char*>(workspace);
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.f.idx);
     float* w = reinterpret_cast<float*>(ws + L.f.w);
@@ -633,7 +694,7 @@ int sse_backward(const void* q, const void* key_logits, const void* v, const voi
     a.H = H;
     a.N = N;
     a.topk = topk;
-    return hip_status(sse::launch_backward(a, dtype, c, d, s));
+    return debug_finish(hip_status(sse::launch_backward(a, dtype, c, d, s)), stream);
 }
 
 int sse_trace_enable(int enable) {
@@ -668,6 +729,14 @@ int sse_trace_read(float* ms_per_stage, int n_stages, int64_t* calls) {
     return SSE_OK;
 }
 
+int sse_debug_checks(int mode) {
+    if (mode == 0 || mode == 1) {
+        debug_on();   // read the environment first, so it cannot override this call later
+        g_debug.store(mode);
+    }
+    return debug_on() ? 1 : 0;
+}
+
 int sse_decode_step(const void* q, const void* key_logits, const void* v, const void* log_alpha,
                     const void* router_logits, int dtype, int B, int H, int c, int d, int N,
                     int topk, float* states, float* o, int32_t* topk_idx, void* stream) {
@@ -679,9 +748,10 @@ int sse_decode_step(const void* q, const void* key_logits, const void* v, const 
     if ((int64_t)B * H * (d / 32) * 256 >= ((int64_t)1 << 32)) return SSE_ERR_UNSUPPORTED;
     if (B > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !states || !o))
         return SSE_ERR_INVALID_ARG;
-    return hip_status(sse::launch_decode(q, key_logits, v, log_alpha, router_logits, dtype, B, H,
-                                         c, d, N, topk, states, o, topk_idx,
-                                         static_cast<hipStream_t>(stream)));
+    const hipError_t e =
+        sse::launch_decode(q, key_logits, v, log_alpha, router_logits, dtype, B, H, c, d, N, topk,
+                           states, o, topk_idx, static_cast<hipStream_t>(stream));
+    return debug_finish(hip_status(e), stream);
 }
 
 int sse_decode_step_ex(const void* q, const void* key_logits, const void* v,
@@ -702,10 +772,11 @@ int sse_decode_step_ex(const void* q, const void* key_logits, const void* v,
     if ((int64_t)B * H * (d / 32) * 256 >= ((int64_t)1 << 32)) return SSE_ERR_UNSUPPORTED;
     if (B > 0 && (!q || !key_logits || !v || !log_alpha || !router_logits || !states || !o))
         return SSE_ERR_INVALID_ARG;
-    return hip_status(sse::launch_decode_ex(
+    const hipError_t e = sse::launch_decode_ex(
         q, key_logits, v, log_alpha, router_logits, q_shared, key_logits_shared,
         read_router_logits, dtype, B, H, c, d, N, topk, read_router_logits ? read_topk : 0, states,
-        o, topk_idx, read_topk_idx, static_cast<hipStream_t>(stream)));
+        o, topk_idx, read_topk_idx, static_cast<hipStream_t>(stream));
+    return debug_finish(hip_status(e), stream);
 }
 
 int sse_router_topk(const void* router_logits, int dtype, int64_t rows, int N, int topk,
@@ -715,8 +786,9 @@ int sse_router_topk(const void* router_logits, int dtype, int64_t rows, int N, i
     if (N > sse::kMaxN || topk > sse::kMaxTopK) return SSE_ERR_UNSUPPORTED;
     if (rows * topk >= INT_MAX) return SSE_ERR_UNSUPPORTED;
     if (rows > 0 && (!router_logits || !topk_idx || !topk_w)) return SSE_ERR_INVALID_ARG;
-    return hip_status(sse::launch_router_rows(router_logits, dtype, rows, N, topk, topk_idx,
-                                              topk_w, static_cast<hipStream_t>(stream)));
+    const hipError_t e = sse::launch_router_rows(router_logits, dtype, rows, N, topk, topk_idx,
+                                                 topk_w, static_cast<hipStream_t>(stream));
+    return debug_finish(hip_status(e), stream);
 }
 
 size_t sse_group_workspace_bytes(int64_t total_tokens, int num_seqs, int max_seqlen, int H, int N,
@@ -744,9 +816,16 @@ int sse_group_by_partition(const int32_t* topk_idx, const float* topk_w,
         return SSE_ERR_UNSUPPORTED;
     const size_t need = L.seg_off - L.counts;
     if (workspace_bytes < need || (need > 0 && !workspace)) return SSE_ERR_WORKSPACE;
-    return hip_status(sse::launch_group(topk_idx, topk_w, cu_seqlens, num_seqs, max_seqlen, H, N,
-                                        topk, static_cast<int32_t*>(workspace), seg_offsets,
-                                        seg_tok, seg_slot, seg_w, static_cast<hipStream_t>(stream)));
+    if (debug_on()) {
+        const int st = debug_check_cu(cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                      static_cast<hipStream_t>(stream));
+        if (st != SSE_OK) return st;
+    }
+    const hipError_t e = sse::launch_group(topk_idx, topk_w, cu_seqlens, num_seqs, max_seqlen, H,
+                                           N, topk, static_cast<int32_t*>(workspace), seg_offsets,
+                                           seg_tok, seg_slot, seg_w,
+                                           static_cast<hipStream_t>(stream));
+    return debug_finish(hip_status(e), stream);
 }
 
 }  // extern "C"

@@ -4,6 +4,8 @@ launch (every call below returns before its first HIP call)."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest  # noqa: F401
 
@@ -50,6 +52,25 @@ def test_host_checks_reject_bad_arguments():
     battery runs under the sanitizers in test_sanitize.py)."""
     import abi_calls
     assert abi_calls.exercise(sse.lib()) > 40
+
+
+def test_debug_mode_switch():
+    """The debug-mode switch touches no device: set, query and restore it in
+    this process; the environment variable sets the mode of a fresh one."""
+    before = sse.sse_debug_checks()
+    try:
+        assert sse.sse_debug_checks(True) is True
+        assert sse.sse_debug_checks() is True
+        assert sse.sse_debug_checks(False) is False
+        assert sse.sse_debug_checks() is False
+    finally:
+        sse.sse_debug_checks(before)
+    code = "import sparse_state_linear_amd as s; print(int(s.sse_debug_checks()))"
+    for val, want in (("1", "1"), ("0", "0"), ("", "0")):
+        env = dict(os.environ, SSE_DEBUG_CHECKS=val, PYTHONPATH=ROOT)
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                             text=True, check=True, timeout=300)
+        assert out.stdout.strip().splitlines()[-1] == want
 
 
 def test_product_path_does_not_touch_the_oracle():
