@@ -167,6 +167,7 @@ struct SwSmem {
     float la[kBC][KS];       // log decay, then its in-chunk sums
     float y[kBC][VS];        // B side: V (forward) or g = w do (reverse)
     float ebc[CK];           // e^{b_C}
+    float btot[sweep_waves<CK, DV>() * kWave / CK][CK];   // per record group: its log decay total
     // metadata of three chunks (the current one and the two ahead)
     float lnz[3][kBC];       // key normalisers (log2)
     float w[3][kBC];
@@ -316,35 +317,50 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
             __syncthreads();
             if (ci + 1 < nch) rows(ci + 1);
             if (ci + 3 < nch) meta_load(ci + 3);
-            // in-chunk sums of the log decay, one state row per thread:
-            // forward the suffix sums b_C - b_r, reverse the inclusive prefix
-            // sums b_r
-            for (int j = tid; j < CK; j += NT) {
+            // in-chunk sums of the log decay: forward the suffix sums
+            // b_C - b_r, reverse the inclusive prefix sums b_r.  Thread
+            // (group, state row j) sums the BG records of its group in
+            // registers, adds the totals of the groups before it (reverse) or
+            // after it (forward), and forms its records' operand values.
+            {
+                constexpr int NG = NT / CK, BG = kBC / NG;
+                static_assert(NT % CK == 0 && kBC % NG == 0, "record groups of whole rows");
+                const int jb = tid % CK, grp = tid / CK, r0 = grp * BG;
+                float sl[BG];
                 float run = 0.f;
                 if constexpr (REV) {
-                    for (int r = 0; r < kBC; r++) {
-                        run += sm.la[r][j];
-                        sm.la[r][j] = run;
+#pragma unroll
+                    for (int i = 0; i < BG; i++) {
+                        run += sm.la[r0 + i][jb];
+                        sl[i] = run;
                     }
                 } else {
-                    for (int r = kBC - 1; r >= 0; r--) {
-                        const float x = sm.la[r][j];
-                        sm.la[r][j] = run;
-                        run += x;
+#pragma unroll
+                    for (int i = BG - 1; i >= 0; i--) {
+                        sl[i] = run;
+                        run += sm.la[r0 + i][jb];
                     }
                 }
-                sm.ebc[j] = expf(run);
-            }
-            __syncthreads();
-            for (int e = tid; e < kBC * CK; e += NT) {
-                const int r = e / CK, j = e % CK;
-                const float s = sm.la[r][j];
-                if constexpr (REV)
-                    sm.x[r][j] *= expf(s);
-                else
-                    sm.x[r][j] = sm.valid[p][r] ? sm.w[p][r] * __builtin_amdgcn_exp2f(
-                                                                   (sm.x[r][j] + s) * kLog2e - sm.lnz[p][r])
-                                                : 0.f;
+                sm.btot[grp][jb] = run;
+                __syncthreads();
+                float other = 0.f;
+                if constexpr (REV) {
+                    for (int g2 = 0; g2 < grp; g2++) other += sm.btot[g2][jb];
+                } else {
+                    for (int g2 = grp + 1; g2 < NG; g2++) other += sm.btot[g2][jb];
+                }
+                if (grp == (REV ? NG - 1 : 0)) sm.ebc[jb] = expf(other + run);
+#pragma unroll
+                for (int i = 0; i < BG; i++) {
+                    const int r = r0 + i;
+                    const float sv = other + sl[i];
+                    if constexpr (REV)
+                        sm.x[r][jb] *= expf(sv);
+                    else
+                        sm.x[r][jb] = sm.valid[p][r] ? sm.w[p][r] * __builtin_amdgcn_exp2f(
+                                                                        (sm.x[r][jb] + sv) * kLog2e - sm.lnz[p][r])
+                                                     : 0.f;
+                }
             }
             __syncthreads();
             // store the carried state (S_in of chunk c, or the G after chunk
@@ -404,6 +420,7 @@ struct ChSmem {
     float A[kBC][lds_stride(kBC)];    // A (masked)
     float GV[kBC][lds_stride(kBC)];   // GV (masked)
     float ebc[CK];               // e^{b_C}
+    float btot[kCW * kWave / CK][CK];   // per record group: its total of the log decay
     float dwp[kCW][kBC];         // per-wave partials of y . g
     float kdp[kCW][kBC];         // per-wave partials of K0 . dKh
     // record lists of the current chunk and the next one
@@ -510,24 +527,37 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         }
     }
     __syncthreads();
-    // inclusive in-chunk cumulative log decay b (one state row per thread)
-    for (int j = tid; j < CK; j += NT) {
+    // inclusive in-chunk cumulative log decay b: thread (group, state row j)
+    // scans the BG records of its group in registers, then adds the totals
+    // of the groups before it; the same thread forms Qt, K0 and e^b of its
+    // records
+    {
+        constexpr int NG = NT / CK, BG = kBC / NG;
+        static_assert(NT % CK == 0 && kBC % NG == 0, "record groups of whole rows");
+        const int jb = tid % CK, grp = tid / CK, r0 = grp * BG;
+        float bl[BG];
         float run = 0.f;
-        for (int r = 0; r < kBC; r++) {
-            run += sm.eb[r][j];
-            sm.eb[r][j] = run;
+#pragma unroll
+        for (int i = 0; i < BG; i++) {
+            run += sm.eb[r0 + i][jb];
+            bl[i] = run;
         }
-        sm.ebc[j] = expf(run);
-    }
-    __syncthreads();
-    for (int e = tid; e < kBC * CK; e += NT) {
-        const int r = e / CK, j = e % CK;
-        const float b = sm.eb[r][j];
-        sm.qt[r][j] *= expf(b);
-        sm.k0[r][j] = sm.slot[cur][r] != kNoSlot
-                          ? __builtin_amdgcn_exp2f((sm.k0[r][j] - b) * kLog2e - sm.lnz[cur][r])
-                          : 0.f;
-        sm.eb[r][j] = expf(b);
+        sm.btot[grp][jb] = run;
+        __syncthreads();
+        float pre = 0.f;
+        for (int g2 = 0; g2 < grp; g2++) pre += sm.btot[g2][jb];
+        if (grp == NG - 1) sm.ebc[jb] = expf(pre + run);
+#pragma unroll
+        for (int i = 0; i < BG; i++) {
+            const int r = r0 + i;
+            const float b = pre + bl[i];
+            const float e = expf(b);
+            sm.qt[r][jb] *= e;
+            sm.k0[r][jb] = sm.slot[cur][r] != kNoSlot
+                               ? __builtin_amdgcn_exp2f((sm.k0[r][jb] - b) * kLog2e - sm.lnz[cur][r])
+                               : 0.f;
+            sm.eb[r][jb] = e;
+        }
     }
     __syncthreads();
 
@@ -731,44 +761,47 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 
 // Per (token, head): sum the k + 1 slots of every gradient; the router
 // logits' gradient through e = softmax(z): dz = e * (de - e . de) with de
-// the gate gradients of the k chosen partitions (zero elsewhere).
+// the gate gradients of the k chosen partitions (zero elsewhere).  One wave
+// per (token, head), kCbRows per block: the wave walks the row's 16-byte
+// pieces of dq, dkey_logits, dlog_alpha (c each) and dv (d), each the sum of
+// its k + 1 slots in slot order, then computes the router part.
+constexpr int kCbRows = 4;
 template <typename TIn>
-__global__ __launch_bounds__(256) void bwd_combine_kernel(const BwdArgs a, int c, int d,
-                                                         int64_t rows) {
-    const int64_t row = (int64_t)blockIdx.x;   // one block per (token, head)
-    if (row >= rows) return;
+__global__ __launch_bounds__(kCbRows * kWave) void bwd_combine_kernel(const BwdArgs a, int c, int d,
+                                                                     int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * kCbRows + threadIdx.x / kWave;
+    if (row >= rows) return;   // wave-uniform
+    const int lane = threadIdx.x % kWave;
     const int K = a.topk, N = a.N, P = K + 1;
     const int64_t sb = row * P;
-    for (int j = threadIdx.x; j < c; j += blockDim.x) {
-        float q = 0.f, k = 0.f, l = 0.f;
+    const int c4 = c / 4, items = 3 * c4 + d / 4;
+    for (int it = lane; it < items; it += kWave) {
+        const int arr = it < 3 * c4 ? it / c4 : 3;   // 0 dq, 1 dkl, 2 dla, 3 dv
+        const int e4 = arr < 3 ? it - arr * c4 : it - 3 * c4;
+        const int n = arr < 3 ? c : d;
+        const float* src = arr == 0 ? a.g_dq : arr == 1 ? a.g_dkl : arr == 2 ? a.g_dla : a.g_dv;
+        float* dst = arr == 0 ? a.dq : arr == 1 ? a.dkl : arr == 2 ? a.dla : a.dv;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int p = 0; p < P; p++) {
-            q += a.g_dq[(sb + p) * c + j];
-            k += a.g_dkl[(sb + p) * c + j];
-            l += a.g_dla[(sb + p) * c + j];
+            const float4 x = *reinterpret_cast<const float4*>(src + (sb + p) * n + 4 * e4);
+            acc.x += x.x;
+            acc.y += x.y;
+            acc.z += x.z;
+            acc.w += x.w;
         }
-        a.dq[row * c + j] = q;
-        a.dkl[row * c + j] = k;
-        a.dla[row * c + j] = l;
+        *reinterpret_cast<float4*>(dst + row * n + 4 * e4) = acc;
     }
-    for (int m = threadIdx.x; m < d; m += blockDim.x) {
-        float x = 0.f;
-        for (int p = 0; p < P; p++) x += a.g_dv[(sb + p) * d + m];
-        a.dv[row * d + m] = x;
-    }
-    if (threadIdx.x < kWave) {
-        // router softmax over N (one wave; N <= 64)
-        const int lane = threadIdx.x;
-        const TIn* z = static_cast<const TIn*>(a.z);
-        const float zi = lane < N ? to_f32(z[row * N + lane]) : -INFINITY;
-        const float zm = wave_max(zi);
-        const float ex = lane < N ? expf(zi - zm) : 0.f;
-        const float e = ex / wave_sum(ex);
-        float de = 0.f;
-        for (int p = 0; p < K; p++)
-            if (a.sel_idx[row * K + p] == lane) de = a.g_dw[sb + p];
-        const float ede = wave_sum(e * de);
-        if (lane < N) a.dz[row * N + lane] = e * (de - ede);
-    }
+    // router softmax over N (N <= 64)
+    const TIn* z = static_cast<const TIn*>(a.z);
+    const float zi = lane < N ? to_f32(z[row * N + lane]) : -INFINITY;
+    const float zm = wave_max(zi);
+    const float ex = lane < N ? expf(zi - zm) : 0.f;
+    const float e = ex / wave_sum(ex);
+    float de = 0.f;
+    for (int p = 0; p < K; p++)
+        if (a.sel_idx[row * K + p] == lane) de = a.g_dw[sb + p];
+    const float ede = wave_sum(e * de);
+    if (lane < N) a.dz[row * N + lane] = e * (de - ede);
 }
 
 namespace {
@@ -805,10 +838,11 @@ hipError_t launch_backward(const BwdArgs& a, int dtype, int c, int d, hipStream_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.rows == 0) return hipSuccess;
+    const unsigned nb = (unsigned)((a.rows + kCbRows - 1) / kCbRows);
     if (dtype == kF32)
-        bwd_combine_kernel<float><<<(unsigned)a.rows, 256, 0, st>>>(a, c, d, a.rows);
+        bwd_combine_kernel<float><<<nb, kCbRows * kWave, 0, st>>>(a, c, d, a.rows);
     else
-        bwd_combine_kernel<bf16_t><<<(unsigned)a.rows, 256, 0, st>>>(a, c, d, a.rows);
+        bwd_combine_kernel<bf16_t><<<nb, kCbRows * kWave, 0, st>>>(a, c, d, a.rows);
     return hipGetLastError();
 }
 
