@@ -47,6 +47,8 @@
 // partition); one block per (token, head) sums the token's k + 1 slots and
 // applies the router softmax Jacobian.  No atomics: every run gives the
 // same bits.
+#include <type_traits>
+
 #include "chunk_common.h"
 
 namespace sse {
@@ -66,6 +68,8 @@ constexpr int kCW = 8;             // waves of a chunk block
 // g4 and column l16 (B operands).  A stride of 34 modulo 64 banks puts the
 // 32 lanes of each half-wave on distinct banks in both patterns.
 constexpr int lds_stride(int n) { return n + (n % 64 == 0 ? 34 : 2); }
+static_assert(lds_stride(32) % 2 == 0 && lds_stride(64) % 2 == 0 && lds_stride(128) % 2 == 0,
+              "even row strides: every row of an LDS operand array is 8-byte aligned");
 
 // 16x16x4 fp32 MFMA: lane l supplies A[l%16][l/16] and B[l/16][l%16]; the
 // output gives lane l column l%16 and rows 4 (l/16) + i, i = 0..3.
@@ -641,6 +645,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         const float ebj = sm.ebc[j];
         float sg = 0.f;   // this lane's part of rowsum(S_in . G~) of row j
         // over the columns m = g4 DV/4 + ks: dQt += g S_in^T, V G~^T
+        constexpr bool kVgBf16 = std::is_same<TIn, bf16_t>::value;
 #pragma unroll
         for (int ks = 0; ks < NKD; ks++) {
             const int mm = g4 * NKD + ks;
@@ -651,7 +656,33 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             for (int rt = 0; rt < 2; rt++) {
                 const int r = 16 * rt + l16;
                 dq[rt] = mf(sm.g[r][mm], st, dq[rt]);
-                vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
+                if constexpr (!kVgBf16) vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
+            }
+        }
+        if constexpr (kVgBf16) {
+            // V is exact in bf16 (bf16 inputs): V G~^T on bf16 MFMA with G~
+            // in two bf16 terms.  k-step t of lane group g4 contracts the
+            // columns g4 DV/4 + 8 t + i (i < 8): the lane's own 8 consecutive
+            // G~ values, and 8 consecutive V values of its record's row.
+#pragma unroll
+            for (int t = 0; t < NKD / 8; t++) {
+                uint32_t pr[4][2];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++)
+                    split_pair<2>(ebj * gr[8 * t + 2 * e2], ebj * gr[8 * t + 2 * e2 + 1], pr[e2]);
+                const u16x8 ghi = __builtin_bit_cast(u16x8, make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]));
+                const u16x8 glo = __builtin_bit_cast(u16x8, make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]));
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    // 8-byte LDS reads: the row stride keeps every row 8-byte aligned
+                    const float2* vr = reinterpret_cast<const float2*>(&sm.v[16 * rt + l16][g4 * NKD + 8 * t]);
+                    const float2 v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3];
+                    const u16x8 va = __builtin_bit_cast(
+                        u16x8, make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v1.x, v1.y),
+                                          pack_bf16x2(v2.x, v2.y), pack_bf16x2(v3.x, v3.y)));
+                    vg[rt] = mfma16(va, ghi, vg[rt]);
+                    vg[rt] = mfma16(va, glo, vg[rt]);
+                }
             }
         }
         // over records s: dQt += GV Kh, dKh += GV^T Qt
