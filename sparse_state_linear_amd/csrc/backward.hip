@@ -33,18 +33,23 @@
 // sweep carries S from the initial state and stores S_in of every chunk;
 // the reverse sweep carries G from dS_final and stores the G of every chunk,
 // and its last G is the gradient of the segment's initial state.  A step is
-// one c x C by C x d product on fp32 MFMA (16x16x4) into the carried state
-// tiles (registers).  The forward sweep also writes every chunk's record
-// list (input row, gradient slot, gate, key normaliser) for launch 2.
+// one c x C by C x d product into the carried state tiles (registers), on
+// fp32 MFMA (16x16x4) for fp32 inputs and on bf16 MFMA for bf16 inputs (the
+// chunk's 32 records as one k-step; the A side in two bf16 terms, the B side
+// V, exact in bf16, or g in two terms).  The forward sweep also writes
+// every chunk's record list (input row, gradient slot, gate, key
+// normaliser) for launch 2.
 // Launch 2 (chunks): one block per chunk of every segment, reading the S_in
 // and G of its chunk, so all chunks run in parallel; 8 waves, wave w owning
 // the 16-column block w of the d-side outputs (y, dV) and the 16-row block w
 // of the c-side ones (dQt, dKh).  The state operands are read straight from
 // the stored states in the MFMA operand layout (rows, or transposed for the
-// products that contract over d).  Every product runs on fp32 MFMA.
+// products that contract over d).  The products run on fp32 MFMA, except
+// V G~^T with bf16 inputs: V is exact in bf16 there, so it runs on bf16
+// MFMA with G~ in two bf16 terms.
 // Launch 3 (combine): each record's gradients went to its own slot [token,
 // head, rank] (rank = its place in the token's top-k list, k for the shared
-// partition); one block per (token, head) sums the token's k + 1 slots and
+// partition); one wave per (token, head) sums the token's k + 1 slots and
 // applies the router softmax Jacobian.  No atomics: every run gives the
 // same bits.
 #include <type_traits>
@@ -172,6 +177,11 @@ struct SwSmem {
     float y[kBC][VS];        // B side: V (forward) or g = w do (reverse)
     float ebc[CK];           // e^{b_C}
     float btot[sweep_waves<CK, DV>() * kWave / CK][CK];   // per record group: its log decay total
+    // bf16 inputs: the A side transposed [state row][record] in two bf16
+    // terms (rows of 80 bytes: 16-byte aligned operand reads, and the 16
+    // rows one read touches fall on distinct banks)
+    uint16_t xh[CK][kBC + 8];
+    uint16_t xl[CK][kBC + 8];
     // metadata of three chunks (the current one and the two ahead)
     float lnz[3][kBC];       // key normalisers (log2)
     float w[3][kBC];
@@ -191,6 +201,7 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
     constexpr int NTILE = (CK / 16) * CT;
     constexpr int TPW = NTILE / kSW;               // state tiles per wave
     static_assert(NTILE % kSW == 0, "every wave owns the same number of tiles");
+    constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for the products
     __shared__ SM sm;
 
     const int nseg = a.num_seqs * a.H * (a.N + 1);
@@ -354,16 +365,30 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                     for (int g2 = grp + 1; g2 < NG; g2++) other += sm.btot[g2][jb];
                 }
                 if (grp == (REV ? NG - 1 : 0)) sm.ebc[jb] = expf(other + run);
+                float xv[BG];
 #pragma unroll
                 for (int i = 0; i < BG; i++) {
                     const int r = r0 + i;
                     const float sv = other + sl[i];
                     if constexpr (REV)
-                        sm.x[r][jb] *= expf(sv);
+                        xv[i] = sm.x[r][jb] * expf(sv);
                     else
-                        sm.x[r][jb] = sm.valid[p][r] ? sm.w[p][r] * __builtin_amdgcn_exp2f(
-                                                                        (sm.x[r][jb] + sv) * kLog2e - sm.lnz[p][r])
-                                                     : 0.f;
+                        xv[i] = sm.valid[p][r] ? sm.w[p][r] * __builtin_amdgcn_exp2f(
+                                                                  (sm.x[r][jb] + sv) * kLog2e - sm.lnz[p][r])
+                                               : 0.f;
+                }
+                if constexpr (kBf) {
+                    static_assert(BG % 2 == 0, "record pairs");
+#pragma unroll
+                    for (int i = 0; i < BG; i += 2) {
+                        uint32_t pr[2];
+                        split_pair<2>(xv[i], xv[i + 1], pr);
+                        *reinterpret_cast<uint32_t*>(&sm.xh[jb][r0 + i]) = pr[0];
+                        *reinterpret_cast<uint32_t*>(&sm.xl[jb][r0 + i]) = pr[1];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < BG; i++) sm.x[r0 + i][jb] = xv[i];
                 }
             }
             __syncthreads();
@@ -381,15 +406,49 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                     X[i][e] *= sm.ebc[j];
                 }
             }
-            // k-steps outermost (not unrolled): each step's operands are read
-            // once for all of the wave's tiles, and few are live at a time
-#pragma unroll 1
-            for (int ks = 0; ks < kBC / 4; ks++) {
-                const int r = 4 * ks + g4;
+            if constexpr (kBf) {
+                // bf16 inputs: the chunk's 32 records as one bf16 k-step.  The
+                // wave's tiles share one column tile, so its B operand (8
+                // records of one column: V, exact in bf16, or g in two
+                // terms) is read once; the A side comes pre-split.
+                static_assert(kSW % CT == 0, "one column tile per wave");
+                const int mt = wv % CT;
+                float yv[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) yv[i] = sm.y[8 * g4 + i][16 * mt + l16];
+                uint32_t pb[4][2];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    if constexpr (REV) {
+                        split_pair<2>(yv[2 * e2], yv[2 * e2 + 1], pb[e2]);
+                    } else {
+                        pb[e2][0] = pack_bf16x2(yv[2 * e2], yv[2 * e2 + 1]);
+                        pb[e2][1] = 0u;
+                    }
+                }
+                const u16x8 bhi = __builtin_bit_cast(u16x8, make_uint4(pb[0][0], pb[1][0], pb[2][0], pb[3][0]));
+                const u16x8 blo = __builtin_bit_cast(u16x8, make_uint4(pb[0][1], pb[1][1], pb[2][1], pb[3][1]));
 #pragma unroll
                 for (int i = 0; i < TPW; i++) {
-                    const int t = wv + kSW * i;
-                    X[i] = mf(sm.x[r][16 * (t / CT) + l16], sm.y[r][16 * (t % CT) + l16], X[i]);
+                    const int jt = (wv + kSW * i) / CT;
+                    const u16x8 ahi = *reinterpret_cast<const u16x8*>(&sm.xh[16 * jt + l16][8 * g4]);
+                    const u16x8 alo = *reinterpret_cast<const u16x8*>(&sm.xl[16 * jt + l16][8 * g4]);
+                    X[i] = mfma16(ahi, bhi, X[i]);
+                    X[i] = mfma16(alo, bhi, X[i]);
+                    if constexpr (REV) X[i] = mfma16(ahi, blo, X[i]);
+                }
+            } else {
+                // k-steps outermost (not unrolled): each step's operands are
+                // read once for all of the wave's tiles, and few are live at a
+                // time
+#pragma unroll 1
+                for (int ks = 0; ks < kBC / 4; ks++) {
+                    const int r = 4 * ks + g4;
+#pragma unroll
+                    for (int i = 0; i < TPW; i++) {
+                        const int t = wv + kSW * i;
+                        X[i] = mf(sm.x[r][16 * (t / CT) + l16], sm.y[r][16 * (t % CT) + l16], X[i]);
+                    }
                 }
             }
         }
