@@ -180,8 +180,8 @@ struct SwSmem {
     // bf16 inputs: the A side transposed [state row][record] in two bf16
     // terms (rows of 80 bytes: 16-byte aligned operand reads, and the 16
     // rows one read touches fall on distinct banks)
-    uint16_t xh[CK][kBC + 8];
-    uint16_t xl[CK][kBC + 8];
+    alignas(16) uint16_t xh[CK][kBC + 8];
+    alignas(16) uint16_t xl[CK][kBC + 8];
     // metadata of three chunks (the current one and the two ahead)
     float lnz[3][kBC];       // key normalisers (log2)
     float w[3][kBC];
@@ -379,12 +379,20 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                 }
                 if constexpr (kBf) {
                     static_assert(BG % 2 == 0, "record pairs");
+                    uint32_t pr[BG / 2][2];
 #pragma unroll
-                    for (int i = 0; i < BG; i += 2) {
-                        uint32_t pr[2];
-                        split_pair<2>(xv[i], xv[i + 1], pr);
-                        *reinterpret_cast<uint32_t*>(&sm.xh[jb][r0 + i]) = pr[0];
-                        *reinterpret_cast<uint32_t*>(&sm.xl[jb][r0 + i]) = pr[1];
+                    for (int i = 0; i < BG; i += 2) split_pair<2>(xv[i], xv[i + 1], pr[i / 2]);
+                    if constexpr (BG == 8) {
+                        // one 16-byte store per term: the 16 rows of a
+                        // quarter-wave fall on distinct banks
+                        *reinterpret_cast<uint4*>(&sm.xh[jb][r0]) = make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]);
+                        *reinterpret_cast<uint4*>(&sm.xl[jb][r0]) = make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < BG; i += 2) {
+                            *reinterpret_cast<uint32_t*>(&sm.xh[jb][r0 + i]) = pr[i / 2][0];
+                            *reinterpret_cast<uint32_t*>(&sm.xl[jb][r0 + i]) = pr[i / 2][1];
+                        }
                     }
                 } else {
 #pragma unroll
