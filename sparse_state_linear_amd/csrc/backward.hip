@@ -504,8 +504,9 @@ struct ChSmem {
 }  // namespace
 
 // One block per checkpoint slot (a slot that holds no chunk exits at once):
-// the chunk's state operands are loaded first, so that their latency
-// overlaps the record-side work.
+// the chunk's state operands are loaded as row blocks first, so that their
+// latency overlaps the record-side work, and as column blocks after it
+// (mostly from L2 by then).
 template <int CK, int DV, typename TIn>
 __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs a) {
     using SM = ChSmem<CK, DV>;
@@ -528,22 +529,15 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     constexpr int cur = 0;
 
     // ---- this wave's state operands.  Column block wv of S_in and G~ (the
-    //      products that contract over state rows): lane (l16, g4) takes row
-    //      4 ks + g4, column 16 wv + l16.  Row block wv (the products that
-    //      contract over columns; any order of the columns will do): lane
-    //      (l16, g4) takes row 16 wv + l16 and the columns g4 DV/4 + ks, so
-    //      each lane reads one contiguous quarter row with 16-byte loads.
+    //      products that contract over state rows; loaded further down):
+    //      lane (l16, g4) takes row 4 ks + g4, column 16 wv + l16.  Row block
+    //      wv (the products that contract over columns; any order of the
+    //      columns will do): lane (l16, g4) takes row 16 wv + l16 and the
+    //      columns g4 DV/4 + ks, so each lane reads one contiguous quarter row
+    //      with 16-byte loads.
     const float* __restrict__ Sin = a.ckS + x * (int64_t)(CK * DV);
     const float* __restrict__ Gc = a.ckG + x * (int64_t)(CK * DV);
     float sc[NKC], gc[NKC], sr[NKD], gr[NKD];
-    if (wv < CT) {
-#pragma unroll
-        for (int ks = 0; ks < NKC; ks++) {
-            const int64_t o = (int64_t)(4 * ks + g4) * DV + 16 * wv + l16;
-            sc[ks] = Sin[o];
-            gc[ks] = Gc[o];
-        }
-    }
     if (wv < RT) {
         const float4* s4 = reinterpret_cast<const float4*>(Sin + (int64_t)(16 * wv + l16) * DV + g4 * NKD);
         const float4* g4p = reinterpret_cast<const float4*>(Gc + (int64_t)(16 * wv + l16) * DV + g4 * NKD);
@@ -632,6 +626,16 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     }
     __syncthreads();
 
+    // the column blocks of S_in and G~: the row blocks, loaded first, have
+    // brought the same lines into L2 by now
+    if (wv < CT) {
+#pragma unroll
+        for (int ks = 0; ks < NKC; ks++) {
+            const int64_t o = (int64_t)(4 * ks + g4) * DV + 16 * wv + l16;
+            sc[ks] = Sin[o];
+            gc[ks] = Gc[o];
+        }
+    }
     // ---- A = Qt Kh^T and GV = g V^T masked to s <= r: the 16x16 tiles
     //      (0,0), (1,0), (1,1) of each, one wave per tile; tile (0,1) is zero
     if (wv < 6) {
