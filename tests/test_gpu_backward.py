@@ -3,9 +3,10 @@ backward: every element of dq, dkey_logits, dv, dlog_alpha, drouter_logits
 and dinitial_states.
 
 Bars (max|err| / rms(ref), per tensor): 5e-3 for bf16 inputs (the bar of the
-forward's bf16 outputs).  The backward computes in fp32 whatever the input
-type, so fp32 inputs get a bar derived from fp32 arithmetic rather than the
-forward's 1e-5: unit roundoff u = 2^-24 = 6e-8; a gradient element sums
+forward's bf16 outputs; some of their products run on bf16 MFMA with
+two-term splits, about 2^-16 relative).  With fp32 inputs the backward
+computes in fp32 throughout, so they get a bar derived from fp32 arithmetic
+rather than the forward's 1e-5: unit roundoff u = 2^-24 = 6e-8; a gradient element sums
 O(n) terms (n up to a segment's records, ~1e3 here), each carried through
 up to n/16 chunk steps, so the rounding error grows like sqrt(n) u ~ 2e-6
 of the largest term; the max/rms ratio of the tensors (~5) and the
@@ -18,7 +19,7 @@ import torch
 import oracle
 import sparse_state_linear_amd as sse
 import sse_inputs as si
-from gpu_util import NAMES, announce, nan_like, oracle_threads, rel_err, to_dev
+from gpu_util import NAMES, announce, nan_like, oracle_threads, rel_err, rel_err_big, to_dev
 
 pytestmark = pytest.mark.gpu
 BWD_TOL = {"bf16": 5e-3, "f32": 2e-4}
@@ -149,34 +150,20 @@ def test_backward_run_twice_bitwise():
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
 
 
-def test_backward_main_full_size_sampled():
+def test_backward_main_full_size():
     """The main workload (B=4, H=16, T=8192, c=d=128, N=16, k=2) in one
-    backward call; eight (sequence, head) units (every element of their
-    gradients) against the oracle, which recomputes each unit alone."""
+    backward call, every element of every gradient against the oracle (all
+    64 (sequence, head) units, on the host threads)."""
     w = si.WORKLOADS["main_bf16"]
     inp = si.forward_inputs(w)
     lengths = [w.T] * w.B
     do, _, _ = _grad_inputs(w, lengths, 780, with_init=False, with_dfinal=False)
     announce("main_bf16 backward full size")
     got = _run(inp, w, do, None, None)
-    cu = inp["cu_seqlens"]
-    units = [(0, 0), (3, 15), (1, 7), (2, 3), (0, 11), (3, 2), (1, 14), (2, 9)]
-
-    def one(u):
-        s, h = u
-        sl = slice(int(cu[s]), int(cu[s + 1]))
-        sub = {n: np.ascontiguousarray(inp[n][sl, h:h + 1]) for n in NAMES}
-        return oracle.backward(*(sub[n] for n in NAMES), np.array([0, sl.stop - sl.start], np.int32),
-                               w.N, w.topk, do[sl, h:h + 1].astype(np.float64))
-
-    from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(min(8, oracle_threads())) as ex:
-        refs = list(ex.map(one, units))
-    for (s, h), ref in zip(units, refs):
-        sl = slice(int(cu[s]), int(cu[s + 1]))
-        for name in GRADS[:5]:
-            e = rel_err(got[name][sl, h], ref[name][:, 0])
-            assert e <= BWD_TOL["bf16"], (s, h, name, e)
-        e = rel_err(got["dinitial_states"][s, h], ref["dinitial_states"][0, 0])
-        assert e <= BWD_TOL["bf16"], (s, h, "dinitial_states", e)
-        print(f"  unit ({s},{h}) ok", flush=True)
+    announce("main_bf16 backward full size: oracle")
+    ref = oracle.backward(*(inp[n] for n in NAMES), inp["cu_seqlens"], w.N, w.topk,
+                          do.astype(np.float64), threads=oracle_threads())
+    for name in GRADS:
+        e = rel_err_big(got[name], ref[name])
+        print(f"  {name} rel err {e:.3e}", flush=True)
+        assert e <= BWD_TOL["bf16"], (name, e)
