@@ -494,6 +494,12 @@ struct ChSmem {
     float btot[kCW * kWave / CK][CK];   // per record group: its total of the log decay
     float dwp[kCW][kBC];         // per-wave partials of y . g
     float kdp[kCW][kBC];         // per-wave partials of K0 . dKh
+    // bf16 inputs: Qt and Kh = w K0 in two bf16 terms [record][state row]
+    // (rows of 2 (CK + 8) bytes, 16-byte aligned operand reads)
+    alignas(16) uint16_t qh[kBC][CK + 8];
+    alignas(16) uint16_t ql[kBC][CK + 8];
+    alignas(16) uint16_t kh[kBC][CK + 8];
+    alignas(16) uint16_t kl[kBC][CK + 8];
     // record lists of the current chunk and the next one
     float w[2][kBC];
     float lnz[2][kBC];
@@ -516,6 +522,8 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     static_assert(CT <= kCW && RT <= kCW, "one column and one row block per wave");
     static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
     static_assert(DV % 32 == 0, "column quarters of whole 8-column pieces");
+    static_assert(CK % 32 == 0, "row quarters of whole 8-row k-steps");
+    constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for some products
     __shared__ SM sm;
     const int64_t x = blockIdx.x;
     if (a.slot_meta[x * kBC].slot == kNoSlot) return;  // uniform: no chunk here
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 
     // ---- this wave's state operands.  Column block wv of S_in and G~ (the
     //      products that contract over state rows; loaded further down):
-    //      lane (l16, g4) takes row 4 ks + g4, column 16 wv + l16.  Row block
+    //      lane (l16, g4) takes row g4 CK/4 + ks, column 16 wv + l16.  Row block
     //      wv (the products that contract over columns; any order of the
     //      columns will do): lane (l16, g4) takes row 16 wv + l16 and the
     //      columns g4 DV/4 + ks, so each lane reads one contiguous quarter row
@@ -617,11 +625,22 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             const int r = r0 + i;
             const float b = pre + bl[i];
             const float e = expf(b);
-            sm.qt[r][jb] *= e;
-            sm.k0[r][jb] = sm.slot[cur][r] != kNoSlot
-                               ? __builtin_amdgcn_exp2f((sm.k0[r][jb] - b) * kLog2e - sm.lnz[cur][r])
-                               : 0.f;
+            const float qv = sm.qt[r][jb] * e;
+            const float kv = sm.slot[cur][r] != kNoSlot
+                                 ? __builtin_amdgcn_exp2f((sm.k0[r][jb] - b) * kLog2e - sm.lnz[cur][r])
+                                 : 0.f;
+            sm.qt[r][jb] = qv;
+            sm.k0[r][jb] = kv;
             sm.eb[r][jb] = e;
+            if constexpr (kBf) {
+                uint16_t tq[2], tk[2];
+                split_levels<2>(qv, tq);
+                split_levels<2>(sm.w[cur][r] * kv, tk);
+                sm.qh[r][jb] = tq[0];
+                sm.ql[r][jb] = tq[1];
+                sm.kh[r][jb] = tk[0];
+                sm.kl[r][jb] = tk[1];
+            }
         }
     }
     __syncthreads();
@@ -631,7 +650,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     if (wv < CT) {
 #pragma unroll
         for (int ks = 0; ks < NKC; ks++) {
-            const int64_t o = (int64_t)(4 * ks + g4) * DV + 16 * wv + l16;
+            const int64_t o = (int64_t)(g4 * NKC + ks) * DV + 16 * wv + l16;
             sc[ks] = Sin[o];
             gc[ks] = Gc[o];
         }
@@ -671,17 +690,55 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         const int m = 16 * wv + l16;
         f32x4b y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4b dv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        // over state rows: y += Qt S_in, dV += Kh G~
+        // over state rows: y += Qt S_in, dV += Kh G~.  Lane group g4 holds
+        // the state rows g4 CK/4 + ks (a contiguous quarter)
+        if constexpr (kBf) {
+            // bf16 MFMA: k-step t of lane group g4 contracts the rows
+            // g4 CK/4 + 8 t + i (i < 8): the lane's own 8 consecutive S_in and
+            // G~ values (split here) and 8 consecutive values of its record's
+            // row of Qt and Kh (split by the decay scan)
+            auto pack8 = [](const uint32_t (&pr)[4][2], int l) {
+                return __builtin_bit_cast(u16x8, make_uint4(pr[0][l], pr[1][l], pr[2][l], pr[3][l]));
+            };
 #pragma unroll
-        for (int ks = 0; ks < NKC; ks++) {
-            const int jj = 4 * ks + g4;
-            const float bs = sc[ks];
-            const float bg = sm.ebc[jj] * gc[ks];
+            for (int t = 0; t < NKC / 8; t++) {
+                const int j0 = g4 * NKC + 8 * t;
+                uint32_t ps[4][2], pg[4][2];
 #pragma unroll
-            for (int rt = 0; rt < 2; rt++) {
-                const int r = 16 * rt + l16;
-                y[rt] = mf(sm.qt[r][jj], bs, y[rt]);
-                dv[rt] = mf(sm.w[cur][r] * sm.k0[r][jj], bg, dv[rt]);
+                for (int e2 = 0; e2 < 4; e2++) {
+                    split_pair<2>(sc[8 * t + 2 * e2], sc[8 * t + 2 * e2 + 1], ps[e2]);
+                    split_pair<2>(sm.ebc[j0 + 2 * e2] * gc[8 * t + 2 * e2],
+                                  sm.ebc[j0 + 2 * e2 + 1] * gc[8 * t + 2 * e2 + 1], pg[e2]);
+                }
+                const u16x8 shi = pack8(ps, 0), slo = pack8(ps, 1);
+                const u16x8 ghi = pack8(pg, 0), glo = pack8(pg, 1);
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    const int r = 16 * rt + l16;
+                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sm.qh[r][j0]);
+                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sm.ql[r][j0]);
+                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sm.kh[r][j0]);
+                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sm.kl[r][j0]);
+                    y[rt] = mfma16(qhi, shi, y[rt]);
+                    y[rt] = mfma16(qhi, slo, y[rt]);
+                    y[rt] = mfma16(qlo, shi, y[rt]);
+                    dv[rt] = mfma16(khi, ghi, dv[rt]);
+                    dv[rt] = mfma16(khi, glo, dv[rt]);
+                    dv[rt] = mfma16(klo, ghi, dv[rt]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKC; ks++) {
+                const int jj = g4 * NKC + ks;
+                const float bs = sc[ks];
+                const float bg = sm.ebc[jj] * gc[ks];
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    const int r = 16 * rt + l16;
+                    y[rt] = mf(sm.qt[r][jj], bs, y[rt]);
+                    dv[rt] = mf(sm.w[cur][r] * sm.k0[r][jj], bg, dv[rt]);
+                }
             }
         }
         // over records s: y += A V, dV += A^T g
