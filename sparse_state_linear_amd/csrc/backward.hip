@@ -480,13 +480,18 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
 
 namespace {
 
-template <int CK, int DV>
+template <int CK, int DV, bool BF>
 struct ChSmem {
     static constexpr int KS = lds_stride(CK), VS = lds_stride(DV);
+    // V: fp32 for fp32 inputs; for bf16 inputs its bf16 bits as loaded
+    // (exact), in rows of 2 (DV + 8) bytes (16-byte aligned operand reads)
+    using VT = typename std::conditional<BF, uint16_t, float>::type;
+    static constexpr int VRS = BF ? DV + 8 : VS;
+    static constexpr int NB = BF ? kBC : 1;   // rows of the bf16-only arrays
     float qt[kBC][KS];           // Qt
     float k0[kBC][KS];           // K0
     float eb[kBC][KS];           // b, then e^b
-    float v[kBC][VS];
+    alignas(16) VT v[kBC][VRS];
     float g[kBC][VS];            // g = w do
     float A[kBC][lds_stride(kBC)];    // A (masked)
     float GV[kBC][lds_stride(kBC)];   // GV (masked)
@@ -494,12 +499,15 @@ struct ChSmem {
     float btot[kCW * kWave / CK][CK];   // per record group: its total of the log decay
     float dwp[kCW][kBC];         // per-wave partials of y . g
     float kdp[kCW][kBC];         // per-wave partials of K0 . dKh
-    // bf16 inputs: Qt and Kh = w K0 in two bf16 terms [record][state row]
-    // (rows of 2 (CK + 8) bytes, 16-byte aligned operand reads)
-    alignas(16) uint16_t qh[kBC][CK + 8];
-    alignas(16) uint16_t ql[kBC][CK + 8];
-    alignas(16) uint16_t kh[kBC][CK + 8];
-    alignas(16) uint16_t kl[kBC][CK + 8];
+    // bf16 inputs: Qt and Kh = w K0 [record][state row], g [record][column]
+    // in two bf16 terms (rows of 2 (n + 8) bytes, 16-byte aligned operand
+    // reads)
+    alignas(16) uint16_t qh[NB][CK + 8];
+    alignas(16) uint16_t ql[NB][CK + 8];
+    alignas(16) uint16_t kh[NB][CK + 8];
+    alignas(16) uint16_t kl[NB][CK + 8];
+    alignas(16) uint16_t gh[NB][DV + 8];
+    alignas(16) uint16_t gl[NB][DV + 8];
     // record lists of the current chunk and the next one
     float w[2][kBC];
     float lnz[2][kBC];
@@ -515,7 +523,8 @@ struct ChSmem {
 // (mostly from L2 by then).
 template <int CK, int DV, typename TIn>
 __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs a) {
-    using SM = ChSmem<CK, DV>;
+    constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for some products
+    using SM = ChSmem<CK, DV, kBf>;
     constexpr int CT = DV / 16, RT = CK / 16;
     constexpr int NT = kCW * kWave;
     constexpr int NKC = CK / 4, NKD = DV / 4;
@@ -523,8 +532,14 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
     static_assert(DV % 32 == 0, "column quarters of whole 8-column pieces");
     static_assert(CK % 32 == 0, "row quarters of whole 8-row k-steps");
-    constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for some products
     __shared__ SM sm;
+    // V[r][m] as fp32
+    auto vf = [&](int r, int m) -> float {
+        if constexpr (kBf)
+            return bf16_bits_to_f32(sm.v[r][m]);
+        else
+            return sm.v[r][m];
+    };
     const int64_t x = blockIdx.x;
     if (a.slot_meta[x * kBC].slot == kNoSlot) return;  // uniform: no chunk here
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -592,10 +607,22 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             pv.load(gv + off);
             pd.load(a.dout + off);
             const float wr = sm.w[cur][rv];
+            float gg[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                sm.v[rv][mv + i] = pv.get(i);
-                sm.g[rv][mv + i] = wr * pd.get(i);
+                gg[i] = wr * pd.get(i);
+                sm.g[rv][mv + i] = gg[i];
+            }
+            if constexpr (kBf) {
+                *reinterpret_cast<uint4*>(&sm.v[rv][mv]) = pv.u;
+                uint32_t pr[4][2];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) split_pair<2>(gg[2 * e2], gg[2 * e2 + 1], pr[e2]);
+                *reinterpret_cast<uint4*>(&sm.gh[rv][mv]) = make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]);
+                *reinterpret_cast<uint4*>(&sm.gl[rv][mv]) = make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; i++) sm.v[rv][mv + i] = pv.get(i);
             }
         }
     }
@@ -670,7 +697,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         } else {
             for (int ks = 0; ks < DV / 4; ks++) {
                 const int m = 4 * ks + g4;
-                acc = mf(sm.g[16 * rt + l16][m], sm.v[16 * st + l16][m], acc);
+                acc = mf(sm.g[16 * rt + l16][m], vf(16 * st + l16, m), acc);
             }
         }
 #pragma unroll
@@ -747,7 +774,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             const int s = 4 * ks + g4;
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
-                y[rt] = mf(sm.A[16 * rt + l16][s], sm.v[s][m], y[rt]);
+                y[rt] = mf(sm.A[16 * rt + l16][s], vf(s, m), y[rt]);
                 dv[rt] = mf(sm.A[s][16 * rt + l16], sm.g[s][m], dv[rt]);
             }
         }
@@ -773,43 +800,52 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         const float ebj = sm.ebc[j];
         float sg = 0.f;   // this lane's part of rowsum(S_in . G~) of row j
         // over the columns m = g4 DV/4 + ks: dQt += g S_in^T, V G~^T
-        constexpr bool kVgBf16 = std::is_same<TIn, bf16_t>::value;
 #pragma unroll
         for (int ks = 0; ks < NKD; ks++) {
             const int mm = g4 * NKD + ks;
             const float st = sr[ks];
             const float gt = ebj * gr[ks];
             sg += st * gt;
-#pragma unroll
-            for (int rt = 0; rt < 2; rt++) {
-                const int r = 16 * rt + l16;
-                dq[rt] = mf(sm.g[r][mm], st, dq[rt]);
-                if constexpr (!kVgBf16) vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
-            }
-        }
-        if constexpr (kVgBf16) {
-            // V is exact in bf16 (bf16 inputs): V G~^T on bf16 MFMA with G~
-            // in two bf16 terms.  k-step t of lane group g4 contracts the
-            // columns g4 DV/4 + 8 t + i (i < 8): the lane's own 8 consecutive
-            // G~ values, and 8 consecutive V values of its record's row.
-#pragma unroll
-            for (int t = 0; t < NKD / 8; t++) {
-                uint32_t pr[4][2];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; e2++)
-                    split_pair<2>(ebj * gr[8 * t + 2 * e2], ebj * gr[8 * t + 2 * e2 + 1], pr[e2]);
-                const u16x8 ghi = __builtin_bit_cast(u16x8, make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]));
-                const u16x8 glo = __builtin_bit_cast(u16x8, make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]));
+            if constexpr (!kBf) {
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
-                    // 8-byte LDS reads: the row stride keeps every row 8-byte aligned
-                    const float2* vr = reinterpret_cast<const float2*>(&sm.v[16 * rt + l16][g4 * NKD + 8 * t]);
-                    const float2 v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3];
-                    const u16x8 va = __builtin_bit_cast(
-                        u16x8, make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v1.x, v1.y),
-                                          pack_bf16x2(v2.x, v2.y), pack_bf16x2(v3.x, v3.y)));
-                    vg[rt] = mfma16(va, ghi, vg[rt]);
-                    vg[rt] = mfma16(va, glo, vg[rt]);
+                    const int r = 16 * rt + l16;
+                    dq[rt] = mf(sm.g[r][mm], st, dq[rt]);
+                    vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
+                }
+            }
+        }
+        if constexpr (kBf) {
+            // bf16 inputs: both products on bf16 MFMA.  k-step t of lane
+            // group g4 contracts the columns g4 DV/4 + 8 t + i (i < 8): the
+            // lane's own 8 consecutive S_in and G~ values (split here) and 8
+            // consecutive values of its record's row of g (split by the row
+            // loader) and of V (exact in bf16).
+            auto pack8 = [](const uint32_t (&pr)[4][2], int l) {
+                return __builtin_bit_cast(u16x8, make_uint4(pr[0][l], pr[1][l], pr[2][l], pr[3][l]));
+            };
+#pragma unroll
+            for (int t = 0; t < NKD / 8; t++) {
+                const int m0 = g4 * NKD + 8 * t;
+                uint32_t pg[4][2], ps[4][2];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    split_pair<2>(ebj * gr[8 * t + 2 * e2], ebj * gr[8 * t + 2 * e2 + 1], pg[e2]);
+                    split_pair<2>(sr[8 * t + 2 * e2], sr[8 * t + 2 * e2 + 1], ps[e2]);
+                }
+                const u16x8 gthi = pack8(pg, 0), gtlo = pack8(pg, 1);
+                const u16x8 shi = pack8(ps, 0), slo = pack8(ps, 1);
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    const int r = 16 * rt + l16;
+                    const u16x8 va = *reinterpret_cast<const u16x8*>(&sm.v[r][m0]);
+                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sm.gh[r][m0]);
+                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sm.gl[r][m0]);
+                    vg[rt] = mfma16(va, gthi, vg[rt]);
+                    vg[rt] = mfma16(va, gtlo, vg[rt]);
+                    dq[rt] = mfma16(ghi, shi, dq[rt]);
+                    dq[rt] = mfma16(ghi, slo, dq[rt]);
+                    dq[rt] = mfma16(glo, shi, dq[rt]);
                 }
             }
         }
