@@ -44,9 +44,12 @@
 // the 16-column block w of the d-side outputs (y, dV) and the 16-row block w
 // of the c-side ones (dQt, dKh).  The state operands are read straight from
 // the stored states in the MFMA operand layout (rows, or transposed for the
-// products that contract over d).  The products run on fp32 MFMA, except
-// V G~^T with bf16 inputs: V is exact in bf16 there, so it runs on bf16
-// MFMA with G~ in two bf16 terms.
+// products that contract over d).  With fp32 inputs every product runs on
+// fp32 MFMA.  With bf16 inputs the four products over state rows or columns
+// (Qt S_in, Kh G~, g S_in^T, V G~^T) run on bf16 MFMA with their operands in
+// two bf16 terms (V is exact in bf16), the products of the two low terms
+// left out; the A and GV tiles and the products over the chunk's records
+// stay on fp32 MFMA.
 // Launch 3 (combine): each record's gradients went to its own slot [token,
 // head, rank] (rank = its place in the token's top-k list, k for the shared
 // partition); one wave per (token, head) sums the token's k + 1 slots and
@@ -519,8 +522,7 @@ struct ChSmem {
 
 // One block per checkpoint slot (a slot that holds no chunk exits at once):
 // the chunk's state operands are loaded as row blocks first, so that their
-// latency overlaps the record-side work, and as column blocks after it
-// (mostly from L2 by then).
+// latency overlaps the record-side work, and as column blocks after it.
 template <int CK, int DV, typename TIn>
 __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs a) {
     constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for some products
@@ -672,8 +674,9 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     }
     __syncthreads();
 
-    // the column blocks of S_in and G~: the row blocks, loaded first, have
-    // brought the same lines into L2 by now
+    // the column blocks of S_in and G~ (issued here, after the record-side
+    // work: faster than with the row blocks, although most of their lines
+    // come from HBM a second time)
     if (wv < CT) {
 #pragma unroll
         for (int ks = 0; ks < NKC; ks++) {
