@@ -194,8 +194,9 @@ struct SwSmem {
 
 }  // namespace
 
-// Blocks [0, NSEG) run the forward sweep of segment u = block, blocks
-// [NSEG, 2 NSEG) the reverse sweep of segment u = block - NSEG.
+// Blocks [0, 2 SH) run the shared chains (u < SH = sequences x heads),
+// forward then reverse; blocks [2 SH, 2 NSEG) the routed segments, forward
+// then reverse.
 template <int CK, int DV, typename TIn>
 __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_kernel(const BwdArgs a) {
     using SM = SwSmem<CK, DV>;
@@ -207,9 +208,14 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
     constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for the products
     __shared__ SM sm;
 
+    // Blocks are dispatched in index order: the shared chains (the longest
+    // segments, every token of a sequence) come first in both directions,
+    // so that they run beside the routed segments instead of after them
     const int nseg = a.num_seqs * a.H * (a.N + 1);
-    const bool rev = (int)blockIdx.x >= nseg;
-    const int u = rev ? (int)blockIdx.x - nseg : (int)blockIdx.x;
+    const int SH = a.num_seqs * a.H, nrt = nseg - SH;
+    const int b = (int)blockIdx.x;
+    const bool rev = b < 2 * SH ? b >= SH : b - 2 * SH >= nrt;
+    const int u = b < 2 * SH ? b % SH : SH + (b - 2 * SH) % nrt;
     const Seg q = seg_of<CK, DV>(a, u);
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
