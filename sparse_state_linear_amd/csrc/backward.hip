@@ -46,10 +46,10 @@
 // the stored states in the MFMA operand layout (rows, or transposed for the
 // products that contract over d).  With fp32 inputs every product runs on
 // fp32 MFMA.  With bf16 inputs the four products over state rows or columns
-// (Qt S_in, Kh G~, g S_in^T, V G~^T) run on bf16 MFMA with their operands in
-// two bf16 terms (V is exact in bf16), the products of the two low terms
-// left out; the A and GV tiles and the products over the chunk's records
-// stay on fp32 MFMA.
+// (Qt S_in, Kh G~, g S_in^T, V G~^T) and the A and GV tiles run on bf16
+// MFMA with their operands in two bf16 terms (V is exact in bf16), the
+// products of the two low terms left out; the products over the chunk's
+// records stay on fp32 MFMA.
 // Launch 3 (combine): each record's gradients went to its own slot [token,
 // head, rank] (rank = its place in the token's top-k list, k for the shared
 // partition); one wave per (token, head) sums the token's k + 1 slots and
@@ -698,7 +698,36 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         const int tt = wv % 3;
         const int rt = tt == 0 ? 0 : 1, st = tt == 2 ? 1 : 0;
         f32x4b acc = {0.f, 0.f, 0.f, 0.f};
-        if (isA) {
+        if constexpr (kBf) {
+            // bf16 MFMA over 32-wide k-steps: lane (l16, g4) supplies the 8
+            // consecutive rows j (or columns m) 32 t + 8 g4 + i of its
+            // record's row of the pre-split operands (Qt, Kh, g in two
+            // terms, V exact); the output layout is that of the fp32 MFMA
+            const int ra = 16 * rt + l16, sb = 16 * st + l16;
+            if (isA) {
+#pragma unroll
+                for (int t = 0; t < CK / 32; t++) {
+                    const int j0 = 32 * t + 8 * g4;
+                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sm.qh[ra][j0]);
+                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sm.ql[ra][j0]);
+                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sm.kh[sb][j0]);
+                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sm.kl[sb][j0]);
+                    acc = mfma16(qhi, khi, acc);
+                    acc = mfma16(qhi, klo, acc);
+                    acc = mfma16(qlo, khi, acc);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < DV / 32; t++) {
+                    const int m0 = 32 * t + 8 * g4;
+                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sm.gh[ra][m0]);
+                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sm.gl[ra][m0]);
+                    const u16x8 vb = *reinterpret_cast<const u16x8*>(&sm.v[sb][m0]);
+                    acc = mfma16(ghi, vb, acc);
+                    acc = mfma16(glo, vb, acc);
+                }
+            }
+        } else if (isA) {
             for (int ks = 0; ks < CK / 4; ks++) {
                 const int j = 4 * ks + g4;
                 acc = mf(sm.qt[16 * rt + l16][j], sm.w[cur][16 * st + l16] * sm.k0[16 * st + l16][j], acc);
