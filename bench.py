@@ -209,20 +209,20 @@ def run_backward(args, w, si, sse, torch):
     nbytes = (HT * 2 * (3 * w.c + w.d + w.N) + HT * 4 * w.d + HT * 4 * (3 * w.c + w.d + w.N)
               + S * w.H * (w.N + 1) * w.c * w.d * 4)
     # five c x d products and three causal C x c / C x d pairs per record (C = 64).
-    # With bf16 inputs the five products run on bf16 MFMA (Qt S_in, Kh G~,
-    # g S_in^T, V G~^T in the chunk pass, Qt^T g in the reverse sweep) and are
-    # priced at its peak; the causal pairs run on fp32 MFMA
+    # With bf16 inputs all of them run on bf16 MFMA (Qt S_in, Kh G~, g S_in^T,
+    # V G~^T, the A and GV tiles and the products over a chunk's records in
+    # the chunk pass, Qt^T g in the reverse sweep) and are priced at its peak
     C = 64
-    flops_f32 = records * 2 * (1.5 * C * w.c + 1.5 * C * w.d)
-    flops_bf16 = records * 2 * (5 * w.c * w.d)
-    flops = flops_f32 + flops_bf16
-    mfma_ms = (flops_f32 / (MFMA_F32_PEAK_TFLOPS * 1e12) + flops_bf16 / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
-    roof_ms = max(nbytes / (HBM_PEAK_GBS * 1e9) * 1e3, mfma_ms)
+    flops = records * 2 * (1.5 * C * w.c + 1.5 * C * w.d + 5 * w.c * w.d)
+    hbm_ms = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    mfma_ms = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    roof_ms = max(hbm_ms, mfma_ms)
+    bound = ("hbm: inputs and do read once, the gradients written once, at 8 TB/s" if hbm_ms >= mfma_ms
+             else "mfma: every product at the bf16 peak (2.5 PFLOP/s)")
     return {"workload": w.notes + ", gradients of all five inputs and the initial states",
             "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "algorithmic_flops": flops, "roofline_ms": roof_ms, "frac": roof_ms / ms,
-            "bound": "mfma: the five c x d products at the bf16 peak (2.5 PFLOP/s), the causal "
-                     "pairs at the fp32 peak (157.3 TFLOP/s)"}
+            "hbm_ms": hbm_ms, "mfma_ms": mfma_ms, "bound": bound}
 
 
 def run_rowsparse(args, si, sse, torch):

@@ -45,11 +45,12 @@
 // of the c-side ones (dQt, dKh).  The state operands are read straight from
 // the stored states in the MFMA operand layout (rows, or transposed for the
 // products that contract over d).  With fp32 inputs every product runs on
-// fp32 MFMA.  With bf16 inputs the four products over state rows or columns
-// (Qt S_in, Kh G~, g S_in^T, V G~^T) and the A and GV tiles run on bf16
-// MFMA with their operands in two bf16 terms (V is exact in bf16), the
-// products of the two low terms left out; the products over the chunk's
-// records stay on fp32 MFMA.
+// fp32 MFMA.  With bf16 inputs every product runs on bf16 MFMA with its
+// operands in two bf16 terms (V is exact in bf16), the products of the two
+// low terms left out: the four over state rows or columns (Qt S_in, Kh G~,
+// g S_in^T, V G~^T), the A and GV tiles, and the four over the chunk's 32
+// records (A V, A^T g, GV Kh, GV^T Qt) as one k-step each, their record-
+// major operands gathered by LDS transpose reads.
 // Launch 3 (combine): each record's gradients went to its own slot [token,
 // head, rank] (rank = its place in the token's top-k list, k for the shared
 // partition); one wave per (token, head) sums the token's k + 1 slots and
@@ -497,13 +498,14 @@ struct ChSmem {
     using VT = typename std::conditional<BF, uint16_t, float>::type;
     static constexpr int VRS = BF ? DV + 8 : VS;
     static constexpr int NB = BF ? kBC : 1;   // rows of the bf16-only arrays
+    static constexpr int NF = BF ? 1 : kBC;   // rows of the fp32-only arrays
     float qt[kBC][KS];           // Qt
     float k0[kBC][KS];           // K0
     float eb[kBC][KS];           // b, then e^b
     alignas(16) VT v[kBC][VRS];
     float g[kBC][VS];            // g = w do
-    float A[kBC][lds_stride(kBC)];    // A (masked)
-    float GV[kBC][lds_stride(kBC)];   // GV (masked)
+    float A[NF][lds_stride(kBC)];     // A (masked), fp32 inputs
+    float GV[NF][lds_stride(kBC)];    // GV (masked), fp32 inputs
     float ebc[CK];               // e^{b_C}
     float btot[kCW * kWave / CK][CK];   // per record group: its total of the log decay
     float dwp[kCW][kBC];         // per-wave partials of y . g
@@ -517,6 +519,11 @@ struct ChSmem {
     alignas(16) uint16_t kl[NB][CK + 8];
     alignas(16) uint16_t gh[NB][DV + 8];
     alignas(16) uint16_t gl[NB][DV + 8];
+    // bf16 inputs: A and GV (masked) [record r][record s] in two bf16 terms
+    alignas(16) uint16_t ah[NB][kBC + 8];
+    alignas(16) uint16_t al[NB][kBC + 8];
+    alignas(16) uint16_t gvh[NB][kBC + 8];
+    alignas(16) uint16_t gvl[NB][kBC + 8];
     // record lists of the current chunk and the next one
     float w[2][kBC];
     float lnz[2][kBC];
@@ -553,6 +560,14 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, g4 = lane / 16;
+    // bf16 MFMA operand over records from a record-major bf16 tile (row
+    // stride `stride` elements): lane (l16, g4) gets records 8 g4 + 0..7 of
+    // column c0 + l16, by two transpose reads; source lane 4 e + b of each
+    // 16-lane group addresses columns c0 + 4 b .. + 3 of record 8 g4 + e (+ 4)
+    auto tr16 = [&](const uint16_t* tile, int stride, int c0) {
+        const int r = 8 * g4 + l16 / 4, c = c0 + 4 * (l16 % 4);
+        return cat_tr(lds_tr(tile + r * stride + c), lds_tr(tile + (r + 4) * stride + c));
+    };
     const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
     const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
     const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
@@ -741,11 +756,26 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int r = 16 * rt + 4 * g4 + e, s = 16 * st + l16;
-            (isA ? sm.A : sm.GV)[r][s] = s <= r ? acc[e] : 0.f;
+            const float val = s <= r ? acc[e] : 0.f;
+            if constexpr (kBf) {
+                uint16_t tv[2];
+                split_levels<2>(val, tv);
+                (isA ? sm.ah : sm.gvh)[r][s] = tv[0];
+                (isA ? sm.al : sm.gvl)[r][s] = tv[1];
+            } else {
+                (isA ? sm.A : sm.GV)[r][s] = val;
+            }
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) (wv == 6 ? sm.A : sm.GV)[4 * g4 + e][16 + l16] = 0.f;
+        for (int e = 0; e < 4; e++) {
+            if constexpr (kBf) {
+                (wv == 6 ? sm.ah : sm.gvh)[4 * g4 + e][16 + l16] = 0;
+                (wv == 6 ? sm.al : sm.gvl)[4 * g4 + e][16 + l16] = 0;
+            } else {
+                (wv == 6 ? sm.A : sm.GV)[4 * g4 + e][16 + l16] = 0.f;
+            }
+        }
     }
     __syncthreads();
 
@@ -807,13 +837,33 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             }
         }
         // over records s: y += A V, dV += A^T g
-#pragma unroll
-        for (int ks = 0; ks < kBC / 4; ks++) {
-            const int s = 4 * ks + g4;
+        if constexpr (kBf) {
+            // the chunk's 32 records as one bf16 k-step: A rows from the
+            // split tiles, A^T, V and g columns by transpose reads
+            const u16x8 vb = tr16(&sm.v[0][0], SM::VRS, 16 * wv);
+            const u16x8 gbh = tr16(&sm.gh[0][0], DV + 8, 16 * wv);
+            const u16x8 gbl = tr16(&sm.gl[0][0], DV + 8, 16 * wv);
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
-                y[rt] = mf(sm.A[16 * rt + l16][s], vf(s, m), y[rt]);
-                dv[rt] = mf(sm.A[s][16 * rt + l16], sm.g[s][m], dv[rt]);
+                const u16x8 ahi = lds8(&sm.ah[16 * rt + l16][8 * g4]);
+                const u16x8 alo = lds8(&sm.al[16 * rt + l16][8 * g4]);
+                const u16x8 athi = tr16(&sm.ah[0][0], kBC + 8, 16 * rt);
+                const u16x8 atlo = tr16(&sm.al[0][0], kBC + 8, 16 * rt);
+                y[rt] = mfma16(ahi, vb, y[rt]);
+                y[rt] = mfma16(alo, vb, y[rt]);
+                dv[rt] = mfma16(athi, gbh, dv[rt]);
+                dv[rt] = mfma16(athi, gbl, dv[rt]);
+                dv[rt] = mfma16(atlo, gbh, dv[rt]);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kBC / 4; ks++) {
+                const int s = 4 * ks + g4;
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    y[rt] = mf(sm.A[16 * rt + l16][s], vf(s, m), y[rt]);
+                    dv[rt] = mf(sm.A[s][16 * rt + l16], sm.g[s][m], dv[rt]);
+                }
             }
         }
 #pragma unroll
@@ -888,13 +938,33 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             }
         }
         // over records s: dQt += GV Kh, dKh += GV^T Qt
-#pragma unroll
-        for (int ks = 0; ks < kBC / 4; ks++) {
-            const int s = 4 * ks + g4;
+        if constexpr (kBf) {
+            const u16x8 kbh = tr16(&sm.kh[0][0], CK + 8, 16 * wv);
+            const u16x8 kbl = tr16(&sm.kl[0][0], CK + 8, 16 * wv);
+            const u16x8 qbh = tr16(&sm.qh[0][0], CK + 8, 16 * wv);
+            const u16x8 qbl = tr16(&sm.ql[0][0], CK + 8, 16 * wv);
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
-                dq[rt] = mf(sm.GV[16 * rt + l16][s], sm.w[cur][s] * sm.k0[s][j], dq[rt]);
-                dk[rt] = mf(sm.GV[s][16 * rt + l16], sm.qt[s][j], dk[rt]);
+                const u16x8 ghi = lds8(&sm.gvh[16 * rt + l16][8 * g4]);
+                const u16x8 glo = lds8(&sm.gvl[16 * rt + l16][8 * g4]);
+                const u16x8 gthi = tr16(&sm.gvh[0][0], kBC + 8, 16 * rt);
+                const u16x8 gtlo = tr16(&sm.gvl[0][0], kBC + 8, 16 * rt);
+                dq[rt] = mfma16(ghi, kbh, dq[rt]);
+                dq[rt] = mfma16(ghi, kbl, dq[rt]);
+                dq[rt] = mfma16(glo, kbh, dq[rt]);
+                dk[rt] = mfma16(gthi, qbh, dk[rt]);
+                dk[rt] = mfma16(gthi, qbl, dk[rt]);
+                dk[rt] = mfma16(gtlo, qbh, dk[rt]);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kBC / 4; ks++) {
+                const int s = 4 * ks + g4;
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    dq[rt] = mf(sm.GV[16 * rt + l16][s], sm.w[cur][s] * sm.k0[s][j], dq[rt]);
+                    dk[rt] = mf(sm.GV[s][16 * rt + l16], sm.qt[s][j], dk[rt]);
+                }
             }
         }
         // the chunk decay term t of row j: rowsum(S_in . G~) over the four
