@@ -284,9 +284,11 @@ int sse_group_by_partition(const int32_t *topk_idx, const float *topk_w,
  * segments, in chunks of 32 records: a forward sweep stores every chunk's
  * starting state and a reverse sweep every chunk's state gradient in the
  * workspace, then all chunks' gradients are computed in parallel from them.
- * Arithmetic in fp32 (fp32 MFMA 16x16x4), whatever the input type; the
- * chunked factorisation needs the sum of log_alpha over any 32 consecutive
- * records of one partition to stay above -80, for either input type.
+ * Accumulation in fp32.  With fp32 inputs every product runs on fp32 MFMA;
+ * with bf16 inputs on bf16 MFMA, each fp32 operand in two bf16 terms (about
+ * 2^-16 relative; the bf16 inputs themselves are exact).  The chunked
+ * factorisation needs the sum of log_alpha over any 32 consecutive records
+ * of one partition to stay above -80, for either input type.
  *   inputs as sse_forward; initial_states [num_seqs, H, N+1, c, d] or NULL
  *   d_o                   [total_tokens, H, d] fp32
  *   d_final_states        [num_seqs, H, N+1, c, d] fp32 or NULL (zeros)
