@@ -157,7 +157,7 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Barrier for LDS hazards only: global loads and atomics may stay in flight.
+// Barrier for LDS hazards only: global loads and stores may stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -19,7 +19,7 @@
 //              chunk n+6, prepare chunk n+1 into stage (n+1)%2, store the
 //              metadata of chunk n+5 into the ring;
 //   consumers: finish chunk n-1 (O += A V with A from the previous
-//              iteration, then the output stores/atomics), compute the causal
+//              iteration, then the output stores), compute the causal
 //              A tiles of chunk n, O = Qt S_in, and S = D (S + Kh^T V);
 //   one barrier.
 // The A tiles of chunk n are written by three waves and read by all four, so
