@@ -56,6 +56,7 @@
 // partition); one wave per (token, head) sums the token's k + 1 slots and
 // applies the router softmax Jacobian.  No atomics: every run gives the
 // same bits.
+#include <algorithm>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -533,9 +534,13 @@ struct ChSmem {
 
 }  // namespace
 
-// One block per checkpoint slot (a slot that holds no chunk exits at once):
-// the chunk's state operands are loaded as row blocks first, so that their
-// latency overlaps the record-side work, and as column blocks after it.
+// Persistent: block b runs the checkpoint slots b, b + G, b + 2G, ... (G =
+// the grid, as many blocks as are resident at once; a slot that holds no
+// chunk is skipped).  Each chunk's state operands are loaded as row blocks
+// first, so that their latency overlaps the record-side work, and as column
+// blocks after it; the next slot's record list is loaded during the current
+// chunk's row work and its rows during the current chunk's products, so a
+// chunk starts with its rows at hand.
 template <int CK, int DV, typename TIn>
 __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs a) {
     constexpr bool kBf = std::is_same<TIn, bf16_t>::value;   // bf16 MFMA for some products
@@ -548,16 +553,24 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
     static_assert(DV % 32 == 0, "column quarters of whole 8-column pieces");
     static_assert(CK % 32 == 0, "row quarters of whole 8-row k-steps");
     __shared__ SM sm;
-    // V[r][m] as fp32
-    auto vf = [&](int r, int m) -> float {
-        if constexpr (kBf)
-            return bf16_bits_to_f32(sm.v[r][m]);
-        else
-            return sm.v[r][m];
-    };
-    const int64_t x = blockIdx.x;
-    if (a.slot_meta[x * kBC].slot == kNoSlot) return;  // uniform: no chunk here
-    const int tid = threadIdx.x, lane = tid % kWave;
+    const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
+    const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
+    const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
+    const TIn* __restrict__ gl = static_cast<const TIn*>(a.la);
+    Row8<TIn> pq, pk, pl, pv;
+    Row8<float> pd;
+    const int64_t G = gridDim.x;
+    int cur = 0;        // record list of the current slot
+    bool have = false;  // its records are in LDS and its rows on their way
+    for (int64_t x = blockIdx.x; x < a.nslot; x += G) {
+    // the LDS struct through an opaque offset (zero) per slot, so that the
+    // compiler computes the operand addresses inside the iteration instead of
+    // hoisting all of them out of the loop and holding them in registers
+    int zo;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zo));
+    SM& sl = *reinterpret_cast<SM*>(reinterpret_cast<char*>(&sm) + zo);
+    // the thread's indices through the same offset, for the same reason
+    const int tid = (int)threadIdx.x + zo, lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, g4 = lane / 16;
     // bf16 MFMA operand over records from a record-major bf16 tile (row
@@ -568,11 +581,47 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         const int r = 8 * g4 + l16 / 4, c = c0 + 4 * (l16 % 4);
         return cat_tr(lds_tr(tile + r * stride + c), lds_tr(tile + (r + 4) * stride + c));
     };
-    const TIn* __restrict__ gq = static_cast<const TIn*>(a.q);
-    const TIn* __restrict__ gk = static_cast<const TIn*>(a.kl);
-    const TIn* __restrict__ gv = static_cast<const TIn*>(a.v);
-    const TIn* __restrict__ gl = static_cast<const TIn*>(a.la);
-    constexpr int cur = 0;
+    // this thread's 8-element pieces of the chunk's rows: q, key logits and
+    // log decay of record rk, columns jk..; v and do of record rv, columns mv..
+    const int rk = tid / (CK / 8), jk = 8 * (tid % (CK / 8));
+    const int rv = tid / (DV / 8), mv = 8 * (tid % (DV / 8));
+    // V[r][m] as fp32
+    auto vf = [&](int r, int m) -> float {
+        if constexpr (kBf)
+            return bf16_bits_to_f32(sl.v[r][m]);
+        else
+            return sl.v[r][m];
+    };
+    // record list b (0 or 1) of LDS
+    auto put_records = [&](int b, const BwdRec& m) {
+        sl.row[b][tid] = m.row;
+        sl.slot[b][tid] = m.slot;
+        sl.w[b][tid] = m.w;
+        sl.lnz[b][tid] = m.lnz;
+    };
+    auto load_rows = [&](int b) {
+        if (tid < kBC * CK / 8) {
+            const int64_t off = (int64_t)sl.row[b][rk] * CK + jk;
+            pq.load(gq + off);
+            pk.load(gk + off);
+            pl.load(gl + off);
+        }
+        if (tid < kBC * DV / 8) {
+            const int64_t off = (int64_t)sl.row[b][rv] * DV + mv;
+            pv.load(gv + off);
+            pd.load(a.dout + off);
+        }
+    };
+    if (!have) {
+        if (tid < kBC) put_records(cur, a.slot_meta[x * kBC + tid]);
+        __syncthreads();
+        if (sl.slot[cur][0] == kNoSlot) {  // uniform: no chunk here
+            __syncthreads();
+            continue;
+        }
+        load_rows(cur);
+    }
+    const int64_t xn = x + G;
 
     // ---- this wave's state operands.  Column block wv of S_in and G~ (the
     //      products that contract over state rows; loaded further down):
@@ -595,61 +644,44 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         }
     }
 
-    // ---- the chunk's records, then its rows (8-element pieces): Qt, K0 and
-    //      b start as q, key logits and log decay; padded records have no
-    //      decay, key or output gradient
-    if (tid < kBC) {
-        const BwdRec m = a.slot_meta[x * kBC + tid];
-        sm.row[cur][tid] = m.row;
-        sm.slot[cur][tid] = m.slot;
-        sm.w[cur][tid] = m.w;
-        sm.lnz[cur][tid] = m.lnz;
-    }
-    __syncthreads();
+    // ---- the chunk's rows (8-element pieces) into LDS: Qt, K0 and b start
+    //      as q, key logits and log decay; padded records have no decay, key
+    //      or output gradient
     {
-        const int rk = tid / (CK / 8), jk = 8 * (tid % (CK / 8));
-        const int rv = tid / (DV / 8), mv = 8 * (tid % (DV / 8));
         if (tid < kBC * CK / 8) {
-            Row8<TIn> pq, pk, pl;
-            const int64_t off = (int64_t)sm.row[cur][rk] * CK + jk;
-            pq.load(gq + off);
-            pk.load(gk + off);
-            pl.load(gl + off);
-            const bool ok = sm.slot[cur][rk] != kNoSlot;
+            const bool ok = sl.slot[cur][rk] != kNoSlot;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                sm.qt[rk][jk + i] = pq.get(i);
-                sm.k0[rk][jk + i] = pk.get(i);
-                sm.eb[rk][jk + i] = ok ? pl.get(i) : 0.f;
+                sl.qt[rk][jk + i] = pq.get(i);
+                sl.k0[rk][jk + i] = pk.get(i);
+                sl.eb[rk][jk + i] = ok ? pl.get(i) : 0.f;
             }
         }
         if (tid < kBC * DV / 8) {
-            Row8<TIn> pv;
-            Row8<float> pd;
-            const int64_t off = (int64_t)sm.row[cur][rv] * DV + mv;
-            pv.load(gv + off);
-            pd.load(a.dout + off);
-            const float wr = sm.w[cur][rv];
+            const float wr = sl.w[cur][rv];
             float gg[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 gg[i] = wr * pd.get(i);
-                sm.g[rv][mv + i] = gg[i];
+                sl.g[rv][mv + i] = gg[i];
             }
             if constexpr (kBf) {
-                *reinterpret_cast<uint4*>(&sm.v[rv][mv]) = pv.u;
+                *reinterpret_cast<uint4*>(&sl.v[rv][mv]) = pv.u;
                 uint32_t pr[4][2];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; e2++) split_pair<2>(gg[2 * e2], gg[2 * e2 + 1], pr[e2]);
-                *reinterpret_cast<uint4*>(&sm.gh[rv][mv]) = make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]);
-                *reinterpret_cast<uint4*>(&sm.gl[rv][mv]) = make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]);
+                *reinterpret_cast<uint4*>(&sl.gh[rv][mv]) = make_uint4(pr[0][0], pr[1][0], pr[2][0], pr[3][0]);
+                *reinterpret_cast<uint4*>(&sl.gl[rv][mv]) = make_uint4(pr[0][1], pr[1][1], pr[2][1], pr[3][1]);
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; i++) sm.v[rv][mv + i] = pv.get(i);
+                for (int i = 0; i < 8; i++) sl.v[rv][mv + i] = pv.get(i);
             }
         }
     }
     __syncthreads();
+    // the next slot's record list (written to LDS after the decay scan)
+    BwdRec mnext{};
+    if (tid < kBC && xn < a.nslot) mnext = a.slot_meta[xn * kBC + tid];
     // inclusive in-chunk cumulative log decay b: thread (group, state row j)
     // scans the BG records of its group in registers, then adds the totals
     // of the groups before it; the same thread forms Qt, K0 and e^b of its
@@ -662,37 +694,38 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < BG; i++) {
-            run += sm.eb[r0 + i][jb];
+            run += sl.eb[r0 + i][jb];
             bl[i] = run;
         }
-        sm.btot[grp][jb] = run;
+        sl.btot[grp][jb] = run;
         __syncthreads();
         float pre = 0.f;
-        for (int g2 = 0; g2 < grp; g2++) pre += sm.btot[g2][jb];
-        if (grp == NG - 1) sm.ebc[jb] = expf(pre + run);
+        for (int g2 = 0; g2 < grp; g2++) pre += sl.btot[g2][jb];
+        if (grp == NG - 1) sl.ebc[jb] = expf(pre + run);
 #pragma unroll
         for (int i = 0; i < BG; i++) {
             const int r = r0 + i;
             const float b = pre + bl[i];
             const float e = expf(b);
-            const float qv = sm.qt[r][jb] * e;
-            const float kv = sm.slot[cur][r] != kNoSlot
-                                 ? __builtin_amdgcn_exp2f((sm.k0[r][jb] - b) * kLog2e - sm.lnz[cur][r])
+            const float qv = sl.qt[r][jb] * e;
+            const float kv = sl.slot[cur][r] != kNoSlot
+                                 ? __builtin_amdgcn_exp2f((sl.k0[r][jb] - b) * kLog2e - sl.lnz[cur][r])
                                  : 0.f;
-            sm.qt[r][jb] = qv;
-            sm.k0[r][jb] = kv;
-            sm.eb[r][jb] = e;
+            sl.qt[r][jb] = qv;
+            sl.k0[r][jb] = kv;
+            sl.eb[r][jb] = e;
             if constexpr (kBf) {
                 uint16_t tq[2], tk[2];
                 split_levels<2>(qv, tq);
-                split_levels<2>(sm.w[cur][r] * kv, tk);
-                sm.qh[r][jb] = tq[0];
-                sm.ql[r][jb] = tq[1];
-                sm.kh[r][jb] = tk[0];
-                sm.kl[r][jb] = tk[1];
+                split_levels<2>(sl.w[cur][r] * kv, tk);
+                sl.qh[r][jb] = tq[0];
+                sl.ql[r][jb] = tq[1];
+                sl.kh[r][jb] = tk[0];
+                sl.kl[r][jb] = tk[1];
             }
         }
     }
+    if (tid < kBC && xn < a.nslot) put_records(cur ^ 1, mnext);
     __syncthreads();
 
     // the column blocks of S_in and G~ (issued here, after the record-side
@@ -723,10 +756,10 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int t = 0; t < CK / 32; t++) {
                     const int j0 = 32 * t + 8 * g4;
-                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sm.qh[ra][j0]);
-                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sm.ql[ra][j0]);
-                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sm.kh[sb][j0]);
-                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sm.kl[sb][j0]);
+                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sl.qh[ra][j0]);
+                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sl.ql[ra][j0]);
+                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sl.kh[sb][j0]);
+                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sl.kl[sb][j0]);
                     acc = mfma16(qhi, khi, acc);
                     acc = mfma16(qhi, klo, acc);
                     acc = mfma16(qlo, khi, acc);
@@ -735,9 +768,9 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int t = 0; t < DV / 32; t++) {
                     const int m0 = 32 * t + 8 * g4;
-                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sm.gh[ra][m0]);
-                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sm.gl[ra][m0]);
-                    const u16x8 vb = *reinterpret_cast<const u16x8*>(&sm.v[sb][m0]);
+                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sl.gh[ra][m0]);
+                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sl.gl[ra][m0]);
+                    const u16x8 vb = *reinterpret_cast<const u16x8*>(&sl.v[sb][m0]);
                     acc = mfma16(ghi, vb, acc);
                     acc = mfma16(glo, vb, acc);
                 }
@@ -745,12 +778,12 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         } else if (isA) {
             for (int ks = 0; ks < CK / 4; ks++) {
                 const int j = 4 * ks + g4;
-                acc = mf(sm.qt[16 * rt + l16][j], sm.w[cur][16 * st + l16] * sm.k0[16 * st + l16][j], acc);
+                acc = mf(sl.qt[16 * rt + l16][j], sl.w[cur][16 * st + l16] * sl.k0[16 * st + l16][j], acc);
             }
         } else {
             for (int ks = 0; ks < DV / 4; ks++) {
                 const int m = 4 * ks + g4;
-                acc = mf(sm.g[16 * rt + l16][m], vf(16 * st + l16, m), acc);
+                acc = mf(sl.g[16 * rt + l16][m], vf(16 * st + l16, m), acc);
             }
         }
 #pragma unroll
@@ -760,20 +793,20 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             if constexpr (kBf) {
                 uint16_t tv[2];
                 split_levels<2>(val, tv);
-                (isA ? sm.ah : sm.gvh)[r][s] = tv[0];
-                (isA ? sm.al : sm.gvl)[r][s] = tv[1];
+                (isA ? sl.ah : sl.gvh)[r][s] = tv[0];
+                (isA ? sl.al : sl.gvl)[r][s] = tv[1];
             } else {
-                (isA ? sm.A : sm.GV)[r][s] = val;
+                (isA ? sl.A : sl.GV)[r][s] = val;
             }
         }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             if constexpr (kBf) {
-                (wv == 6 ? sm.ah : sm.gvh)[4 * g4 + e][16 + l16] = 0;
-                (wv == 6 ? sm.al : sm.gvl)[4 * g4 + e][16 + l16] = 0;
+                (wv == 6 ? sl.ah : sl.gvh)[4 * g4 + e][16 + l16] = 0;
+                (wv == 6 ? sl.al : sl.gvl)[4 * g4 + e][16 + l16] = 0;
             } else {
-                (wv == 6 ? sm.A : sm.GV)[4 * g4 + e][16 + l16] = 0.f;
+                (wv == 6 ? sl.A : sl.GV)[4 * g4 + e][16 + l16] = 0.f;
             }
         }
     }
@@ -802,18 +835,18 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int e2 = 0; e2 < 4; e2++) {
                     split_pair<2>(sc[8 * t + 2 * e2], sc[8 * t + 2 * e2 + 1], ps[e2]);
-                    split_pair<2>(sm.ebc[j0 + 2 * e2] * gc[8 * t + 2 * e2],
-                                  sm.ebc[j0 + 2 * e2 + 1] * gc[8 * t + 2 * e2 + 1], pg[e2]);
+                    split_pair<2>(sl.ebc[j0 + 2 * e2] * gc[8 * t + 2 * e2],
+                                  sl.ebc[j0 + 2 * e2 + 1] * gc[8 * t + 2 * e2 + 1], pg[e2]);
                 }
                 const u16x8 shi = pack8(ps, 0), slo = pack8(ps, 1);
                 const u16x8 ghi = pack8(pg, 0), glo = pack8(pg, 1);
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int r = 16 * rt + l16;
-                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sm.qh[r][j0]);
-                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sm.ql[r][j0]);
-                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sm.kh[r][j0]);
-                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sm.kl[r][j0]);
+                    const u16x8 qhi = *reinterpret_cast<const u16x8*>(&sl.qh[r][j0]);
+                    const u16x8 qlo = *reinterpret_cast<const u16x8*>(&sl.ql[r][j0]);
+                    const u16x8 khi = *reinterpret_cast<const u16x8*>(&sl.kh[r][j0]);
+                    const u16x8 klo = *reinterpret_cast<const u16x8*>(&sl.kl[r][j0]);
                     y[rt] = mfma16(qhi, shi, y[rt]);
                     y[rt] = mfma16(qhi, slo, y[rt]);
                     y[rt] = mfma16(qlo, shi, y[rt]);
@@ -827,12 +860,12 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             for (int ks = 0; ks < NKC; ks++) {
                 const int jj = g4 * NKC + ks;
                 const float bs = sc[ks];
-                const float bg = sm.ebc[jj] * gc[ks];
+                const float bg = sl.ebc[jj] * gc[ks];
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int r = 16 * rt + l16;
-                    y[rt] = mf(sm.qt[r][jj], bs, y[rt]);
-                    dv[rt] = mf(sm.w[cur][r] * sm.k0[r][jj], bg, dv[rt]);
+                    y[rt] = mf(sl.qt[r][jj], bs, y[rt]);
+                    dv[rt] = mf(sl.w[cur][r] * sl.k0[r][jj], bg, dv[rt]);
                 }
             }
         }
@@ -840,15 +873,15 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         if constexpr (kBf) {
             // the chunk's 32 records as one bf16 k-step: A rows from the
             // split tiles, A^T, V and g columns by transpose reads
-            const u16x8 vb = tr16(&sm.v[0][0], SM::VRS, 16 * wv);
-            const u16x8 gbh = tr16(&sm.gh[0][0], DV + 8, 16 * wv);
-            const u16x8 gbl = tr16(&sm.gl[0][0], DV + 8, 16 * wv);
+            const u16x8 vb = tr16(&sl.v[0][0], SM::VRS, 16 * wv);
+            const u16x8 gbh = tr16(&sl.gh[0][0], DV + 8, 16 * wv);
+            const u16x8 gbl = tr16(&sl.gl[0][0], DV + 8, 16 * wv);
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
-                const u16x8 ahi = lds8(&sm.ah[16 * rt + l16][8 * g4]);
-                const u16x8 alo = lds8(&sm.al[16 * rt + l16][8 * g4]);
-                const u16x8 athi = tr16(&sm.ah[0][0], kBC + 8, 16 * rt);
-                const u16x8 atlo = tr16(&sm.al[0][0], kBC + 8, 16 * rt);
+                const u16x8 ahi = lds8(&sl.ah[16 * rt + l16][8 * g4]);
+                const u16x8 alo = lds8(&sl.al[16 * rt + l16][8 * g4]);
+                const u16x8 athi = tr16(&sl.ah[0][0], kBC + 8, 16 * rt);
+                const u16x8 atlo = tr16(&sl.al[0][0], kBC + 8, 16 * rt);
                 y[rt] = mfma16(ahi, vb, y[rt]);
                 y[rt] = mfma16(alo, vb, y[rt]);
                 dv[rt] = mfma16(athi, gbh, dv[rt]);
@@ -861,8 +894,8 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
                 const int s = 4 * ks + g4;
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
-                    y[rt] = mf(sm.A[16 * rt + l16][s], vf(s, m), y[rt]);
-                    dv[rt] = mf(sm.A[s][16 * rt + l16], sm.g[s][m], dv[rt]);
+                    y[rt] = mf(sl.A[16 * rt + l16][s], vf(s, m), y[rt]);
+                    dv[rt] = mf(sl.A[s][16 * rt + l16], sl.g[s][m], dv[rt]);
                 }
             }
         }
@@ -871,10 +904,15 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 16 * rt + 4 * g4 + e;
-                if (sm.slot[cur][r] != kNoSlot) a.g_dv[(int64_t)sm.slot[cur][r] * DV + m] = dv[rt][e];
-                yg[rt][e] = y[rt][e] * sm.g[r][m];
+                if (sl.slot[cur][r] != kNoSlot) a.g_dv[(int64_t)sl.slot[cur][r] * DV + m] = dv[rt][e];
+                yg[rt][e] = y[rt][e] * sl.g[r][m];
             }
     }
+
+    // the next slot's rows, loading while this chunk's c-side products run
+    // (issued here, when the column blocks' registers are free)
+    have = xn < a.nslot && sl.slot[cur ^ 1][0] != kNoSlot;
+    if (have) load_rows(cur ^ 1);
 
     // ---- c-side outputs of row block wv: dQt, dKh, the chunk decay term,
     //      dlog_alpha and dq
@@ -885,7 +923,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         f32x4b dq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4b vg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4b dk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const float ebj = sm.ebc[j];
+        const float ebj = sl.ebc[j];
         float sg = 0.f;   // this lane's part of rowsum(S_in . G~) of row j
         // over the columns m = g4 DV/4 + ks: dQt += g S_in^T, V G~^T
 #pragma unroll
@@ -898,8 +936,8 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int r = 16 * rt + l16;
-                    dq[rt] = mf(sm.g[r][mm], st, dq[rt]);
-                    vg[rt] = mf(sm.v[r][mm], gt, vg[rt]);
+                    dq[rt] = mf(sl.g[r][mm], st, dq[rt]);
+                    vg[rt] = mf(sl.v[r][mm], gt, vg[rt]);
                 }
             }
         }
@@ -926,9 +964,9 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int r = 16 * rt + l16;
-                    const u16x8 va = *reinterpret_cast<const u16x8*>(&sm.v[r][m0]);
-                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sm.gh[r][m0]);
-                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sm.gl[r][m0]);
+                    const u16x8 va = *reinterpret_cast<const u16x8*>(&sl.v[r][m0]);
+                    const u16x8 ghi = *reinterpret_cast<const u16x8*>(&sl.gh[r][m0]);
+                    const u16x8 glo = *reinterpret_cast<const u16x8*>(&sl.gl[r][m0]);
                     vg[rt] = mfma16(va, gthi, vg[rt]);
                     vg[rt] = mfma16(va, gtlo, vg[rt]);
                     dq[rt] = mfma16(ghi, shi, dq[rt]);
@@ -939,16 +977,16 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         }
         // over records s: dQt += GV Kh, dKh += GV^T Qt
         if constexpr (kBf) {
-            const u16x8 kbh = tr16(&sm.kh[0][0], CK + 8, 16 * wv);
-            const u16x8 kbl = tr16(&sm.kl[0][0], CK + 8, 16 * wv);
-            const u16x8 qbh = tr16(&sm.qh[0][0], CK + 8, 16 * wv);
-            const u16x8 qbl = tr16(&sm.ql[0][0], CK + 8, 16 * wv);
+            const u16x8 kbh = tr16(&sl.kh[0][0], CK + 8, 16 * wv);
+            const u16x8 kbl = tr16(&sl.kl[0][0], CK + 8, 16 * wv);
+            const u16x8 qbh = tr16(&sl.qh[0][0], CK + 8, 16 * wv);
+            const u16x8 qbl = tr16(&sl.ql[0][0], CK + 8, 16 * wv);
 #pragma unroll
             for (int rt = 0; rt < 2; rt++) {
-                const u16x8 ghi = lds8(&sm.gvh[16 * rt + l16][8 * g4]);
-                const u16x8 glo = lds8(&sm.gvl[16 * rt + l16][8 * g4]);
-                const u16x8 gthi = tr16(&sm.gvh[0][0], kBC + 8, 16 * rt);
-                const u16x8 gtlo = tr16(&sm.gvl[0][0], kBC + 8, 16 * rt);
+                const u16x8 ghi = lds8(&sl.gvh[16 * rt + l16][8 * g4]);
+                const u16x8 glo = lds8(&sl.gvl[16 * rt + l16][8 * g4]);
+                const u16x8 gthi = tr16(&sl.gvh[0][0], kBC + 8, 16 * rt);
+                const u16x8 gtlo = tr16(&sl.gvl[0][0], kBC + 8, 16 * rt);
                 dq[rt] = mfma16(ghi, kbh, dq[rt]);
                 dq[rt] = mfma16(ghi, kbl, dq[rt]);
                 dq[rt] = mfma16(glo, kbh, dq[rt]);
@@ -962,8 +1000,8 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
                 const int s = 4 * ks + g4;
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
-                    dq[rt] = mf(sm.GV[16 * rt + l16][s], sm.w[cur][s] * sm.k0[s][j], dq[rt]);
-                    dk[rt] = mf(sm.GV[s][16 * rt + l16], sm.qt[s][j], dk[rt]);
+                    dq[rt] = mf(sl.GV[16 * rt + l16][s], sl.w[cur][s] * sl.k0[s][j], dq[rt]);
+                    dk[rt] = mf(sl.GV[s][16 * rt + l16], sl.qt[s][j], dk[rt]);
                 }
             }
         }
@@ -975,7 +1013,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int s = 16 * rt + 4 * g4 + e;
-                t2 += sm.w[cur][s] * sm.k0[s][j] * vg[rt][e];
+                t2 += sl.w[cur][s] * sl.k0[s][j] * vg[rt][e];
             }
         float tj = sg + t2;
         tj += __shfl_xor(tj, 16, kWave);
@@ -991,9 +1029,9 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             for (int e = 3; e >= 0; e--) {
                 const int s = 16 * rt + 4 * g4 + e;
                 dkh[rt][e] = vg[rt][e] + dk[rt][e];
-                run += sm.qt[s][j] * dq[rt][e] - sm.w[cur][s] * sm.k0[s][j] * dkh[rt][e];
+                run += sl.qt[s][j] * dq[rt][e] - sl.w[cur][s] * sl.k0[s][j] * dkh[rt][e];
                 db[rt][e] = run;
-                kd[rt][e] = sm.k0[s][j] * dkh[rt][e];
+                kd[rt][e] = sl.k0[s][j] * dkh[rt][e];
             }
             tot[rt] = run;
         }
@@ -1012,10 +1050,10 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int s = 16 * rt + 4 * g4 + e;
-                if (sm.slot[cur][s] != kNoSlot) {
-                    const int64_t o = (int64_t)sm.slot[cur][s] * CK + j;
+                if (sl.slot[cur][s] != kNoSlot) {
+                    const int64_t o = (int64_t)sl.slot[cur][s] * CK + j;
                     a.g_dla[o] = db[rt][e] + above[rt] + (rt == 0 ? all1 : 0.f) + tj;
-                    a.g_dq[o] = dq[rt][e] * sm.eb[s][j];
+                    a.g_dq[o] = dq[rt][e] * sl.eb[s][j];
                 }
             }
     }
@@ -1026,8 +1064,8 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             const float x1 = row_reduce<16>(yg[rt][e], [](float p, float o) { return p + o; });
             const float x2 = row_reduce<16>(kd[rt][e], [](float p, float o) { return p + o; });
             if (l16 == 0) {
-                sm.dwp[wv][16 * rt + 4 * g4 + e] = x1;
-                sm.kdp[wv][16 * rt + 4 * g4 + e] = x2;
+                sl.dwp[wv][16 * rt + 4 * g4 + e] = x1;
+                sl.kdp[wv][16 * rt + 4 * g4 + e] = x2;
             }
         }
     __syncthreads();
@@ -1040,25 +1078,30 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int s = 16 * rt + 4 * g4 + e;
-                if (sm.slot[cur][s] != kNoSlot) {
+                if (sl.slot[cur][s] != kNoSlot) {
                     float kds = 0.f;
 #pragma unroll
-                    for (int w2 = 0; w2 < kCW; w2++) kds += sm.kdp[w2][s];
-                    a.g_dkl[(int64_t)sm.slot[cur][s] * CK + j] =
-                        sm.w[cur][s] * sm.k0[s][j] * (dkh[rt][e] - sm.eb[s][j] * kds);
+                    for (int w2 = 0; w2 < kCW; w2++) kds += sl.kdp[w2][s];
+                    a.g_dkl[(int64_t)sl.slot[cur][s] * CK + j] =
+                        sl.w[cur][s] * sl.k0[s][j] * (dkh[rt][e] - sl.eb[s][j] * kds);
                 }
             }
     }
-    if (tid < kBC && sm.slot[cur][tid] != kNoSlot) {
+    if (tid < kBC && sl.slot[cur][tid] != kNoSlot) {
         float yg2 = 0.f, kds = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < kCW; w2++) {
-            yg2 += sm.dwp[w2][tid];
-            kds += sm.kdp[w2][tid];
+            yg2 += sl.dwp[w2][tid];
+            kds += sl.kdp[w2][tid];
         }
         // y . do = (y . g) / w; a gate of zero has no gradient through e
-        const float wr = sm.w[cur][tid];
-        a.g_dw[sm.slot[cur][tid]] = (wr > 0.f ? yg2 / wr : 0.f) + kds;
+        const float wr = sl.w[cur][tid];
+        a.g_dw[sl.slot[cur][tid]] = (wr > 0.f ? yg2 / wr : 0.f) + kds;
+    }
+    // every read of this chunk's LDS is done before the next chunk's rows
+    // and records overwrite it
+    __syncthreads();
+    cur ^= 1;
     }
 }
 
@@ -1114,7 +1157,21 @@ void launch_bwd_cfg(const BwdArgs& a, hipStream_t st) {
     const int64_t nseg = (int64_t)a.num_seqs * a.H * (a.N + 1);
     if (nseg == 0) return;
     bwd_sweep_kernel<CK, DV, TIn><<<(unsigned)(2 * nseg), sweep_waves<CK, DV>() * kWave, 0, st>>>(a);
-    if (a.nslot > 0) bwd_chunk_kernel<CK, DV, TIn><<<(unsigned)a.nslot, kCW * kWave, 0, st>>>(a);
+    if (a.nslot > 0) {
+        // as many chunk blocks as the device holds at once (each walks the
+        // slots b, b + grid, ...)
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_chunk_kernel<CK, DV, TIn>, kCW * kWave,
+                                                         0) != hipSuccess ||
+            cus < 1 || per_cu < 1) {
+            cus = 256;
+            per_cu = 1;
+        }
+        const int64_t grid = std::min<int64_t>(a.nslot, (int64_t)cus * per_cu);
+        bwd_chunk_kernel<CK, DV, TIn><<<(unsigned)grid, kCW * kWave, 0, st>>>(a);
+    }
 }
 
 template <typename TIn>
