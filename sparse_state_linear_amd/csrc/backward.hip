@@ -257,7 +257,8 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
         }
 
         // Pipelined over chunks: the record list of chunk ci + 3 and the rows
-        // of chunk ci + 1 are loaded while chunk ci is prepared and multiplied.
+        // of chunk ci + 2 are loaded while chunk ci is prepared and multiplied
+        // (the rows into the register set chunk ci's rows just left).
         constexpr int NT = kSW * kWave;
         static_assert(kBC * CK / 8 <= NT && kBC * DV / 8 <= NT, "one 8-element piece per thread");
         auto order = [&](int64_t ci) { return REV ? nch - 1 - ci : ci; };
@@ -298,30 +299,36 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
         const int rk = tid / (CK / 8), jk = 8 * (tid % (CK / 8));
         const int rv = tid / (DV / 8), mv = 8 * (tid % (DV / 8));
         const bool kpiece = tid < kBC * CK / 8, vpiece = tid < kBC * DV / 8;
-        Row8<TIn> px, pl, pv;
-        Row8<float> pd;
-        auto rows = [&](int64_t ci) {
+        Row8<TIn> px[2], pl[2], pv[2];
+        Row8<float> pd[2];
+        auto rows = [&](int64_t ci, auto SI) {
+            constexpr int S = decltype(SI)::value;
             const int p = (int)(ci % 3);
             if (kpiece) {
                 const int64_t off = (int64_t)sm.row[p][rk] * CK + jk;
-                px.load((REV ? gq : gk) + off);
-                pl.load(gl + off);
+                px[S].load((REV ? gq : gk) + off);
+                pl[S].load(gl + off);
             }
             if (vpiece) {
                 const int64_t off = (int64_t)sm.row[p][rv] * DV + mv;
                 if constexpr (REV)
-                    pd.load(a.dout + off);
+                    pd[S].load(a.dout + off);
                 else
-                    pv.load(gv + off);
+                    pv[S].load(gv + off);
             }
         };
+        const std::integral_constant<int, 0> I0{};
+        const std::integral_constant<int, 1> I1{};
         if (nch > 0) meta(0);
         if (nch > 1) meta(1);
         if (nch > 2) meta_load(2);
         __syncthreads();
-        if (nch > 0) rows(0);
+        if (nch > 0) rows(0, I0);
+        if (nch > 1) rows(1, I1);
 
-        for (int64_t ci = 0; ci < nch; ci++) {
+        // chunk ci, its rows in register set S = ci % 2
+        auto step = [&](int64_t ci, auto SI) {
+            constexpr int S = decltype(SI)::value;
             const int64_t c = order(ci);
             const int p = (int)(ci % 3);
             __syncthreads();   // the previous chunk's products are done with x, y
@@ -330,18 +337,18 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                 const bool ok = sm.valid[p][rk] != 0;
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    sm.x[rk][jk + i] = px.get(i);
-                    sm.la[rk][jk + i] = ok ? pl.get(i) : 0.f;
+                    sm.x[rk][jk + i] = px[S].get(i);
+                    sm.la[rk][jk + i] = ok ? pl[S].get(i) : 0.f;
                 }
             }
             if (vpiece) {
                 const float wr = sm.w[p][rv];
 #pragma unroll
-                for (int i = 0; i < 8; i++) sm.y[rv][mv + i] = REV ? wr * pd.get(i) : pv.get(i);
+                for (int i = 0; i < 8; i++) sm.y[rv][mv + i] = REV ? wr * pd[S].get(i) : pv[S].get(i);
             }
             if (ci + 2 < nch) meta_store(ci + 2);
             __syncthreads();
-            if (ci + 1 < nch) rows(ci + 1);
+            if (ci + 2 < nch) rows(ci + 2, SI);
             if (ci + 3 < nch) meta_load(ci + 3);
             // in-chunk sums of the log decay: forward the suffix sums
             // b_C - b_r, reverse the inclusive prefix sums b_r.  Thread
@@ -470,7 +477,13 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                     }
                 }
             }
+        };
+        int64_t ci = 0;
+        for (; ci + 1 < nch; ci += 2) {
+            step(ci, I0);
+            step(ci + 1, I1);
         }
+        if (ci < nch) step(ci, I0);
         // the reverse sweep's last G is the gradient of the initial state
         if (REV && a.dinit) {
 #pragma unroll
