@@ -167,3 +167,14 @@ def test_backward_main_full_size():
         e = rel_err_big(got[name], ref[name])
         print(f"  {name} rel err {e:.3e}", flush=True)
         assert e <= BWD_TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("dtype,c,d", [("bf16", 64, 64), ("f32", 32, 32)])
+def test_backward_many_slots(dtype, c, d):
+    """N = 64, k = 8 over 2,200 tokens: about 1,500 chunk slots, far more
+    than the chunk pass's resident blocks, many of them empty (the spare
+    slot after each of the 256 routed segments), so every block walks
+    several slots, prefetching the next one's records and rows, and skips
+    empty ones on the way."""
+    w = si.Workload(f"bwd_many_slots_{dtype}", dtype, H=2, c=c, d=d, N=64, topk=8)
+    _check(w, [1500, 700], seed=790 + c)
