@@ -31,8 +31,9 @@
 //
 // Launch 1 (sweeps): one block per segment and direction.  The forward
 // sweep carries S from the initial state and stores S_in of every chunk;
-// the reverse sweep carries G from dS_final and stores the G of every chunk,
-// and its last G is the gradient of the segment's initial state.  A step is
+// the reverse sweep carries G from dS_final and stores G~ = D G of every
+// chunk (the form the chunk launch uses), and its last G is the gradient of
+// the segment's initial state.  A step is
 // one c x C by C x d product into the carried state tiles (registers), on
 // fp32 MFMA (16x16x4) for fp32 inputs and on bf16 MFMA for bf16 inputs (the
 // chunk's 32 records as one k-step; the A side in two bf16 terms, the B side
@@ -418,8 +419,9 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
                 }
             }
             __syncthreads();
-            // store the carried state (S_in of chunk c, or the G after chunk
-            // c), then X = D X + x^T y
+            // store the carried state (S_in of chunk c, or D G with G the
+            // gradient after chunk c: the only form the chunk launch uses),
+            // then X = D X + x^T y
             float* ck = (REV ? a.ckG : a.ckS) + (q.base + c) * (int64_t)(CK * DV);
 #pragma unroll
             for (int i = 0; i < TPW; i++) {
@@ -428,8 +430,9 @@ __global__ __launch_bounds__((sweep_waves<CK, DV>() * kWave)) void bwd_sweep_ker
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int j = 16 * jt + 4 * g4 + e;
+                    if constexpr (REV) X[i][e] *= sm.ebc[j];
                     ck[(int64_t)j * DV + 16 * mt + l16] = X[i][e];
-                    X[i][e] *= sm.ebc[j];
+                    if constexpr (!REV) X[i][e] *= sm.ebc[j];
                 }
             }
             if constexpr (kBf) {
@@ -520,7 +523,6 @@ struct ChSmem {
     float g[kBC][VS];            // g = w do
     float A[NF][lds_stride(kBC)];     // A (masked), fp32 inputs
     float GV[NF][lds_stride(kBC)];    // GV (masked), fp32 inputs
-    float ebc[CK];               // e^{b_C}
     float btot[kCW * kWave / CK][CK];   // per record group: its total of the log decay
     float dwp[kCW][kBC];         // per-wave partials of y . g
     float kdp[kCW][kBC];         // per-wave partials of K0 . dKh
@@ -714,7 +716,6 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         __syncthreads();
         float pre = 0.f;
         for (int g2 = 0; g2 < grp; g2++) pre += sl.btot[g2][jb];
-        if (grp == NG - 1) sl.ebc[jb] = expf(pre + run);
 #pragma unroll
         for (int i = 0; i < BG; i++) {
             const int r = r0 + i;
@@ -848,8 +849,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
 #pragma unroll
                 for (int e2 = 0; e2 < 4; e2++) {
                     split_pair<2>(sc[8 * t + 2 * e2], sc[8 * t + 2 * e2 + 1], ps[e2]);
-                    split_pair<2>(sl.ebc[j0 + 2 * e2] * gc[8 * t + 2 * e2],
-                                  sl.ebc[j0 + 2 * e2 + 1] * gc[8 * t + 2 * e2 + 1], pg[e2]);
+                    split_pair<2>(gc[8 * t + 2 * e2], gc[8 * t + 2 * e2 + 1], pg[e2]);
                 }
                 const u16x8 shi = pack8(ps, 0), slo = pack8(ps, 1);
                 const u16x8 ghi = pack8(pg, 0), glo = pack8(pg, 1);
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
             for (int ks = 0; ks < NKC; ks++) {
                 const int jj = g4 * NKC + ks;
                 const float bs = sc[ks];
-                const float bg = sl.ebc[jj] * gc[ks];
+                const float bg = gc[ks];
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int r = 16 * rt + l16;
@@ -936,14 +936,13 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
         f32x4b dq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4b vg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4b dk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const float ebj = sl.ebc[j];
         float sg = 0.f;   // this lane's part of rowsum(S_in . G~) of row j
         // over the columns m = g4 DV/4 + ks: dQt += g S_in^T, V G~^T
 #pragma unroll
         for (int ks = 0; ks < NKD; ks++) {
             const int mm = g4 * NKD + ks;
             const float st = sr[ks];
-            const float gt = ebj * gr[ks];
+            const float gt = gr[ks];
             sg += st * gt;
             if constexpr (!kBf) {
 #pragma unroll
@@ -969,7 +968,7 @@ __global__ __launch_bounds__(kCW * kWave, 1) void bwd_chunk_kernel(const BwdArgs
                 uint32_t pg[4][2], ps[4][2];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; e2++) {
-                    split_pair<2>(ebj * gr[8 * t + 2 * e2], ebj * gr[8 * t + 2 * e2 + 1], pg[e2]);
+                    split_pair<2>(gr[8 * t + 2 * e2], gr[8 * t + 2 * e2 + 1], pg[e2]);
                     split_pair<2>(sr[8 * t + 2 * e2], sr[8 * t + 2 * e2 + 1], ps[e2]);
                 }
                 const u16x8 gthi = pack8(pg, 0), gtlo = pack8(pg, 1);

@@ -177,7 +177,8 @@ struct BwdArgs {
     const float* dfinal;          // gradient of the final states, or null
     const float* dout;            // [T, H, d] gradient of o
     float* ckS;                   // [nslot, c, d] state at the start of each chunk
-    float* ckG;                   // [nslot, c, d] state gradient after each chunk
+    float* ckG;                   // [nslot, c, d] D G: the state gradient after each
+                                  // chunk times the chunk's decay diag(e^{b_C})
     BwdRec* slot_meta;            // [nslot, 32] the records of each slot's chunk
     int64_t nslot, sh_slots;      // slots in all; slots of the shared chains
     float *g_dq, *g_dkl, *g_dla;  // per-record slots [T*H*(topk+1), c]
