@@ -113,13 +113,15 @@ def test_backward_without_init_or_dfinal():
     _check(w, [600, 90], seed=730, with_init=False, with_dfinal=False)
 
 
-def test_backward_gate_limit():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_gate_limit(dtype):
     """log_alpha = -1.24 on every row (strong decay near the documented
     limit)."""
-    w = si.Workload("bwd_gate", "bf16", H=2, c=64, d=64, N=4, topk=2)
+    w = si.Workload(f"bwd_gate_{dtype}", dtype, H=2, c=64, d=64, N=4, topk=2)
     lengths = [400, 61]
     inp = si.forward_inputs(w, lengths=lengths, seed=740)
-    inp["log_alpha"] = si.f32_to_bf16_bits(np.full(inp["log_alpha"].shape, -1.24, np.float32))
+    la = np.full(inp["log_alpha"].shape, -1.24, np.float32)
+    inp["log_alpha"] = si.f32_to_bf16_bits(la) if dtype == "bf16" else la
     _check(w, lengths, 740, inp=inp)
 
 
