@@ -79,8 +79,16 @@ def chunk_flops(records, c, d, C=64):
     return records * 2 * (C * c / 2 + C * d / 2 + 2 * c * d)
 
 
-def run_forward(args, w, si, sse, torch, inp=None, schedule=None):
-    """Time sse_forward (or sse_forward_ex with the given schedule) on w."""
+def run_forward(args, w, si, sse, torch, inp=None, schedule=None, step_stats=None, prewarm_s=0.0):
+    """Time sse_forward (or sse_forward_ex with the given schedule) on w.
+    With prewarm_s > 0, forwards run untimed for that long before the
+    warm-up steps: on a GPU that has been idle the first forwards run about
+    10 % slower (3 warm-up forwards: 0.87 ms per timed step on the main
+    workload; 30: 0.78), so the timed window would otherwise measure the
+    clock ramp rather than the steady state.
+    With a dict `step_stats`, also time `args.steps` more calls one by one
+    (an event pair around each, after the timed window) and put their
+    median, min and max in it."""
     if inp is None:
         inp = si.forward_inputs(w)
     cu = inp["cu_seqlens"]
@@ -102,6 +110,12 @@ def run_forward(args, w, si, sse, torch, inp=None, schedule=None):
             sse.sse_forward_ex(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"],
                                max_len, schedule=schedule, o=o, final_states=fs, workspace=ws)
 
+    if prewarm_s > 0:
+        t_end = time.perf_counter() + prewarm_s
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -120,6 +134,17 @@ def run_forward(args, w, si, sse, torch, inp=None, schedule=None):
         step()
     stages, calls = sse.sse_trace_read()
     sse.sse_trace_enable(False)
+    if step_stats is not None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) for a, b in ev)
+        step_stats.update({"median": per[len(per) // 2], "min": per[0], "max": per[-1],
+                           "calls": len(per)})
     return T, S, total_ms, {k: v / max(calls, 1) for k, v in stages.items()}, calls
 
 
@@ -459,7 +484,9 @@ def main():
         print(json.dumps({"only": args.only, **rec}), flush=True)
         return
     log("forward", w.notes)
-    T, S, total_ms, stages, calls = run_forward(args, w, si, sse, torch)
+    step_stats = {}
+    T, S, total_ms, stages, calls = run_forward(args, w, si, sse, torch, step_stats=step_stats,
+                                                prewarm_s=0.3)
     ms = total_ms / args.steps
     tokens_per_s = T / (ms * 1e-3)
     # dominant kernel: the routed pass (k of the k+1 partition reads)
@@ -585,6 +612,7 @@ def main():
             "stage_ms": stages,
             "traced_calls": calls,
         },
+        "step_ms": step_stats,
         "varlen_forward": varlen,
         "measured_peaks": peaks,
         "decode": decode,
