@@ -180,3 +180,23 @@ def test_backward_many_slots(dtype, c, d):
     empty ones on the way."""
     w = si.Workload(f"bwd_many_slots_{dtype}", dtype, H=2, c=c, d=d, N=64, topk=8)
     _check(w, [1500, 700], seed=790 + c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_all_sequences_empty(dtype):
+    """Every sequence empty: no records, every chunk slot empty.  The
+    initial-state gradient is d_final_states passed through unchanged (bit
+    for bit, as the oracle gives), and the token gradients are empty."""
+    w = si.Workload(f"bwd_empty_{dtype}", dtype, H=2, c=64, d=64, N=8, topk=2)
+    lengths = [0, 0]
+    inp = si.forward_inputs(w, lengths=lengths, seed=795)
+    do, dfin, init = _grad_inputs(w, lengths, 795)
+    announce(w.name, "lengths", lengths, "sse_backward")
+    got = _run(inp, w, do, dfin, init)
+    ref = oracle.backward(*(inp[n] for n in NAMES), inp["cu_seqlens"], w.N, w.topk,
+                          do.astype(np.float64), dfinal_states=dfin.astype(np.float64),
+                          initial_states=init.astype(np.float64), threads=oracle_threads())
+    for name in GRADS[:-1]:
+        assert got[name].size == 0 and ref[name].size == 0, name
+    assert np.array_equal(ref["dinitial_states"], dfin.astype(np.float64))
+    assert np.array_equal(got["dinitial_states"].view(np.uint32), dfin.view(np.uint32))

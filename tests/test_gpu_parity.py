@@ -301,6 +301,25 @@ def test_initial_states_and_unselected_partition():
     assert np.array_equal(got["fs"][:, :, 7].view(np.uint32), init[:, :, 7].view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_all_sequences_empty(dtype):
+    """Every sequence empty: o is empty and every final state equals its
+    initial state byte for byte (each partition keeps an identity
+    transition)."""
+    w = si.Workload(f"fwd_empty_{dtype}", dtype, H=2, c=64, d=64, N=8, topk=2)
+    inp = si.forward_inputs(w, lengths=[0, 0, 0], seed=23)
+    init = np.random.default_rng(24).standard_normal((3, w.H, w.N + 1, w.c, w.d)).astype(np.float32)
+    d = {n: to_dev(inp[n]) for n in NAMES + ("cu_seqlens",)}
+    announce(w.name, "lengths [0, 0, 0]", "sse_forward")
+    fs = nan_like((3, w.H, w.N + 1, w.c, w.d))
+    o = nan_like((0, w.H, w.d))
+    sse.sse_forward(d["q"], d["key_logits"], d["v"], d["log_alpha"], d["router_logits"], w.N,
+                    w.topk, d["cu_seqlens"], 0, torch.from_numpy(init).cuda(), o=o, final_states=fs)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert np.array_equal(fs.cpu().numpy().view(np.uint32), init.view(np.uint32))
+
+
 def test_resume_matches_one_pass():
     w = si.Workload("resume", "bf16", H=2, c=128, d=128, N=8, topk=2)
     inp = si.forward_inputs(w, lengths=[500], seed=31)
