@@ -148,14 +148,42 @@ def run_forward(args, w, si, sse, torch, inp=None, schedule=None, step_stats=Non
     return T, S, total_ms, {k: v / max(calls, 1) for k, v in stages.items()}, calls
 
 
+def fwd_bwd_ms(w, si, sse, torch, inp, steps=10, warmup=2):
+    """ms of one sse_forward followed by one sse_backward of <d_o, o> (all
+    input gradients, no initial states) on the inputs `inp`."""
+    cu = inp["cu_seqlens"]
+    T, S = int(cu[-1]), len(cu) - 1
+    max_len = int((cu[1:] - cu[:-1]).max())
+    d_in = {n: to_dev(inp[n]) for n in NAMES + ("cu_seqlens",)}
+    o = torch.empty((T, w.H, w.d), dtype=torch.float32, device="cuda")
+    fs = torch.empty((S, w.H, w.N + 1, w.c, w.d), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(sse.sse_forward_workspace_bytes(T, S, max_len, w.H, w.c, w.d, w.N, w.topk),
+                      dtype=torch.uint8, device="cuda")
+    do = torch.randn((T, w.H, w.d), dtype=torch.float32, device="cuda")
+    out = {nm: torch.empty(shp, dtype=torch.float32, device="cuda") for nm, shp in (
+        ("dq", (T, w.H, w.c)), ("dkey_logits", (T, w.H, w.c)), ("dlog_alpha", (T, w.H, w.c)),
+        ("dv", (T, w.H, w.d)), ("drouter_logits", (T, w.H, w.N)))}
+    wsb = torch.empty(sse.sse_backward_workspace_bytes(T, S, max_len, w.H, w.c, w.d, w.N, w.topk),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        sse.sse_forward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], max_len,
+                        o=o, final_states=fs, workspace=wsf)
+        sse.sse_backward(*(d_in[n] for n in NAMES), w.N, w.topk, d_in["cu_seqlens"], do,
+                         max_len, workspace=wsb, out=out)
+
+    return timed(torch, step, steps, warmup)
+
+
 def fig6_sweep(args, si, sse, torch):
     """Forward time of the varlen path in the operator-timing setting of
     "Scaling Linear Attention with Sparse State Expansion: 中文研读笔记"
     (§2.6, Fig. 6): 8 heads, head dim 128, one routed partition per token,
     two sequences of L/2 tokens, N = 4, 8, 16; bf16 inputs here.  That figure
     times forward plus backward on another GPU and gives no values in the
-    text; this measures the forward only, to see how the time moves with N
-    at fixed k."""
+    text.  Both schedules' forwards are timed, and the varlen schedule's
+    forward plus backward (the masked schedule has no backward here), to see
+    how the time moves with N at fixed k."""
     from types import SimpleNamespace
     ns = SimpleNamespace(warmup=2, steps=10)
     rows = []
@@ -173,20 +201,28 @@ def fig6_sweep(args, si, sse, torch):
                 T, S, total_ms, stages, _ = run_forward(ns, w, si, sse, torch, inp=inp,
                                                         schedule=sched)
                 ms = total_ms / ns.steps
-                rows.append({"L": L, "N": N, "schedule": sched, "ms": ms,
-                             "tokens_per_s": T / (ms * 1e-3), "stage_ms": stages})
-                log(f"fig6 L={L} N={N} {sched}: {ms:.3f} ms")
-    spread, faster = {}, {}
+                row = {"L": L, "N": N, "schedule": sched, "ms": ms,
+                       "tokens_per_s": T / (ms * 1e-3), "stage_ms": stages}
+                if sched == "varlen":
+                    row["fwd_bwd_ms"] = fwd_bwd_ms(w, si, sse, torch, inp)
+                rows.append(row)
+                log(f"fig6 L={L} N={N} {sched}: {ms:.3f} ms" +
+                    (f", forward + backward {row['fwd_bwd_ms']:.3f} ms" if sched == "varlen" else ""))
+    spread, spread_fb, faster = {}, {}, {}
     for L in sorted({r["L"] for r in rows}):
         t = [r["ms"] for r in rows if r["L"] == L and r["schedule"] == "varlen"]
         spread[str(L)] = max(t) / min(t)
+        t = [r["fwd_bwd_ms"] for r in rows if r["L"] == L and r["schedule"] == "varlen"]
+        spread_fb[str(L)] = max(t) / min(t)
         for N in (4, 8, 16):
             tv = [r["ms"] for r in rows if r["L"] == L and r["N"] == N and r["schedule"] == "varlen"][0]
             tm = [r["ms"] for r in rows if r["L"] == L and r["N"] == N and r["schedule"] == "masked"][0]
             faster[f"L{L}_N{N}"] = "masked" if tm < tv else "varlen"
     return {"setting": "H=8, c=d=128, k=1, cu_seqlens=[0, L/2, L], N in {4, 8, 16}, bf16 "
-                       "inputs, router logits N(0,1), forward only, varlen and masked schedules",
-            "rows": rows, "varlen_max_over_min_across_N": spread, "faster_schedule": faster}
+                       "inputs, router logits N(0,1), forward of both schedules, forward + backward "
+                       "of the varlen schedule",
+            "rows": rows, "varlen_max_over_min_across_N": spread,
+            "varlen_fwd_bwd_max_over_min_across_N": spread_fb, "faster_schedule": faster}
 
 
 def timed(torch, fn, steps, warmup):
