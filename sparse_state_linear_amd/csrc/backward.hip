@@ -58,6 +58,7 @@
 // applies the router softmax Jacobian.  No atomics: every run gives the
 // same bits.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -1171,17 +1172,26 @@ void launch_bwd_cfg(const BwdArgs& a, hipStream_t st) {
     bwd_sweep_kernel<CK, DV, TIn><<<(unsigned)(2 * nseg), sweep_waves<CK, DV>() * kWave, 0, st>>>(a);
     if (a.nslot > 0) {
         // as many chunk blocks as the device holds at once (each walks the
-        // slots b, b + grid, ...)
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_chunk_kernel<CK, DV, TIn>, kCW * kWave,
-                                                         0) != hipSuccess ||
-            cus < 1 || per_cu < 1) {
-            cus = 256;
-            per_cu = 1;
+        // slots b, b + grid, ...); queried once per device and shape
+        constexpr int kDevs = 64;
+        static std::atomic<int> resident[kDevs];   // 0: not queried yet
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) dev = -1;
+        int blocks = dev >= 0 ? resident[dev].load(std::memory_order_relaxed) : 0;
+        if (blocks <= 0) {
+            int cus = 0, per_cu = 0;
+            if (dev < 0 ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_chunk_kernel<CK, DV, TIn>,
+                                                             kCW * kWave, 0) != hipSuccess ||
+                cus < 1 || per_cu < 1) {
+                cus = 256;
+                per_cu = 1;
+            }
+            blocks = cus * per_cu;
+            if (dev >= 0) resident[dev].store(blocks, std::memory_order_relaxed);
         }
-        const int64_t grid = std::min<int64_t>(a.nslot, (int64_t)cus * per_cu);
+        const int64_t grid = std::min<int64_t>(a.nslot, (int64_t)blocks);
         bwd_chunk_kernel<CK, DV, TIn><<<(unsigned)grid, kCW * kWave, 0, st>>>(a);
     }
 }
