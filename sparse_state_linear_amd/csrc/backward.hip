@@ -40,8 +40,10 @@
 // V, exact in bf16, or g in two terms).  The forward sweep also writes
 // every chunk's record list (input row, gradient slot, gate, key
 // normaliser) for launch 2.
-// Launch 2 (chunks): one block per chunk of every segment, reading the S_in
-// and G of its chunk, so all chunks run in parallel; 8 waves, wave w owning
+// Launch 2 (chunks): every chunk's gradients from its stored S_in and G~, so
+// all chunks are independent; persistent 8-wave blocks, each walking every
+// G-th checkpoint slot with the next slot's records and rows prefetched;
+// wave w owning
 // the 16-column block w of the d-side outputs (y, dV) and the 16-row block w
 // of the c-side ones (dQt, dKh).  The state operands are read straight from
 // the stored states in the MFMA operand layout (rows, or transposed for the
