@@ -4,9 +4,14 @@ One step = one sse_forward over the main workload (bf16, B=4, H=16, T=8192,
 c=d=128, N=16, k=2, router std 1.5): routing + counts, grouping, chunked
 GLA over all partition segments with the combine into o.  ``value`` is that
 forward's throughput in tokens/s (B*T tokens per step, all heads), with the
-inputs already resident in HBM.  The decode step (256 sequences x H=16,
-c=d=128, N=16, k=2, 64 consecutive steps) is timed in the same run and
-reported under "decode".
+inputs already resident in HBM, timed over --steps calls after 0.3 s of
+untimed forwards and --warmup warm-up calls (the first forwards on an idle
+GPU run slower); "step_ms" gives median, min and max of further forwards
+timed one by one.  The decode step (256 sequences x H=16, c=d=128, N=16,
+k=2, 64 consecutive steps), the varlen forward, the masking schedule, the
+backward and the row-sparse variant are timed in the same run; --fig6 adds
+the operator-timing sweep of the page's Fig. 6 (forward of both schedules,
+forward + backward of the varlen schedule).
 
 roofline: the dominant kernel is the chunked GLA pass with the longest
 time (the routed pass); its duration comes from HIP events recorded around it
