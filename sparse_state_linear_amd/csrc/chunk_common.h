@@ -81,33 +81,6 @@ __device__ __forceinline__ void split4(const float (&x)[kPC], uint2 (&out)[L]) {
     for (int l = 0; l < L; l++) out[l] = make_uint2(lo[l], hi[l]);
 }
 
-__device__ __forceinline__ uint16_t elem(const uint2& v, int e) {
-    const uint32_t w = (e < 2) ? v.x : v.y;
-    return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-}
-
-// Store R consecutive 16-bit values (R in {1, 2, 4, 8}).
-template <int R>
-__device__ __forceinline__ void store_run(uint16_t* p, const uint16_t (&v)[R]) {
-    if constexpr (R == 1) {
-        p[0] = v[0];
-    } else if constexpr (R == 2) {
-        *reinterpret_cast<uint32_t*>(p) = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-    } else if constexpr (R == 4) {
-        uint2 x;
-        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-        *reinterpret_cast<uint2*>(p) = x;
-    } else {
-        uint4 x;
-        x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-        x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-        x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-        x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-        *reinterpret_cast<uint4*>(p) = x;
-    }
-}
-
 __device__ __forceinline__ u16x8 lds8(const uint16_t* p) {
     return *reinterpret_cast<const u16x8*>(p);
 }
@@ -121,11 +94,6 @@ __device__ __forceinline__ s16x4 lds_tr(const uint16_t* p) {
 }
 __device__ __forceinline__ u16x8 cat_tr(const s16x4& a, const s16x4& b) {
     return __builtin_bit_cast(u16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-__device__ __forceinline__ u16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) {
-    const u16x4 a = *reinterpret_cast<const u16x4*>(p0);
-    const u16x4 b = *reinterpret_cast<const u16x4*>(p1);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // sum over term pairs (x, y) with x + y < max(LA, LB) of A_x B_y
@@ -160,22 +128,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Barrier for LDS hazards only: global loads and stores may stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Causal 16x16 tile ti of A^T (s-tile st, r-tile rt).  The first nt(nt+1)/2
-// tiles have st <= rt; the remaining nt/2 are the tiles just above the
-// diagonal inside each 32-record block, stored as zeros.
-template <int C>
-__device__ __forceinline__ void a_tile(int ti, int& st, int& rt) {
-    constexpr int nt = C / 16, ncausal = nt * (nt + 1) / 2;
-    if (ti < ncausal) {
-        rt = 0;
-        while ((rt + 1) * (rt + 2) / 2 <= ti) rt++;
-        st = ti - rt * (rt + 1) / 2;
-    } else {
-        rt = 2 * (ti - ncausal);
-        st = rt + 1;
-    }
 }
 
 }  // namespace
