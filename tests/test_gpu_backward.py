@@ -129,7 +129,9 @@ def test_backward_tied_router_logits():
     w = si.Workload("bwd_ties", "bf16", H=2, c=64, d=64, N=8, topk=3)
     lengths = [300, 20]
     inp = si.forward_inputs(w, lengths=lengths, seed=750)
-    z = np.random.default_rng(751).integers(-2, 3, inp["router_logits"].shape).astype(np.float32)
+    rng = np.random.default_rng(751)
+    z = rng.integers(-2, 3, inp["router_logits"].shape).astype(np.float32)
+    z[(z == 0) & (rng.random(z.shape) < 0.5)] = -0.0   # -0 ties with +0
     inp["router_logits"] = si.f32_to_bf16_bits(z)
     _check(w, lengths, 750, inp=inp)
 

@@ -238,8 +238,10 @@ def test_gate_limit_uniform_decay(dtype):
 
 def _tied_router(inp, w, rng):
     """Integer-valued router logits in [-2, 2]: most rows hold equal values,
-    so the order of equal logits (lower index first) decides the top-k."""
+    so the order of equal logits (lower index first) decides the top-k.  Half
+    the zeros are -0, which ties with +0 (they are the same value)."""
     z = rng.integers(-2, 3, inp["router_logits"].shape).astype(np.float32)
+    z[(z == 0) & (rng.random(z.shape) < 0.5)] = -0.0
     inp["router_logits"] = si.f32_to_bf16_bits(z) if w.dtype == "bf16" else z
     return inp
 

@@ -108,11 +108,15 @@ def test_rowsparse_pieces(n_seq, H):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rowsparse_tied_key_logits(dtype):
     """Integer-valued key logits in [-2, 2]: the k-th largest value is tied
-    in most rows, and the lower rows must win, as in the oracle."""
+    in most rows, and the lower rows must win, as in the oracle.  Half the
+    zeros are -0, which ties with +0."""
     w = si.Workload(f"rowsparse_ties_{dtype}", dtype, H=2, c=64, d=64, N=1, topk=1)
     lengths = [400, 33]
     inp = si.forward_inputs(w, lengths=lengths, seed=230)
-    kl = np.random.default_rng(231).integers(-2, 3, inp["key_logits"].shape).astype(np.float32)
+    rng = np.random.default_rng(231)
+    kl = rng.integers(-2, 3, inp["key_logits"].shape).astype(np.float32)
+    kl[(kl == 0) & (rng.random(kl.shape) < 0.5)] = -0.0
+    assert np.signbit(kl[kl == 0]).any()
     inp["key_logits"] = si.f32_to_bf16_bits(kl) if dtype == "bf16" else kl
     for k in (5, 16):
         _check(w, lengths, k, True, seed=0, inp=inp)
