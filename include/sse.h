@@ -22,7 +22,8 @@
  * Conventions for every entry point
  *   - Device pointers unless stated otherwise; buffers are dense, row-major,
  *     in the layouts given.  The caller owns every buffer; the library never
- *     allocates or frees memory and never synchronises the stream.
+ *     allocates or frees memory and never synchronises the stream (debug
+ *     mode, below, does).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All
  *     work is enqueued on it asynchronously.
  *   - `dtype` selects the storage type of the five token inputs:
@@ -44,6 +45,9 @@
  *     -80 (the chunked factorisation multiplies by exp of minus the in-chunk
  *     sum in fp32; fp32 inputs are computed in fp64, where the sum over any 16
  *     consecutive records only has to stay above -700).
+ *     q, key_logits, v, log_alpha, the states, o, the gradients and the
+ *     workspace start at 16-byte-aligned addresses (device allocators give
+ *     256): their rows are read and written in 16-byte pieces.
  */
 #ifndef SSE_H
 #define SSE_H
