@@ -701,7 +701,14 @@ int sse_trace_enable(int enable) {
     if (enable && !g_trace.created) {
         for (int i = 0; i < kTraceCalls; i++)
             for (int j = 0; j < kTraceMarks; j++)
-                if (hipEventCreate(&g_trace.ev[i][j]) != hipSuccess) return SSE_ERR_HIP;
+                if (hipEventCreate(&g_trace.ev[i][j]) != hipSuccess) {
+                    // release the events made so far; tracing stays off
+                    for (int x = 0; x <= i; x++)
+                        for (int y = 0; y < (x < i ? kTraceMarks : j); y++)
+                            (void)hipEventDestroy(g_trace.ev[x][y]);
+                    g_trace.on = false;
+                    return SSE_ERR_HIP;
+                }
         g_trace.created = true;
     }
     g_trace.on = enable != 0;
