@@ -45,9 +45,10 @@
  *     -80 (the chunked factorisation multiplies by exp of minus the in-chunk
  *     sum in fp32; fp32 inputs are computed in fp64, where the sum over any 16
  *     consecutive records only has to stay above -700).
- *     q, key_logits, v, log_alpha, the states, o, the gradients and the
- *     workspace start at 16-byte-aligned addresses (device allocators give
- *     256): their rows are read and written in 16-byte pieces.
+ *     The token inputs (q, key_logits, v, log_alpha, router_logits), the
+ *     states, o, the gradients and the workspace start at 16-byte-aligned
+ *     addresses (device allocators give 256): their rows are read and
+ *     written in 16-byte pieces.
  */
 #ifndef SSE_H
 #define SSE_H
